@@ -1,0 +1,214 @@
+"""Pins of the oracle's LayerNorm, GELU, attention, time embedding, steering,
+CFG merge and sampler (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ald_oracle as O
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def test_layer_norm_vs_torch_cpu_and_moments():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((16, 256)) * 3 + 1).astype(np.float16)
+    g = (1 + 0.02 * rng.standard_normal(256)).astype(np.float32)
+    b = (0.02 * rng.standard_normal(256)).astype(np.float32)
+    y = O.layer_norm(x, g, b).astype(np.float64)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x.astype(np.float64)), (256,),
+                                         torch.from_numpy(g.astype(np.float64)),
+                                         torch.from_numpy(b.astype(np.float64)), eps=1e-5).numpy()
+    assert np.max(np.abs(y - ref)) <= 2.0 ** -9 * np.max(np.abs(ref))
+    y1 = O.layer_norm(x, np.ones(256, np.float32), np.zeros(256, np.float32)).astype(np.float64)
+    assert np.allclose(y1.mean(axis=1), 0, atol=2e-3)
+    assert np.allclose(y1.var(axis=1), 1, atol=5e-3)
+
+
+def test_layer_norm_constant_row():
+    x = np.full((2, 64), 3.0, np.float16)
+    y = O.layer_norm(x, np.ones(64, np.float32), np.full(64, 0.25, np.float32))
+    assert np.all(y == np.float16(0.25))   # zero variance: (x - mu) = 0 exactly
+
+
+# ---------------------------------------------------------------- GELU
+
+def test_gelu_values():
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    assert O.gelu(np.array([1.0]))[0] == pytest.approx(0.8413447460685429, abs=1e-15)  # Phi(1)
+    x = np.linspace(-6, 6, 101)
+    # erf is odd, so gelu(x) - gelu(-x) = x
+    assert np.allclose(O.gelu(x) - O.gelu(-x), x, atol=1e-14)
+    ref = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    assert np.allclose(O.gelu(x), ref, atol=1e-15)
+
+
+# ---------------------------------------------------------------- attention
+
+def _naive_attn(q, k, v, scale):
+    Sq, nh, d = q.shape
+    Sk = k.shape[0]
+    out = np.zeros((Sq, nh, d))
+    for h in range(nh):
+        for i in range(Sq):
+            s = [sum(float(q[i, h, c]) * float(k[j, h, c]) for c in range(d)) * scale for j in range(Sk)]
+            m = max(s)
+            e = [math.exp(z - m) for z in s]
+            z = math.fsum(e)
+            for c in range(d):
+                out[i, h, c] = math.fsum(e[j] * float(v[j, h, c]) for j in range(Sk)) / z
+    return out
+
+
+def test_attention_naive_loops():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((5, 2, 8)).astype(np.float16)
+    k = rng.standard_normal((7, 2, 8)).astype(np.float16)
+    v = rng.standard_normal((7, 2, 8)).astype(np.float16)
+    got = O.attention(q, k, v, 1 / math.sqrt(8)).astype(np.float64)
+    ref = _naive_attn(q, k, v, 1 / math.sqrt(8))
+    assert np.max(np.abs(got - ref)) <= 2.0 ** -11 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((9, 3, 64)).astype(np.float16)
+    v = rng.standard_normal((1, 3, 64)).astype(np.float16)
+    k = rng.standard_normal((1, 3, 64)).astype(np.float16)
+    # a single key: the softmax weight is exactly 1, output = v
+    assert np.array_equal(O.attention(q, k, v, 0.125), np.broadcast_to(v, (9, 3, 64)))
+    # identical keys: uniform weights, output = mean of the values
+    k = np.broadcast_to(rng.standard_normal((1, 3, 64)).astype(np.float16), (6, 3, 64))
+    v = rng.standard_normal((6, 3, 64)).astype(np.float16)
+    got = O.attention(q, k, v, 0.125).astype(np.float64)
+    ref = np.broadcast_to(v.astype(np.float64).mean(axis=0), got.shape)
+    assert np.max(np.abs(got - ref)) <= 2.0 ** -10
+    # permuting keys and values together leaves the output unchanged
+    k2 = rng.standard_normal((6, 3, 64)).astype(np.float16)
+    p = rng.permutation(6)
+    a = O.attention(q, k2, v, 0.125).astype(np.float64)
+    b = O.attention(q, k2[p], v[p], 0.125).astype(np.float64)
+    assert np.max(np.abs(a - b)) <= 2.0 ** -10
+
+
+def test_attention_varlen_equals_dense_per_sequence():
+    rng = np.random.default_rng(3)
+    lens = [3, 1, 10]
+    tot = sum(lens)
+    nh, d = 2, 16
+    q = rng.standard_normal((tot, nh * d)).astype(np.float16)
+    k = rng.standard_normal((tot, nh * d)).astype(np.float16)
+    v = rng.standard_normal((tot, nh * d)).astype(np.float16)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    out = O.attention_varlen(q, k, v, cu, cu, nh, 0.25)
+    for b in range(3):
+        s0, s1 = cu[b], cu[b + 1]
+        ref = _naive_attn(q[s0:s1].reshape(-1, nh, d), k[s0:s1].reshape(-1, nh, d),
+                          v[s0:s1].reshape(-1, nh, d), 0.25).reshape(s1 - s0, nh * d)
+        assert np.max(np.abs(out[s0:s1].astype(np.float64) - ref)) <= 2.0 ** -10
+
+
+# ---------------------------------------------------------------- time embedding
+
+def test_timestep_embedding_values():
+    e = O.timestep_embedding(np.array([0.0, 0.5]), 8)
+    assert np.array_equal(e[0], [0, 0, 0, 0, 1, 1, 1, 1])
+    # omega_0 = 1: first entry is sin(1000 t), entry H/2 is cos(1000 t)
+    assert e[1, 0] == pytest.approx(math.sin(500.0), abs=1e-12)
+    assert e[1, 4] == pytest.approx(math.cos(500.0), abs=1e-12)
+    # omega_j = 1e4^(-j/(H/2)): j = 2 of H/2 = 4 is 1e-2
+    assert e[1, 2] == pytest.approx(math.sin(500.0 * 1e-2), abs=1e-12)
+    assert np.allclose(e[:, :4] ** 2 + e[:, 4:] ** 2, 1.0)
+
+
+# ---------------------------------------------------------------- steering
+
+def test_steer_alpha_zero_is_bit_identical():
+    rng = np.random.default_rng(4)
+    h = rng.standard_normal((6, 32)).astype(np.float16)
+    h[0, 0] = np.float16(-0.0)
+    h[1, 3] = np.float16(np.nan)
+    d = rng.standard_normal(32)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    out = O.steer_add(h, np.zeros(6, np.float32), 7.5, d)
+    assert out.tobytes() == h.tobytes()     # -0.0 and NaN bits kept
+    alpha = np.array([0, 0.5, 0, 0.25, 0, 1.0], np.float32)
+    out = O.steer_add(h, alpha, 7.5, d)
+    for i in (0, 2, 4):
+        assert out[i].tobytes() == h[i].tobytes()
+
+
+def test_steer_closed_form_and_linearity():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal((4, 64)).astype(np.float16)
+    d = rng.standard_normal(64)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    hn = 3.0
+    delta = {}
+    for a in (0.25, 0.5, 1.0):
+        out = O.steer_add(h, np.full(4, a, np.float32), hn, d).astype(np.float64)
+        delta[a] = out - h.astype(np.float64)
+        # rank-one update along d with magnitude alpha * ||h_bar||
+        assert np.allclose(delta[a], a * hn * d.astype(np.float64)[None, :], atol=2.0 ** -8)
+        assert np.allclose(np.linalg.norm(delta[a], axis=1), a * hn, rtol=2e-3)
+    assert np.allclose(delta[1.0], 2 * delta[0.5], atol=2.0 ** -8)
+    assert np.allclose(delta[0.5], 2 * delta[0.25], atol=2.0 ** -8)
+
+
+def test_mean_row_norm():
+    h = np.array([[3, 4, 0], [0, 0, 1]], np.float16)
+    assert O.mean_row_norm(h) == pytest.approx(3.0)   # (5 + 1) / 2
+
+
+# ---------------------------------------------------------------- CFG merge
+
+def test_cfg_special_values_and_affinity():
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((5, 64)).astype(np.float16)
+    u = rng.standard_normal((5, 64)).astype(np.float16)
+    assert np.array_equal(O.cfg_merge(c, u, 1.0), c.astype(np.float32))
+    assert np.array_equal(O.cfg_merge(c, u, 0.0), u.astype(np.float32))
+    cf, uf = c.astype(np.float64), u.astype(np.float64)
+    for w in (3.0, 1.5, 4.75):
+        assert np.allclose(O.cfg_merge(c, u, w), cf + (w - 1) * (cf - uf), rtol=1e-6, atol=1e-5)
+    assert np.array_equal(O.cfg_merge(c, c, 3.0), c.astype(np.float32))
+
+
+# ---------------------------------------------------------------- sampler
+
+def test_euler_closed_form_and_constant_field():
+    rng = np.random.default_rng(7)
+    x0 = rng.standard_normal((10, 64)).astype(np.float32)
+    eps = rng.standard_normal((10, 64)).astype(np.float32)
+    # the exact velocity of the straight path x_t = (1-t) x0 + t eps is eps - x0;
+    # Euler on any grid from t = 1 to 0 integrates it exactly (up to fp32 rounding)
+    tg = 1 - np.arange(9) / 8
+    x = eps.copy()
+    for i in range(8):
+        x = O.euler_update(x, eps - x0, tg[i], tg[i + 1])
+    assert np.allclose(x, x0, atol=1e-5)
+    y = O.euler_update(x0, eps, 1.0, 0.875)
+    assert np.array_equal(y, (x0 + np.float32(-0.125) * eps).astype(np.float32))
+
+
+def test_renoise_endpoints_and_path():
+    rng = np.random.default_rng(8)
+    x0 = rng.standard_normal((4, 64)).astype(np.float32)
+    eps = rng.standard_normal((4, 64)).astype(np.float32)
+    assert np.array_equal(O.renoise(x0, eps, 0.0), x0)
+    assert np.array_equal(O.renoise(x0, eps, 1.0), eps)
+    # warm start at t_k then exact-velocity Euler reaches x0
+    N, k = 16, 6
+    tg = 1 - np.arange(N + 1) / N
+    x = O.renoise(x0, eps, tg[k])
+    for i in range(k, N):
+        x = O.euler_update(x, eps - x0, tg[i], tg[i + 1])
+    assert np.allclose(x, x0, atol=1e-5)
+
+
+def test_skip_start_step():
+    assert O.skip_start_step(0.3, 16) == 5      # 4.8 + 0.5 -> 5
+    assert O.skip_start_step(0.7, 16) == 11     # 11.2 + 0.5 -> 11
+    assert O.skip_start_step(0.5, 8) == 4
+    assert O.skip_start_step(0.0, 8) == 0

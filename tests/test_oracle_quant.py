@@ -1,0 +1,193 @@
+"""Pins of the oracle's quantizers and integer GEMM (CPU only).
+
+The pages give 8-bit weights, W8A8 arithmetic and 4-bit storage (aria,
+Section III-A) but no quantizer formula and no worked values; the pins are
+hand-derived closed forms (tests/golden), brute force, and error bounds that
+hold for any correct symmetric round-to-nearest quantizer.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import ald_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def test_q8_hand_cases():
+    for case in _load("q8_ties.json")["cases"]:
+        u = np.array([case["u"]], dtype=np.float16)
+        q, s = O.quantize_rows_q8(u)
+        assert q.dtype == np.int8
+        assert q[0].tolist() == case["codes"], case["why"]
+        assert float(s[0]) == pytest.approx(case["scale"], rel=0, abs=0), case["why"]
+
+
+def test_q8_scale_is_fp32_quotient():
+    # s must be the correctly rounded fp32 value of amax / 127 (exact rational check)
+    rng = np.random.default_rng(5)
+    u = rng.standard_normal((64, 96)).astype(np.float16)
+    _, s = O.quantize_rows_q8(u)
+    for i in range(u.shape[0]):
+        amax = Fraction(float(np.max(np.abs(u[i].astype(np.float64)))))
+        exact = amax / 127
+        got = Fraction(float(s[i]))
+        # nearest fp32: neighbours are further away
+        up = Fraction(float(np.nextafter(np.float32(s[i]), np.float32(np.inf))))
+        dn = Fraction(float(np.nextafter(np.float32(s[i]), np.float32(-np.inf))))
+        assert abs(got - exact) <= abs(up - exact) and abs(got - exact) <= abs(dn - exact)
+
+
+def test_q8_round_to_nearest_bound_and_range():
+    rng = np.random.default_rng(1)
+    u = (rng.standard_normal((200, 257)) * rng.uniform(0.01, 50, size=(200, 1))).astype(np.float16)
+    u[3] = 0
+    u[7, :] = np.float16(-3.0)
+    q, s = O.quantize_rows_q8(u)
+    uf = u.astype(np.float64)
+    amax = np.max(np.abs(uf), axis=1)
+    for i in range(u.shape[0]):
+        if amax[i] == 0:
+            assert s[i] == 0 and not q[i].any()
+            continue
+        # codes are the nearest integers to 127 u / amax (up to fp32 rounding of the product)
+        ideal = 127.0 * uf[i] / amax[i]
+        assert np.all(np.abs(q[i] - ideal) <= 0.5 + 1e-4)
+        assert np.max(np.abs(q[i])) == 127          # the amax element saturates exactly
+        assert np.all(np.abs(q[i]) <= 127)
+        assert np.all(np.sign(q[i]) * np.sign(uf[i]) >= 0)
+        # monotone in u
+        order = np.argsort(uf[i], kind="stable")
+        assert np.all(np.diff(q[i][order].astype(np.int64)) >= 0)
+        # |u - q s| <= s / 2 (plus fp32 slack)
+        err = np.abs(uf[i] - q[i] * float(s[i]))
+        assert np.all(err <= 0.5 * float(s[i]) * (1 + 1e-5) + 1e-12)
+
+
+def test_int_gemm_brute_force():
+    rng = np.random.default_rng(2)
+    for (M, N, K) in [(1, 1, 1), (3, 5, 7), (17, 9, 64), (5, 33, 130)]:
+        a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        b = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+        acc = O.int_gemm(a, b)
+        for m in range(M):
+            for n in range(N):
+                ref = 0
+                for k in range(K):
+                    ref += int(a[m, k]) * int(b[n, k])
+                assert acc[m, n] == ref
+
+
+def test_int_gemm_extremes_exact():
+    K = 8192
+    a = np.full((2, K), 127, np.int8)
+    a[1] = -127
+    b = np.full((3, K), 127, np.int8)
+    b[1] = -127
+    b[2, ::2] = -127
+    acc = O.int_gemm(a, b)
+    assert acc[0, 0] == K * 127 * 127
+    assert acc[1, 0] == -K * 127 * 127
+    assert acc[0, 1] == -K * 127 * 127
+    assert acc[0, 2] == 0
+
+
+def test_w8a8_error_bound_and_orientation():
+    rng = np.random.default_rng(3)
+    M, K, N = 24, 192, 40
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * rng.standard_normal(N)).astype(np.float32)
+    wq, ws = O.quantize_rows_q8(w)
+    r = O.w8a8_linear(x, wq, ws, b)
+    xf, wf = x.astype(np.float64), w.astype(np.float64)
+    exact = xf @ wf.T + b
+    bound = (np.abs(xf) @ (np.ones_like(wf) * ws[:, None] / 2).T
+             + (np.ones_like(xf) * r.x_scale[:, None] / 2) @ np.abs(wf).T
+             + K * (r.x_scale[:, None] * ws[None, :]) / 4)
+    fp16_round = np.abs(exact) * 2.0 ** -11 + 2.0 ** -24
+    assert np.all(np.abs(r.y.astype(np.float64) - exact) <= bound * 1.0001 + fp16_round * 1.01)
+    # the raw accumulators are the integer products of the codes
+    assert np.array_equal(r.acc, O.int_gemm(r.xq, wq))
+
+
+def test_w8a8_residual_and_gelu():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((8, 64)).astype(np.float16)
+    w = (0.05 * rng.standard_normal((16, 64))).astype(np.float16)
+    res = rng.standard_normal((8, 16)).astype(np.float16)
+    wq, ws = O.quantize_rows_q8(w)
+    base = O.w8a8_linear(x, wq, ws, None)
+    deq = base.acc * base.x_scale[:, None].astype(np.float64) * ws[None, :].astype(np.float64)
+    withres = O.w8a8_linear(x, wq, ws, None, residual=res).y.astype(np.float64)
+    assert np.allclose(withres, deq + res.astype(np.float64), atol=2e-3, rtol=2e-3)
+    gl = O.w8a8_linear(x, wq, ws, None, act=1).y.astype(np.float64)
+    from math import erf, sqrt
+    ref = np.vectorize(lambda v: 0.5 * v * (1 + erf(v / sqrt(2))))(deq)
+    assert np.allclose(gl, ref, atol=1e-3, rtol=1e-3)
+
+
+def test_q4_pack_fixture():
+    g = _load("q4_pack.json")
+    for case in g["pack_cases"]:
+        codes = np.array(case["codes"], dtype=np.int64)
+        # build a row whose quantization yields exactly these codes: s = 1 needs amax 7
+        row = codes.astype(np.float16)
+        row = np.concatenate([row, np.zeros(32 - len(row), np.float16)])
+        row[-1] = np.float16(7.0)  # amax 7 -> s = 1
+        packed, s = O.quantize_q4(row[None, :])
+        assert float(s[0, 0]) == 1.0
+        assert packed[0, :len(case["bytes"])].tolist() == case["bytes"], case["why"]
+        assert O.unpack_q4(packed)[0, :len(codes)].tolist() == codes.tolist()
+    rc = g["reconstruct_case"]
+    w = (np.array(rc["codes"], np.float64) * rc["s"]).astype(np.float16)[None, :]
+    packed, s = O.quantize_q4(w)
+    assert float(s[0, 0]) == rc["s"]
+    assert O.unpack_q4(packed)[0].tolist() == rc["codes"]
+    assert np.array_equal(O.dequantize_q4(packed, s), w)
+
+
+def test_q4_error_bound():
+    rng = np.random.default_rng(6)
+    N, K = 48, 256
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float16)
+    w[5, 32:64] = 0
+    packed, s = O.quantize_q4(w)
+    codes = O.unpack_q4(packed).astype(np.int64)
+    assert codes.min() >= -7 and codes.max() <= 7
+    deq = O.dequantize_q4(packed, s).astype(np.float64)
+    wf = w.astype(np.float64)
+    s_el = np.repeat(s.astype(np.float64), 32, axis=1)
+    # fp16 ulp of the largest dequantized magnitude in the group (7 s)
+    ulp = np.repeat(np.array([[np.spacing(np.float16(7 * v)) for v in row] for row in s.astype(np.float32)],
+                             dtype=np.float64), 32, axis=1)
+    assert np.all(np.abs(wf - deq) <= s_el / 2 * (1 + 1e-6) + ulp / 2 + 1e-12)
+    assert not codes[5, 32:64].any() and s[5, 1] == 0
+    # the group's extreme saturates at +-7 and amax/7 is the (fp16-rounded) scale
+    amax = np.max(np.abs(wf.reshape(N, K // 32, 32)), axis=2)
+    assert np.allclose(s.astype(np.float64), amax / 7, rtol=2 ** -10)
+
+
+def test_planted_rounding_mistake_is_caught(monkeypatch):
+    """A quantizer that truncates instead of rounding half-even must fail the tie pin."""
+    real = O.quantize_rows_q8
+
+    def trunc(u16):
+        u = np.asarray(u16, np.float16).astype(np.float32)
+        amax = np.max(np.abs(u), axis=1).astype(np.float32)
+        inv = np.where(amax > 0, np.float32(127) / np.where(amax > 0, amax, 1), 0).astype(np.float32)
+        return np.clip(np.trunc(u * inv[:, None]), -127, 127).astype(np.int8), (amax / np.float32(127)).astype(np.float32)
+
+    monkeypatch.setattr(O, "quantize_rows_q8", trunc)
+    with pytest.raises(AssertionError):
+        test_q8_hand_cases()
+    monkeypatch.setattr(O, "quantize_rows_q8", real)
+    test_q8_hand_cases()

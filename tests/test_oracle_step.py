@@ -1,0 +1,139 @@
+"""Whole-step invariants of the oracle (CPU only).
+
+No page prints a worked example of a DiT step, so the composed step is
+"parity unpinned" by the pages; these invariants pin what the method fixes:
+permutation equivariance over latent tokens (no positional encoding in the
+reading), request independence, alpha = 0 identity with the unsteered pass,
+guidance 1 = conditional branch, the null-prompt companion's cross-attention
+reducing to the value bias, and steering confined to its step span.
+"""
+import numpy as np
+import pytest
+
+import ald_inputs as I
+from oracle import ald_oracle as O
+
+CFG = I.TINY
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    p = I.make_params(CFG)
+    m = O.prepare_model(CFG, p)
+    inp = I.make_inputs(CFG)
+    kv = O.text_kv(m, inp.text)
+    return m, inp, kv
+
+
+def _step(m, x, seqlens, kv, alpha=0.0, w=3.0, resid=5.0, direction=None, cfg_over=None):
+    R = len(seqlens)
+    d = direction if direction is not None else np.eye(CFG.hidden, dtype=np.float32)[0]
+    return O.dit_step(m, x, seqlens, kv, np.full(R, 1.0, np.float32), np.full(R, 0.875, np.float32),
+                      np.full(R, w, np.float32), np.full(R, alpha, np.float32), resid, d)
+
+
+def test_uncond_text_kv_is_value_bias(tiny):
+    m, inp, kv = tiny
+    T, H = CFG.text_tokens, CFG.hidden
+    for li, blk in enumerate(m.params.blocks):
+        unc = kv[li][T:]        # R = 1: CFG row 1 is the null prompt
+        assert np.array_equal(unc, np.broadcast_to(blk.b["kv"].astype(np.float16), unc.shape))
+
+
+def test_alpha_zero_equals_unsteered(tiny):
+    m, inp, kv = tiny
+    x1, _ = _step(m, inp.x, inp.seqlens, kv, alpha=0.0, direction=inp.direction)
+    m_off = O.PreparedModel(CFG.replace(steer_block=-1), m.params, m.lin)
+    x2, _ = _step(m_off, inp.x, inp.seqlens, kv, alpha=0.0, direction=inp.direction)
+    assert x1.tobytes() == x2.tobytes()
+    x3, _ = _step(m, inp.x, inp.seqlens, kv, alpha=0.5, direction=inp.direction)
+    assert not np.array_equal(x1, x3)
+
+
+def test_guidance_one_is_cond_branch(tiny):
+    m, inp, kv = tiny
+    x, tr = _step(m, inp.x, inp.seqlens, kv, w=1.0)
+    N = int(inp.seqlens.sum())
+    assert np.array_equal(tr.v_hat, tr.v[:N].astype(np.float32))
+    assert np.array_equal(x, O.euler_update(inp.x, tr.v[:N].astype(np.float32), 1.0, 0.875))
+
+
+def test_permutation_equivariance(tiny):
+    m, inp, kv = tiny
+    rng = np.random.default_rng(11)
+    p = rng.permutation(CFG.seq)
+    xa, _ = _step(m, inp.x, inp.seqlens, kv, alpha=0.5, direction=inp.direction)
+    xb, _ = _step(m, inp.x[p], inp.seqlens, kv, alpha=0.5, direction=inp.direction)
+    assert O.normwise_rel_err(xb, xa[p]) < 1e-3
+
+
+def test_request_independence():
+    cfg = CFG.replace(requests=2)
+    p = I.make_params(cfg)
+    m = O.prepare_model(cfg, p)
+    inp = I.make_inputs(cfg, seqlens=np.array([64, 17]))
+    kv = O.text_kv(m, inp.text)
+    tc = np.array([1.0, 0.625], np.float32)
+    tn = np.array([0.875, 0.5], np.float32)
+    w = np.array([3.0, 1.5], np.float32)
+    a = np.array([0.5, 0.0], np.float32)
+    x2, _ = O.dit_step(m, inp.x, inp.seqlens, kv, tc, tn, w, a, 4.0, inp.direction)
+    T = cfg.text_tokens
+    for r, (lo, hi) in enumerate([(0, 64), (64, 81)]):
+        kv_r = [k.reshape(4, T, -1)[[r, 2 + r]].reshape(2 * T, -1) for k in kv]
+        x1, _ = O.dit_step(m, inp.x[lo:hi], [hi - lo], kv_r, tc[r:r + 1], tn[r:r + 1], w[r:r + 1],
+                           a[r:r + 1], 4.0, inp.direction)
+        assert O.normwise_rel_err(x2[lo:hi], x1) < 1e-3
+
+
+def test_inactive_request_keeps_latent():
+    cfg = CFG.replace(requests=2)
+    m = O.prepare_model(cfg, I.make_params(cfg))
+    inp = I.make_inputs(cfg, seqlens=np.array([20, 30]))
+    kv = O.text_kv(m, inp.text)
+    x, _ = O.dit_step(m, inp.x, inp.seqlens, kv, np.ones(2, np.float32), np.full(2, 0.875, np.float32),
+                      np.full(2, 3.0, np.float32), np.zeros(2, np.float32), 1.0, inp.direction,
+                      active=np.array([True, False]))
+    assert np.array_equal(x[20:], inp.x[20:])
+    assert not np.array_equal(x[:20], inp.x[:20])
+
+
+def test_steering_only_inside_span():
+    cfg = CFG.replace(n_steps=4, steer_steps=(1, 2))
+    m = O.prepare_model(cfg, I.make_params(cfg))
+    inp = I.make_inputs(cfg)
+    kv = O.text_kv(m, inp.text)
+    x_on, tr_on = O.run_sampler(m, inp, kv, resid_norm=5.0)
+    x_off, tr_off = O.run_sampler(m, inp, kv, resid_norm=5.0, alpha_override=np.zeros_like(inp.alpha))
+    assert np.array_equal(tr_on[0].v, tr_off[0].v)          # step 0 outside the span
+    assert not np.array_equal(tr_on[1].v, tr_off[1].v)      # step 1 steered
+    assert not np.array_equal(x_on, x_off)
+
+
+def test_warm_start_renoise_in_sampler():
+    cfg = CFG.replace(requests=2, n_steps=4)
+    m = O.prepare_model(cfg, I.make_params(cfg))
+    inp = I.make_mixed_inputs(cfg, seqlens=np.array([16, 24]), warm=np.array([False, True]))
+    inp.start_step = np.array([0, 2])
+    inp.alpha[:] = 0
+    kv = O.text_kv(m, inp.text)
+    x, tr = O.run_sampler(m, inp, kv, steps=[0, 1])
+    # before its start step the warm request's latent is untouched
+    assert np.array_equal(x[16:], inp.x[16:])
+    x2, _ = O.run_sampler(m, inp, kv, steps=[2])
+    # at its start step it is re-noised to t_2 just before the model pass
+    xin = inp.x.copy()
+    xin[16:] = O.renoise(inp.x0[16:], inp.eps[16:], inp.t_grid[2])
+    xr, _ = O.dit_step(m, xin, inp.seqlens, kv, np.full(2, inp.t_grid[2], np.float32),
+                       np.full(2, inp.t_grid[3], np.float32), inp.guidance, np.zeros(2, np.float32),
+                       0.0, inp.direction, active=np.array([True, True]))
+    assert np.array_equal(x2, xr)
+
+
+def test_resid_norm_calibration_trace(tiny):
+    m, inp, kv = tiny
+    _, tr = O.dit_step(m, inp.x, inp.seqlens, kv, np.ones(1, np.float32), np.full(1, 0.875, np.float32),
+                       np.full(1, 3.0, np.float32), np.zeros(1, np.float32), 0.0, inp.direction,
+                       keep_blocks=[1])
+    n = O.mean_row_norm(tr.block_out[1])
+    assert np.isfinite(n) and n > 0
