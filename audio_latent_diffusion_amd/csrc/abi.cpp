@@ -1,0 +1,615 @@
+// C ABI of the DiT denoise step: host-side validation, workspace carving,
+// kernel enqueueing and graph capture.  No device allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "../../include/ald.h"
+#include "kernels.h"
+
+using namespace ald;
+
+namespace {
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+std::once_flag g_prep;
+void prepare() { std::call_once(g_prep, [] { gemm_prepare(); }); }
+
+inline int launched() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? ALD_OK : ALD_E_LAUNCH;
+}
+
+#define CHECK(cond, code) \
+  do {                    \
+    if (!(cond)) return (code); \
+  } while (0)
+
+// linear layer in any precision, A given as fp16 (F16/Q4) or int8 codes (W8A8)
+struct Lin {
+  int wmode;
+  const void* w;
+  const void* scale;
+  const float* bias;
+};
+
+int check_epilogue(int M, int N, const uint16_t* residual, int64_t ldr, int act, const uint16_t* y, int64_t ldy) {
+  CHECK(act == ALD_ACT_NONE || act == ALD_ACT_GELU, ALD_E_INVALID);
+  if (y) CHECK(ldy >= N && M >= 0, ALD_E_INVALID);
+  if (residual) CHECK(ldr >= N, ALD_E_INVALID);
+  return ALD_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Carve {
+  uint8_t* base;
+  size_t off = 0;
+  size_t cap;
+  template <class T>
+  T* take(size_t n) {
+    T* p = reinterpret_cast<T*>(base + off);
+    off += align256(n * sizeof(T));
+    return p;
+  }
+  bool ok() const { return off <= cap; }
+};
+
+struct StepBuffers {
+  uint16_t* h;
+  uint16_t* big;
+  uint16_t* ao;
+  uint16_t* u;
+  int8_t* codes;
+  float* xs;
+  uint16_t* v;
+  int32_t* cu2;
+};
+
+// same carve used by dit_workspace_size (with base = nullptr) and dit_step
+size_t carve_step(const dit_config* c, int64_t n_tok, int R, uint8_t* base, size_t cap, StepBuffers* b) {
+  const int64_t M = 2 * n_tok;
+  const int64_t H = c->hidden, F = c->mlp, C = c->channels;
+  const int64_t rows_t = 2 * (int64_t)R * c->text_tokens;
+  const int64_t wide = std::max<int64_t>(3 * H, F);
+  const int64_t codes = std::max<int64_t>(M * std::max<int64_t>(H, F), rows_t * c->text_dim);
+  Carve cv{base, 0, cap};
+  StepBuffers t;
+  t.h = cv.take<uint16_t>(M * H);
+  t.big = cv.take<uint16_t>(M * wide);
+  t.ao = cv.take<uint16_t>(M * H);
+  t.u = cv.take<uint16_t>(M * H);
+  t.codes = cv.take<int8_t>(codes);
+  t.xs = cv.take<float>(std::max<int64_t>(M, rows_t));
+  t.v = cv.take<uint16_t>(M * C);
+  t.cu2 = cv.take<int32_t>(2 * (int64_t)R + 1);
+  if (b) *b = t;
+  return cv.off;
+}
+
+int check_config(const dit_config* c) {
+  CHECK(c, ALD_E_INVALID);
+  CHECK(c->n_blocks >= 0 && c->hidden > 0 && c->n_heads > 0 && c->mlp > 0 && c->channels > 0 &&
+            c->text_tokens > 0 && c->text_dim > 0,
+        ALD_E_INVALID);
+  CHECK(c->wmode == ALD_W8A8 || c->wmode == ALD_F16 || c->wmode == ALD_Q4, ALD_E_INVALID);
+  CHECK(c->head_dim == 64 && c->hidden == c->n_heads * 64, ALD_E_UNSUPPORTED);
+  CHECK(c->hidden % 16 == 0 && c->mlp % 16 == 0 && c->text_dim % 16 == 0 && c->channels % 8 == 0,
+        ALD_E_UNSUPPORTED);
+  if (c->wmode == ALD_Q4)
+    CHECK(c->hidden % 32 == 0 && c->mlp % 32 == 0 && c->text_dim % 32 == 0, ALD_E_UNSUPPORTED);
+  CHECK(c->hidden <= 8192 && c->mlp <= 8192 && c->text_dim <= 8192, ALD_E_UNSUPPORTED);
+  CHECK(c->hidden % 2 == 0, ALD_E_UNSUPPORTED);
+  CHECK(c->steer_block >= -1 && c->steer_block < c->n_blocks, ALD_E_INVALID);
+  CHECK(c->ln_eps >= 0.0f, ALD_E_INVALID);
+  return ALD_OK;
+}
+
+int check_linear(const dit_linear& l, int wmode) {
+  CHECK(l.w && al16(l.w), ALD_E_INVALID);
+  if (wmode != ALD_F16) CHECK(l.scale != nullptr, ALD_E_INVALID);
+  return ALD_OK;
+}
+
+int check_weights(const dit_config* c, const dit_weights* w) {
+  CHECK(w, ALD_E_INVALID);
+  CHECK(c->n_blocks == 0 || w->blocks, ALD_E_INVALID);
+  CHECK(w->w_in && w->b_in && w->lnf_g && w->lnf_b && w->w_out && w->b_out, ALD_E_INVALID);
+  CHECK(al16(w->w_in) && al16(w->w_out) && al16(w->lnf_g) && al16(w->lnf_b), ALD_E_INVALID);
+  for (int l = 0; l < c->n_blocks; ++l) {
+    const dit_block_weights& b = w->blocks[l];
+    CHECK(b.ln1_g && b.ln1_b && b.ln2_g && b.ln2_b && b.ln3_g && b.ln3_b, ALD_E_INVALID);
+    CHECK(al16(b.ln1_g) && al16(b.ln1_b) && al16(b.ln2_g) && al16(b.ln2_b) && al16(b.ln3_g) && al16(b.ln3_b),
+          ALD_E_INVALID);
+    const dit_linear* ls[7] = {&b.qkv, &b.o, &b.q, &b.kv, &b.ox, &b.up, &b.down};
+    for (auto* p : ls) {
+      int e = check_linear(*p, c->wmode);
+      if (e) return e;
+    }
+  }
+  return ALD_OK;
+}
+
+// y[M, N] = epilogue(A . W^T) for one block linear; A is int8 codes (W8A8,
+// with per-row scales xs) or fp16 (F16 / Q4)
+void run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, const float* xs, int M, int K, int N,
+                const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy, hipStream_t st) {
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.B = L.w;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi.bias = L.bias;
+  g.epi.residual = residual;
+  g.epi.ldr = ldr;
+  g.epi.y = y;
+  g.epi.ldy = ldy;
+  g.epi.act = act;
+  if (wmode == ALD_W8A8) {
+    g.epi.x_scale = xs;
+    g.epi.w_scale = static_cast<const float*>(L.scale);
+    launch_gemm(A_I8, B_I8, g, st);
+  } else if (wmode == ALD_Q4) {
+    g.b_scale = static_cast<const uint16_t*>(L.scale);
+    launch_gemm(A_F16, B_Q4, g, st);
+  } else {
+    launch_gemm(A_F16, B_F16, g, st);
+  }
+}
+
+// activation input of a linear: W8A8 quantizes per token, else fp16 as is
+struct ActIn {
+  const void* A;
+  int64_t lda;
+  const float* xs;
+};
+
+ActIn quantize_in(int wmode, const uint16_t* x, int64_t ldx, int M, int K, const StepBuffers& b, hipStream_t st) {
+  if (wmode == ALD_W8A8) {
+    launch_row_quant(x, ldx, M, K, b.codes, K, b.xs, st);
+    return {b.codes, K, b.xs};
+  }
+  return {x, ldx, nullptr};
+}
+
+ActIn layernorm_in(int wmode, const uint16_t* x, int M, int H, const float* g, const float* be, float eps,
+                   const StepBuffers& b, hipStream_t st) {
+  if (wmode == ALD_W8A8) {
+    launch_ln_quant(x, H, M, H, g, be, eps, nullptr, b.codes, b.xs, st);
+    return {b.codes, H, b.xs};
+  }
+  launch_ln_f16(x, H, M, H, g, be, eps, b.u, H, st);
+  return {b.u, H, nullptr};
+}
+
+int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args* a, void* ws, size_t ws_bytes,
+                 hipStream_t st) {
+  int e = check_config(c);
+  if (e) return e;
+  e = check_weights(c, w);
+  if (e) return e;
+  CHECK(a, ALD_E_INVALID);
+  CHECK(a->R > 0 && a->n_tok > 0, ALD_E_INVALID);
+  CHECK(a->x && al16(a->x) && a->text_kv && al16(a->text_kv), ALD_E_INVALID);
+  CHECK(a->t_cur && a->t_next && a->guidance, ALD_E_INVALID);
+  const bool varlen = a->cu_seqlens != nullptr;
+  if (varlen) {
+    CHECK(a->row_req && a->max_seq > 0, ALD_E_INVALID);
+  } else {
+    CHECK(a->seq > 0 && (int64_t)a->seq * a->R == a->n_tok, ALD_E_INVALID);
+  }
+  if (c->steer_block >= 0) CHECK(a->alpha && a->direction && al16(a->direction), ALD_E_INVALID);
+  if (a->renoise) CHECK(a->x0 && a->eps && al16(a->x0) && al16(a->eps), ALD_E_INVALID);
+  if (a->v_out) CHECK(al16(a->v_out), ALD_E_INVALID);
+  CHECK(2 * a->n_tok <= INT32_MAX, ALD_E_UNSUPPORTED);
+  CHECK(ws && al16(ws), ALD_E_INVALID);
+  StepBuffers b;
+  size_t need = carve_step(c, a->n_tok, a->R, static_cast<uint8_t*>(ws), ws_bytes, &b);
+  CHECK(need <= ws_bytes, ALD_E_WORKSPACE);
+  prepare();
+
+  const int H = c->hidden, F = c->mlp, C = c->channels, T = c->text_tokens, nh = c->n_heads;
+  const int64_t n_tok = a->n_tok;
+  const int M = (int)(2 * n_tok);
+  const int R = a->R;
+  const int wm = c->wmode;
+  RowMap map{n_tok, varlen ? 1 : a->seq, R, varlen ? a->row_req : nullptr};
+  const int max_sq = varlen ? a->max_seq : a->seq;
+  const int32_t* cu2 = nullptr;
+  if (varlen) {
+    launch_cu_pairs(a->cu_seqlens, R, n_tok, b.cu2, st);
+    cu2 = b.cu2;
+  }
+  if (a->renoise) launch_renoise(a->x, a->x0, a->eps, n_tok, C, map, a->t_cur, a->renoise, st);
+
+  // input projection of the fp32 latent (both CFG rows read the same latent) + time embedding
+  {
+    GemmArgs g;
+    g.A = a->x;
+    g.lda = C;
+    g.a_mod = n_tok;
+    g.B = w->w_in;
+    g.M = M;
+    g.N = H;
+    g.K = C;
+    g.epi.bias = w->b_in;
+    g.epi.y = b.h;
+    g.epi.ldy = H;
+    g.epi.temb_t = a->t_cur;
+    g.epi.n_tok = n_tok;
+    g.epi.rows_per_req = map.rows_per_req;
+    g.epi.row_req = map.row_req;
+    launch_gemm(A_F32, B_F16, g, st);
+  }
+
+  const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
+  for (int l = 0; l < c->n_blocks; ++l) {
+    const dit_block_weights& bw = w->blocks[l];
+    const uint16_t* kv = a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
+    // self-attention
+    ActIn in = layernorm_in(wm, b.h, M, H, bw.ln1_g, bw.ln1_b, c->ln_eps, b, st);
+    run_linear(bw.qkv, wm, in.A, in.lda, in.xs, M, H, 3 * H, nullptr, 0, 0, b.big, 3 * H, st);
+    AttnArgs at{b.big, b.big + H, b.big + 2 * H, b.ao, 3 * H, 3 * H, H, nh, a->seq, a->seq, cu2, cu2, sl2};
+    launch_attn(at, 2 * R, max_sq, st);
+    in = quantize_in(wm, b.ao, H, M, H, b, st);
+    run_linear(bw.o, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st);
+    // cross-attention to the text
+    in = layernorm_in(wm, b.h, M, H, bw.ln2_g, bw.ln2_b, c->ln_eps, b, st);
+    run_linear(bw.q, wm, in.A, in.lda, in.xs, M, H, H, nullptr, 0, 0, b.big, H, st);
+    AttnArgs ax{b.big, kv, kv + H, b.ao, H, 2 * H, H, nh, a->seq, T, cu2, nullptr, sl2};
+    launch_attn(ax, 2 * R, max_sq, st);
+    in = quantize_in(wm, b.ao, H, M, H, b, st);
+    run_linear(bw.ox, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st);
+    // GELU MLP
+    in = layernorm_in(wm, b.h, M, H, bw.ln3_g, bw.ln3_b, c->ln_eps, b, st);
+    run_linear(bw.up, wm, in.A, in.lda, in.xs, M, H, F, nullptr, 0, ALD_ACT_GELU, b.big, F, st);
+    in = quantize_in(wm, b.big, F, M, F, b, st);
+    run_linear(bw.down, wm, in.A, in.lda, in.xs, M, F, H, b.h, H, 0, b.h, H, st);
+    if (l == c->steer_block) {
+      if (a->block_norms) launch_row_norms(b.h, H, M, H, a->block_norms, st);
+      launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, st);
+    }
+  }
+
+  // final LayerNorm + output projection -> velocity of both CFG rows
+  launch_ln_f16(b.h, H, M, H, w->lnf_g, w->lnf_b, c->ln_eps, b.u, H, st);
+  uint16_t* v = a->v_out ? a->v_out : b.v;
+  {
+    GemmArgs g;
+    g.A = b.u;
+    g.lda = H;
+    g.B = w->w_out;
+    g.M = M;
+    g.N = C;
+    g.K = H;
+    g.epi.bias = w->b_out;
+    g.epi.y = v;
+    g.epi.ldy = C;
+    launch_gemm(A_F16, B_F16, g, st);
+  }
+  launch_cfg_euler(v, a->x, n_tok, C, map, a->guidance, a->t_cur, a->t_next, a->active, st);
+  return launched();
+}
+
+struct GraphHandle {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* ald_strerror(int code) {
+  switch (code) {
+    case ALD_OK: return "ok";
+    case ALD_E_INVALID: return "invalid argument (null, misaligned, negative size or bad enum)";
+    case ALD_E_UNSUPPORTED: return "unsupported shape or mode";
+    case ALD_E_WORKSPACE: return "workspace too small";
+    case ALD_E_LAUNCH: return "HIP launch error";
+    default: return "unknown error";
+  }
+}
+
+int ald_version(void) { return ALD_VERSION; }
+
+int quantize_rows_q8(const uint16_t* x, int64_t ldx, int M, int K, int8_t* q, int64_t ldq, float* scale,
+                     hipStream_t stream) {
+  CHECK(M >= 0 && K >= 0, ALD_E_INVALID);
+  if (M == 0) return ALD_OK;
+  CHECK(x && q && scale, ALD_E_INVALID);
+  CHECK(K % 8 == 0 && ldx >= K && ldq >= K && ldx % 8 == 0 && ldq % 8 == 0 && al16(x) && al8(q), ALD_E_INVALID);
+  CHECK(K <= 8192, ALD_E_UNSUPPORTED);
+  launch_row_quant(x, ldx, M, K, q, ldq, scale, stream);
+  return launched();
+}
+
+int quantize_q4(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* scales, hipStream_t stream) {
+  CHECK(N >= 0 && K >= 0, ALD_E_INVALID);
+  if (N == 0 || K == 0) return ALD_OK;
+  CHECK(w && packed && scales && al16(w) && al16(packed), ALD_E_INVALID);
+  CHECK(K % 32 == 0, ALD_E_UNSUPPORTED);
+  launch_q4_pack(w, N, K, packed, scales, stream);
+  return launched();
+}
+
+int ln_quant(const uint16_t* x, int64_t ldx, int M, int H, const float* gamma, const float* beta, float eps,
+             uint16_t* u_out, int8_t* q, float* scale, hipStream_t stream) {
+  CHECK(M >= 0 && H > 0, ALD_E_INVALID);
+  if (M == 0) return ALD_OK;
+  CHECK(x && gamma && beta && q && scale, ALD_E_INVALID);
+  CHECK(H % 8 == 0 && ldx >= H && ldx % 8 == 0 && al16(x) && al16(gamma) && al16(beta) && al8(q), ALD_E_INVALID);
+  if (u_out) CHECK(al16(u_out), ALD_E_INVALID);
+  CHECK(H <= 8192, ALD_E_UNSUPPORTED);
+  launch_ln_quant(x, ldx, M, H, gamma, beta, eps, u_out, q, scale, stream);
+  return launched();
+}
+
+int ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* gamma, const float* beta, float eps,
+           uint16_t* y, int64_t ldy, hipStream_t stream) {
+  CHECK(M >= 0 && H > 0, ALD_E_INVALID);
+  if (M == 0) return ALD_OK;
+  CHECK(x && gamma && beta && y, ALD_E_INVALID);
+  CHECK(H % 8 == 0 && ldx >= H && ldy >= H && ldx % 8 == 0 && ldy % 8 == 0 && al16(x) && al16(y) && al16(gamma) &&
+            al16(beta),
+        ALD_E_INVALID);
+  CHECK(H <= 8192, ALD_E_UNSUPPORTED);
+  launch_ln_f16(x, ldx, M, H, gamma, beta, eps, y, ldy, stream);
+  return launched();
+}
+
+int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, const float* w_scale, int N,
+                const float* bias, const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy,
+                int8_t* xq, float* x_scale, int32_t* acc, unsigned flags, hipStream_t stream) {
+  CHECK(M >= 0 && N >= 0 && K > 0, ALD_E_INVALID);
+  CHECK((flags & ~ALD_PREQUANT) == 0, ALD_E_INVALID);
+  int e = check_epilogue(M, N, residual, ldr, act, y, ldy);
+  if (e) return e;
+  if (M == 0 || N == 0) return ALD_OK;
+  CHECK(wq && w_scale && xq && x_scale && (y || acc), ALD_E_INVALID);
+  CHECK(K % 16 == 0 && al16(wq) && al16(xq), ALD_E_INVALID);
+  CHECK(K <= 8192, ALD_E_UNSUPPORTED);
+  if (!(flags & ALD_PREQUANT)) {
+    CHECK(x && al16(x) && ldx >= K && ldx % 8 == 0, ALD_E_INVALID);
+  }
+  prepare();
+  if (!(flags & ALD_PREQUANT)) launch_row_quant(x, ldx, M, K, xq, K, x_scale, stream);
+  GemmArgs g;
+  g.A = xq;
+  g.lda = K;
+  g.B = wq;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi.x_scale = x_scale;
+  g.epi.w_scale = w_scale;
+  g.epi.bias = bias;
+  g.epi.residual = residual;
+  g.epi.ldr = ldr;
+  g.epi.y = y;
+  g.epi.ldy = ldy;
+  g.epi.acc = acc;
+  g.epi.act = act;
+  launch_gemm(A_I8, B_I8, g, stream);
+  return launched();
+}
+
+int q4_linear(const uint16_t* x, int64_t ldx, int M, int K, const uint8_t* wq4, const uint16_t* w_scale, int N,
+              const float* bias, const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy,
+              hipStream_t stream) {
+  CHECK(M >= 0 && N >= 0 && K > 0, ALD_E_INVALID);
+  int e = check_epilogue(M, N, residual, ldr, act, y, ldy);
+  if (e) return e;
+  if (M == 0 || N == 0) return ALD_OK;
+  CHECK(x && wq4 && w_scale && y, ALD_E_INVALID);
+  CHECK(al16(x) && al16(wq4) && ldx >= K && ldx % 8 == 0, ALD_E_INVALID);
+  CHECK(K % 32 == 0, ALD_E_UNSUPPORTED);
+  prepare();
+  GemmArgs g;
+  g.A = x;
+  g.lda = ldx;
+  g.B = wq4;
+  g.b_scale = w_scale;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi.bias = bias;
+  g.epi.residual = residual;
+  g.epi.ldr = ldr;
+  g.epi.y = y;
+  g.epi.ldy = ldy;
+  g.epi.act = act;
+  launch_gemm(A_F16, B_Q4, g, stream);
+  return launched();
+}
+
+int f16_linear(const uint16_t* x, int64_t ldx, int M, int K, const uint16_t* w, int N, const float* bias,
+               const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy, hipStream_t stream) {
+  CHECK(M >= 0 && N >= 0 && K > 0, ALD_E_INVALID);
+  int e = check_epilogue(M, N, residual, ldr, act, y, ldy);
+  if (e) return e;
+  if (M == 0 || N == 0) return ALD_OK;
+  CHECK(x && w && y, ALD_E_INVALID);
+  CHECK(K % 8 == 0 && al16(x) && al16(w) && ldx >= K && ldx % 8 == 0, ALD_E_INVALID);
+  prepare();
+  GemmArgs g;
+  g.A = x;
+  g.lda = ldx;
+  g.B = w;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi.bias = bias;
+  g.epi.residual = residual;
+  g.epi.ldr = ldr;
+  g.epi.y = y;
+  g.epi.ldy = ldy;
+  g.epi.act = act;
+  launch_gemm(A_F16, B_F16, g, stream);
+  return launched();
+}
+
+int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t q_stride, int64_t kv_stride,
+             int n_heads, int head_dim, int batch, int Sq, int Sk, const int32_t* cu_seqlens_q,
+             const int32_t* cu_seqlens_k, int max_sq, int max_sk, float scale, uint16_t* out, int64_t o_stride,
+             hipStream_t stream) {
+  CHECK(n_heads > 0 && batch >= 0, ALD_E_INVALID);
+  CHECK(head_dim == 64, ALD_E_UNSUPPORTED);
+  if (batch == 0) return ALD_OK;
+  CHECK(q && k && v && out && al16(q) && al16(k) && al16(v) && al16(out), ALD_E_INVALID);
+  const int64_t width = (int64_t)n_heads * 64;
+  CHECK(q_stride >= width && kv_stride >= width && o_stride >= width, ALD_E_INVALID);
+  CHECK(q_stride % 8 == 0 && kv_stride % 8 == 0 && o_stride % 8 == 0, ALD_E_INVALID);
+  if (cu_seqlens_q) CHECK(max_sq >= 0, ALD_E_INVALID);
+  else CHECK(Sq >= 0, ALD_E_INVALID);
+  if (cu_seqlens_k) CHECK(max_sk >= 0, ALD_E_INVALID);
+  else CHECK(Sk >= 0, ALD_E_INVALID);
+  const int msq = cu_seqlens_q ? max_sq : Sq;
+  if (msq == 0) return ALD_OK;
+  AttnArgs a{q, k, v, out, q_stride, kv_stride, o_stride, n_heads, Sq, Sk, cu_seqlens_q, cu_seqlens_k,
+             scale * 1.4426950408889634f};
+  launch_attn(a, batch, msq, stream);
+  return launched();
+}
+
+int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R, const int32_t* row_req,
+              const float* alpha, float resid_norm, const float* dir, int mode, hipStream_t stream) {
+  CHECK(M >= 0 && H > 0, ALD_E_INVALID);
+  CHECK(mode == ALD_STEER_ADD || mode == ALD_STEER_PROJECT, ALD_E_INVALID);
+  CHECK(mode == ALD_STEER_ADD, ALD_E_UNSUPPORTED);
+  if (M == 0) return ALD_OK;
+  CHECK(h && alpha && dir && al16(h) && al16(dir), ALD_E_INVALID);
+  CHECK(H % 8 == 0 && ldh >= H && ldh % 8 == 0, ALD_E_INVALID);
+  if (!row_req) CHECK(rows_per_req > 0 && R > 0, ALD_E_INVALID);
+  RowMap map{0, row_req ? 1 : rows_per_req, row_req ? 1 : R, row_req};
+  launch_steer(h, ldh, M, H, map, alpha, resid_norm, dir, stream);
+  return launched();
+}
+
+int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req, const int32_t* row_req, const float* w,
+              float* v_hat, hipStream_t stream) {
+  CHECK(n_tok >= 0 && C > 0, ALD_E_INVALID);
+  if (n_tok == 0) return ALD_OK;
+  CHECK(v && w && v_hat && al16(v) && al16(v_hat), ALD_E_INVALID);
+  CHECK(C % 8 == 0, ALD_E_INVALID);
+  if (!row_req) CHECK(rows_per_req > 0, ALD_E_INVALID);
+  RowMap map{0, row_req ? 1 : rows_per_req, INT32_MAX, row_req};
+  launch_cfg_merge(v, n_tok, C, map, w, v_hat, stream);
+  return launched();
+}
+
+int sampler_update(int op, float* x, const float* v_hat, const float* x0, const float* eps, int64_t n_tok, int C,
+                   int rows_per_req, const int32_t* row_req, const float* t_cur, const float* t_next,
+                   const uint8_t* active, hipStream_t stream) {
+  CHECK(op == ALD_EULER || op == ALD_RENOISE, ALD_E_INVALID);
+  CHECK(n_tok >= 0 && C > 0, ALD_E_INVALID);
+  if (n_tok == 0) return ALD_OK;
+  CHECK(x && t_cur && al16(x) && C % 4 == 0, ALD_E_INVALID);
+  if (!row_req) CHECK(rows_per_req > 0, ALD_E_INVALID);
+  RowMap map{0, row_req ? 1 : rows_per_req, INT32_MAX, row_req};
+  if (op == ALD_EULER) {
+    CHECK(v_hat && t_next && al16(v_hat), ALD_E_INVALID);
+    launch_euler(x, v_hat, n_tok, C, map, t_cur, t_next, active, stream);
+  } else {
+    CHECK(x0 && eps && al16(x0) && al16(eps), ALD_E_INVALID);
+    launch_renoise(x, x0, eps, n_tok, C, map, t_cur, active, stream);
+  }
+  return launched();
+}
+
+size_t dit_workspace_size(const dit_config* cfg, int64_t max_tokens, int R) {
+  if (check_config(cfg) != ALD_OK || max_tokens < 0 || R < 0) return 0;
+  return carve_step(cfg, max_tokens, R, nullptr, SIZE_MAX, nullptr);
+}
+
+int dit_text_kv(const dit_config* c, const dit_weights* w, const uint16_t* text, int rows, uint16_t* kv_out,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  int e = check_config(c);
+  if (e) return e;
+  e = check_weights(c, w);
+  if (e) return e;
+  CHECK(rows >= 0, ALD_E_INVALID);
+  if (rows == 0 || c->n_blocks == 0) return ALD_OK;
+  CHECK(text && kv_out && ws && al16(text) && al16(kv_out) && al16(ws), ALD_E_INVALID);
+  const int Dt = c->text_dim, H = c->hidden;
+  size_t need = align256((size_t)rows * Dt) + align256((size_t)rows * 4);
+  CHECK(need <= ws_bytes, ALD_E_WORKSPACE);
+  prepare();
+  int8_t* codes = static_cast<int8_t*>(ws);
+  float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)rows * Dt));
+  const void* A = text;
+  int64_t lda = Dt;
+  if (c->wmode == ALD_W8A8) {
+    launch_row_quant(text, Dt, rows, Dt, codes, Dt, xs, stream);
+    A = codes;
+  }
+  for (int l = 0; l < c->n_blocks; ++l)
+    run_linear(w->blocks[l].kv, c->wmode, A, lda, xs, rows, Dt, 2 * H, nullptr, 0, 0,
+               kv_out + (int64_t)l * rows * 2 * H, 2 * H, stream);
+  return launched();
+}
+
+int dit_step(const dit_config* cfg, const dit_weights* w, const dit_step_args* args, void* ws, size_t ws_bytes,
+             hipStream_t stream) {
+  return enqueue_step(cfg, w, args, ws, ws_bytes, stream);
+}
+
+int dit_graph_capture(const dit_config* cfg, const dit_weights* w, const dit_step_args* args, int n_steps, void* ws,
+                      size_t ws_bytes, hipStream_t stream, void** graph_out) {
+  CHECK(args && graph_out && n_steps > 0, ALD_E_INVALID);
+  CHECK(stream != nullptr, ALD_E_INVALID);  // the legacy null stream cannot be captured
+  *graph_out = nullptr;
+  // validate every step before opening the capture
+  int e = check_config(cfg);
+  if (e) return e;
+  e = check_weights(cfg, w);
+  if (e) return e;
+  prepare();
+  if (hipStreamBeginCapture(stream, hipStreamCaptureModeRelaxed) != hipSuccess) return ALD_E_LAUNCH;
+  int rc = ALD_OK;
+  for (int i = 0; i < n_steps && rc == ALD_OK; ++i) rc = enqueue_step(cfg, w, &args[i], ws, ws_bytes, stream);
+  hipGraph_t graph = nullptr;
+  hipError_t ce = hipStreamEndCapture(stream, &graph);
+  if (rc != ALD_OK || ce != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc != ALD_OK ? rc : ALD_E_LAUNCH;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return ALD_E_LAUNCH;
+  }
+  GraphHandle* gh = new (std::nothrow) GraphHandle{graph, exec};
+  if (!gh) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return ALD_E_LAUNCH;
+  }
+  *graph_out = gh;
+  return ALD_OK;
+}
+
+int dit_graph_launch(void* graph, hipStream_t stream) {
+  CHECK(graph, ALD_E_INVALID);
+  GraphHandle* gh = static_cast<GraphHandle*>(graph);
+  return hipGraphLaunch(gh->exec, stream) == hipSuccess ? ALD_OK : ALD_E_LAUNCH;
+}
+
+int dit_graph_destroy(void* graph) {
+  CHECK(graph, ALD_E_INVALID);
+  GraphHandle* gh = static_cast<GraphHandle*>(graph);
+  (void)hipGraphExecDestroy(gh->exec);
+  (void)hipGraphDestroy(gh->graph);
+  delete gh;
+  return ALD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// Bandwidth-bound elementwise kernels: steering add, CFG merge, sampler
+// updates (Euler, warm-start re-noise), their fusion used inside the step,
+// per-row L2 norms (steering calibration) and the CFG-pair sequence offsets.
+// Every thread moves one 16-byte (fp16 x 8) or 16-byte (fp32 x 4) vector.
+#include "common.h"
+#include "kernels.h"
+
+namespace ald {
+
+__device__ __forceinline__ int req_of(const RowMap& m, int64_t row) {
+  int64_t i = m.n_tok_mod ? row % m.n_tok_mod : row;
+  return m.row_req ? m.row_req[i] : (int)((i / m.rows_per_req) % m.R);
+}
+
+// h[m, :] += (alpha[r] * resid_norm) * dir  -- rows with alpha == 0 untouched
+__global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, int64_t ldh, int M, int H, RowMap map,
+                                                    const float* __restrict__ alpha, float resid_norm,
+                                                    const float* __restrict__ dir) {
+  const int cpr = H >> 3;  // 8-element chunks per row
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * cpr) return;
+  const int64_t row = idx / cpr;
+  const int c = (int)(idx - row * cpr) * 8;
+  const float a = alpha[req_of(map, row)];
+  if (a == 0.0f) return;  // exact no-op: no write at all
+  const float coef = a * resid_norm;
+  uint16_t* p = h + row * ldh + c;
+  v4i raw = ld16(p);
+  uint16_t* hv = reinterpret_cast<uint16_t*>(&raw);
+  const float4 d0 = *reinterpret_cast<const float4*>(dir + c);
+  const float4 d1 = *reinterpret_cast<const float4*>(dir + c + 4);
+  const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hv[i] = f2h(h2f(hv[i]) + coef * dd[i]);
+  st16(p, raw);
+}
+
+__device__ __forceinline__ void load4h(const uint16_t* p, float f[4]) {
+  uint2 r = *reinterpret_cast<const uint2*>(p);
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = h2f(h[i]);
+}
+
+// v_hat = w * cond + (1 - w) * uncond, fp32
+__global__ __launch_bounds__(256) void cfg_merge_kernel(const uint16_t* __restrict__ v, int64_t n_tok, int C,
+                                                        RowMap map, const float* __restrict__ w,
+                                                        float* __restrict__ v_hat) {
+  const int cq = C >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tok * cq) return;
+  const int64_t tok = idx / cq;
+  const int c = (int)(idx - tok * cq) * 4;
+  const float wr = w[req_of(map, tok)];
+  const float wu = 1.0f - wr;
+  float fc[4], fu[4];
+  load4h(v + tok * C + c, fc);
+  load4h(v + (n_tok + tok) * C + c, fu);
+  float4 o;
+  o.x = wr * fc[0] + wu * fu[0];
+  o.y = wr * fc[1] + wu * fu[1];
+  o.z = wr * fc[2] + wu * fu[2];
+  o.w = wr * fc[3] + wu * fu[3];
+  *reinterpret_cast<float4*>(v_hat + tok * C + c) = o;
+}
+
+__global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ x, const float* __restrict__ v_hat,
+                                                    int64_t n_tok, int C, RowMap map, const float* __restrict__ t_cur,
+                                                    const float* __restrict__ t_next,
+                                                    const uint8_t* __restrict__ active) {
+  const int cq = C >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tok * cq) return;
+  const int64_t tok = idx / cq;
+  const int c = (int)(idx - tok * cq) * 4;
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const float dt = t_next[r] - t_cur[r];
+  float4* px = reinterpret_cast<float4*>(x + tok * C + c);
+  float4 xv = *px;
+  const float4 vv = *reinterpret_cast<const float4*>(v_hat + tok * C + c);
+  xv.x += dt * vv.x;
+  xv.y += dt * vv.y;
+  xv.z += dt * vv.z;
+  xv.w += dt * vv.w;
+  *px = xv;
+}
+
+__global__ __launch_bounds__(256) void renoise_kernel(float* __restrict__ x, const float* __restrict__ x0,
+                                                      const float* __restrict__ eps, int64_t n_tok, int C, RowMap map,
+                                                      const float* __restrict__ t_cur,
+                                                      const uint8_t* __restrict__ active) {
+  const int cq = C >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tok * cq) return;
+  const int64_t tok = idx / cq;
+  const int c = (int)(idx - tok * cq) * 4;
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const float t = t_cur[r];
+  const float s = 1.0f - t;
+  const float4 a = *reinterpret_cast<const float4*>(x0 + tok * C + c);
+  const float4 e = *reinterpret_cast<const float4*>(eps + tok * C + c);
+  float4 o;
+  o.x = s * a.x + t * e.x;
+  o.y = s * a.y + t * e.y;
+  o.z = s * a.z + t * e.z;
+  o.w = s * a.w + t * e.w;
+  *reinterpret_cast<float4*>(x + tok * C + c) = o;
+}
+
+// fused CFG merge + Euler for the step: v_hat never touches memory
+__global__ __launch_bounds__(256) void cfg_euler_kernel(const uint16_t* __restrict__ v, float* __restrict__ x,
+                                                        int64_t n_tok, int C, RowMap map, const float* __restrict__ w,
+                                                        const float* __restrict__ t_cur,
+                                                        const float* __restrict__ t_next,
+                                                        const uint8_t* __restrict__ active) {
+  const int cq = C >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tok * cq) return;
+  const int64_t tok = idx / cq;
+  const int c = (int)(idx - tok * cq) * 4;
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const float wr = w[r];
+  const float wu = 1.0f - wr;
+  const float dt = t_next[r] - t_cur[r];
+  float fc[4], fu[4];
+  load4h(v + tok * C + c, fc);
+  load4h(v + (n_tok + tok) * C + c, fu);
+  float4* px = reinterpret_cast<float4*>(x + tok * C + c);
+  float4 xv = *px;
+  float vh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vh[i] = wr * fc[i] + wu * fu[i];
+  xv.x += dt * vh[0];
+  xv.y += dt * vh[1];
+  xv.z += dt * vh[2];
+  xv.w += dt * vh[3];
+  *px = xv;
+}
+
+// per-row L2 norm (fp32), one wave per row
+__global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restrict__ h, int64_t ldh, int M, int H,
+                                                        float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const uint16_t* row = h + (int64_t)m * ldh;
+  float s = 0.0f;
+  for (int e = lane * 8; e < H; e += 512) {
+    v4i raw = ld16(row + e);
+    const uint16_t* hv = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float f = h2f(hv[i]);
+      s += f * f;
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[m] = sqrtf(s);
+}
+
+// offsets of the 2R CFG sequences: cond rows of every request, then uncond
+__global__ void cu_pairs_kernel(const int32_t* __restrict__ cu, int R, int64_t n_tok, int32_t* __restrict__ cu2) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b > 2 * R) return;
+  cu2[b] = b <= R ? cu[b] : (int32_t)(n_tok + cu[b - R]);
+}
+
+static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+
+void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
+                  const float* dir, hipStream_t st) {
+  int64_t n = (int64_t)M * (H / 8);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(steer_kernel, grid_for(n), dim3(256), 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+}
+
+void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,
+                      hipStream_t st) {
+  int64_t n = n_tok * (C / 4);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(cfg_merge_kernel, grid_for(n), dim3(256), 0, st, v, n_tok, C, map, w, v_hat);
+}
+
+void launch_euler(float* x, const float* v_hat, int64_t n_tok, int C, RowMap map, const float* t_cur,
+                  const float* t_next, const uint8_t* active, hipStream_t st) {
+  int64_t n = n_tok * (C / 4);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(euler_kernel, grid_for(n), dim3(256), 0, st, x, v_hat, n_tok, C, map, t_cur, t_next, active);
+}
+
+void launch_renoise(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
+                    const float* t_cur, const uint8_t* active, hipStream_t st) {
+  int64_t n = n_tok * (C / 4);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(renoise_kernel, grid_for(n), dim3(256), 0, st, x, x0, eps, n_tok, C, map, t_cur, active);
+}
+
+void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
+                      const float* t_cur, const float* t_next, const uint8_t* active, hipStream_t st) {
+  int64_t n = n_tok * (C / 4);
+  if (n <= 0) return;
+  hipLaunchKernelGGL(cfg_euler_kernel, grid_for(n), dim3(256), 0, st, v, x, n_tok, C, map, w, t_cur, t_next,
+                     active);
+}
+
+void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, h, ldh, M, H, out);
+}
+
+void launch_cu_pairs(const int32_t* cu, int R, int64_t n_tok, int32_t* cu2, hipStream_t st) {
+  hipLaunchKernelGGL(cu_pairs_kernel, grid_for(2 * R + 1), dim3(256), 0, st, cu, R, n_tok, cu2);
+}
+
+}  // namespace ald

@@ -1,0 +1,84 @@
+// Internal launchers shared by the C ABI (abi.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ald {
+
+enum AKind { A_I8 = 0, A_F16 = 1, A_F32 = 2 };
+enum BKind { B_I8 = 0, B_F16 = 1, B_Q4 = 2 };
+
+struct EpiArgs {
+  const float* x_scale = nullptr;   // [M]    (int8 A)
+  const float* w_scale = nullptr;   // [N]    (int8 B)
+  const float* bias = nullptr;      // [N]
+  const uint16_t* residual = nullptr;
+  int64_t ldr = 0;
+  uint16_t* y = nullptr;
+  int64_t ldy = 0;
+  int32_t* acc = nullptr;           // [M, N] raw accumulators (int8 path)
+  int act = 0;
+  // time embedding added per (row, col) (input projection)
+  const float* temb_t = nullptr;    // t per request
+  int64_t n_tok = 1;                // row -> token: row % n_tok
+  int rows_per_req = 1;             // token -> request: token / rows_per_req
+  const int32_t* row_req = nullptr; //   ... or row_req[token]
+};
+
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0;
+  int64_t a_mod = 1;                // fp32 A: source row = m % a_mod
+  const void* B = nullptr;          // [N, K] int8/fp16, or packed q4 [N, K/2]
+  const uint16_t* b_scale = nullptr;// q4 group scales [N, K/32]
+  int M = 0, N = 0, K = 0;
+  EpiArgs epi;
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  int64_t q_stride, kv_stride, o_stride;
+  int n_heads;
+  int Sq, Sk;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct RowMap {        // token / row -> request
+  int64_t n_tok_mod;   // row -> token: row % n_tok_mod (0: row itself)
+  int rows_per_req;    // token -> request: (token / rows_per_req) % R
+  int R;
+  const int32_t* row_req;  // or row_req[token]
+};
+
+void launch_row_quant(const uint16_t* x, int64_t ldx, int M, int K, int8_t* q, int64_t ldq, float* scale,
+                      hipStream_t st);
+void launch_ln_quant(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
+                     uint16_t* u_out, int8_t* q, float* scale, hipStream_t st);
+void launch_ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
+                   uint16_t* y, int64_t ldy, hipStream_t st);
+void launch_q4_pack(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* scales, hipStream_t st);
+
+void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st);
+void gemm_prepare();  // one-time kernel attributes (large dynamic LDS)
+
+void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st);
+
+void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
+                  const float* dir, hipStream_t st);
+void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,
+                      hipStream_t st);
+void launch_euler(float* x, const float* v_hat, int64_t n_tok, int C, RowMap map, const float* t_cur,
+                  const float* t_next, const uint8_t* active, hipStream_t st);
+void launch_renoise(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
+                    const float* t_cur, const uint8_t* active, hipStream_t st);
+void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
+                      const float* t_cur, const float* t_next, const uint8_t* active, hipStream_t st);
+void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st);
+void launch_cu_pairs(const int32_t* cu, int R, int64_t n_tok, int32_t* cu2, hipStream_t st);
+
+}  // namespace ald

@@ -1,0 +1,327 @@
+/*
+ * ald.h -- C ABI of the MI355X (gfx950) audio-latent DiT denoise step.
+ *
+ * One denoising step of a text-conditioned audio-latent diffusion transformer
+ * as described by "A Quantized Native Runtime for On-Device Semantic Audio
+ * Generation" (aria): a DiT denoiser over the audio latent that cross-attends
+ * to the text (Section II, reference model), run with 8-bit weights and
+ * 8-bit arithmetic (W8A8), 4-bit weights or half precision (Section III-A,
+ * runtime), with an activation-steering add at one block's output whose
+ * strength lives in device memory so that a captured step loop never needs
+ * re-capture (Section III, steering; the Chinese summary of the same paper
+ * gives the formula h <- h + alpha * ||h_bar|| * d_hat).  Classifier-free
+ * guidance runs the cond row and its null-prompt companion in one batch and
+ * merges them with w * cond + (1 - w) * uncond ("An Efficient vLLM-Based
+ * Inference Pipeline for Unified Audio Understanding and Generation",
+ * Section 2.4, Eq. (1)).  The sampler may warm-start from a cached clean
+ * latent forward-noised to an intermediate step ("SoundWeaver: Semantic
+ * Warm-Starting for Text-to-Audio Diffusion Serving", Section 2).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless a parameter says "host".
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and keeps no pointer between calls (the graph object of
+ *     dit_graph_capture is the one exception: it records the pointers it was
+ *     captured with, which must stay valid until it is destroyed).
+ *   - fp16 tensors are IEEE binary16 bit patterns passed as uint16_t.
+ *   - Matrices are row-major; leading dimensions (ld*) are in elements.
+ *   - All work is enqueued on `stream`; calls never synchronise the host,
+ *     never read device memory on the host, and can be captured into a
+ *     hipGraph.
+ *   - Arguments are validated on the host before any launch.  Return value:
+ *     ALD_OK, or a negative ALD_E_* code; on error nothing was enqueued.
+ *   - Vector accesses are 16 bytes wide: fp16/int8 row pointers and leading
+ *     dimensions must give 16-byte aligned rows (ALD_E_INVALID otherwise).
+ */
+#ifndef ALD_H
+#define ALD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ALD_VERSION 100
+
+enum {
+  ALD_OK = 0,
+  ALD_E_INVALID = -1,      /* null pointer, misalignment, negative size, bad enum   */
+  ALD_E_UNSUPPORTED = -2,  /* shape the kernels do not cover (e.g. head_dim != 64)  */
+  ALD_E_WORKSPACE = -3,    /* workspace smaller than dit_workspace_size()          */
+  ALD_E_LAUNCH = -4        /* the HIP runtime reported an error after a launch      */
+};
+
+/* Weight precision of the block linears (aria, Section III-A: the precision
+ * ladder fp16 / 8-bit / W8A8 / 4-bit). */
+enum { ALD_W8A8 = 0, ALD_F16 = 1, ALD_Q4 = 2 };
+
+/* Epilogue activation. */
+enum { ALD_ACT_NONE = 0, ALD_ACT_GELU = 1 };
+
+/* w8a8_linear flags. */
+#define ALD_PREQUANT 1u   /* xq / x_scale are inputs (already quantized); x unused */
+
+/* sampler_update ops. */
+enum { ALD_EULER = 0, ALD_RENOISE = 1 };
+
+/* steer_add modes (aria, Section III: add the direction, or project onto it). */
+enum { ALD_STEER_ADD = 0, ALD_STEER_PROJECT = 1 };
+
+const char* ald_strerror(int code);
+int ald_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Quantizers (aria, Section III-A: 8-bit weights, activations quantized   *
+ * alongside weights for W8A8, 4-bit weights).                             *
+ * ------------------------------------------------------------------------ */
+
+/* Symmetric per-row int8 quantization of an fp16 [M, K] matrix (per-token
+ * activation scales, or per-output-channel weight scales).
+ *   amax = max |x| of the row; scale[m] = fp32(amax / 127);
+ *   q = clamp(rint_half_even(fp32(x * fp32(127 / amax))), -127, 127);
+ *   amax == 0 gives scale 0 and zero codes.
+ * x [M, ldx] fp16; q [M, ldq] int8 out; scale [M] fp32 out.
+ * K % 8 == 0 and K <= 8192 (one row is held in registers). */
+int quantize_rows_q8(const uint16_t* x, int64_t ldx, int M, int K,
+                     int8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+
+/* 4-bit weight packing, groups of 32 along K with fp16 scales:
+ *   s = fp16(fp32(amax_g) / 7); q = clamp(rint(fp32(w) / fp32(s)), -7, 7)
+ *   (s == 0 gives zero codes); two's-complement nibbles, byte j of a row holds
+ *   k = 2j in the low nibble and k = 2j + 1 in the high nibble.
+ * w [N, K] fp16 (dense); packed [N, K/2] out; scales [N, K/32] fp16 out.
+ * K % 32 == 0. */
+int quantize_q4(const uint16_t* w, int N, int K, uint8_t* packed,
+                uint16_t* scales, hipStream_t stream);
+
+/* LayerNorm over H (fp32 statistics, biased variance, affine gamma/beta),
+ * rounded to fp16, then per-row int8 quantization of that fp16 row exactly
+ * as quantize_rows_q8.  u_out [M, H] fp16 (optional, NULL to skip) receives
+ * the fp16 LayerNorm output the codes were taken from; q [M, H] dense.
+ * H % 8 == 0, H <= 8192. */
+int ln_quant(const uint16_t* x, int64_t ldx, int M, int H, const float* gamma,
+             const float* beta, float eps, uint16_t* u_out, int8_t* q,
+             float* scale, hipStream_t stream);
+
+/* LayerNorm to fp16 without quantization: y [M, ldy]. */
+int ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* gamma,
+           const float* beta, float eps, uint16_t* y, int64_t ldy,
+           hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Linear layers.  Weights are output-major: W [N, K], y = x W^T.           *
+ * Epilogue (fp32, one rounding to fp16):                                   *
+ *   y = act(acc * dequant + bias) + residual                               *
+ * residual may alias y (in-place residual add: same ld required).          *
+ * ------------------------------------------------------------------------ */
+
+/* W8A8 linear (aria, Section III-A: 8-bit arithmetic on integer matrix
+ * units, activations quantized with the weights).
+ * Per-token dynamic quantization of x (as quantize_rows_q8) into xq/x_scale
+ * (caller buffers, [M, K] and [M]) unless flags & ALD_PREQUANT, in which case
+ * xq/x_scale are inputs and x may be NULL.  int8 x int8 -> int32 on MFMA;
+ * dequant acc * x_scale[m] * w_scale[n].
+ *   x [M, ldx] fp16; wq [N, K] int8 (dense); w_scale [N] fp32;
+ *   bias [N] fp32 or NULL; residual [M, ldr] fp16 or NULL; act ALD_ACT_*;
+ *   y [M, ldy] fp16 out (may be NULL when acc is given);
+ *   acc [M, N] int32 out or NULL: the raw accumulators (bit-exact observable).
+ * K % 16 == 0, K <= 8192. */
+int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K,
+                const int8_t* wq, const float* w_scale, int N,
+                const float* bias, const uint16_t* residual, int64_t ldr,
+                int act, uint16_t* y, int64_t ldy, int8_t* xq, float* x_scale,
+                int32_t* acc, unsigned flags, hipStream_t stream);
+
+/* 4-bit weight-only linear: W = fp16(q * s) dequantized inside the GEMM main
+ * loop, fp16 x fp16 -> fp32 on MFMA.  wq4 [N, K/2], w_scale [N, K/32] fp16
+ * (layout of quantize_q4).  K % 32 == 0. */
+int q4_linear(const uint16_t* x, int64_t ldx, int M, int K,
+              const uint8_t* wq4, const uint16_t* w_scale, int N,
+              const float* bias, const uint16_t* residual, int64_t ldr,
+              int act, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+/* fp16-weight linear (aria: half-precision matrix multiplies), fp32
+ * accumulation.  w [N, K] fp16 dense.  K % 8 == 0. */
+int f16_linear(const uint16_t* x, int64_t ldx, int M, int K,
+               const uint16_t* w, int N, const float* bias,
+               const uint16_t* residual, int64_t ldr, int act, uint16_t* y,
+               int64_t ldy, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Attention (aria: half-precision attention on the GPU path; the DiT       *
+ * self-attends over the latent and cross-attends to the text).             *
+ * ------------------------------------------------------------------------ */
+
+/* Non-causal softmax attention, fp16 in/out, fp32 softmax, head_dim 64.
+ * Token-major layouts: q[(row) * q_stride + h * 64 + c]; k and v share
+ * kv_stride; out[(row) * o_stride + h * 64 + c].
+ * Sequence b (0 <= b < batch) uses query rows
+ *   cu_seqlens_q ? [cu_q[b], cu_q[b+1]) : [b * Sq, (b+1) * Sq)
+ * and key rows
+ *   cu_seqlens_k ? [cu_k[b], cu_k[b+1]) : [b * Sk, (b+1) * Sk).
+ * With cu_seqlens, max_sq / max_sk bound the lengths (host values); lengths
+ * above them are a caller error (rows beyond are not computed).  A sequence
+ * with no keys writes zeros.  scale multiplies q.k (e.g. 1/sqrt(64)).
+ * head_dim must be 64 (ALD_E_UNSUPPORTED otherwise); strides % 8 == 0. */
+int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+             int64_t q_stride, int64_t kv_stride, int n_heads, int head_dim,
+             int batch, int Sq, int Sk, const int32_t* cu_seqlens_q,
+             const int32_t* cu_seqlens_k, int max_sq, int max_sk, float scale,
+             uint16_t* out, int64_t o_stride, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Steering, CFG merge, sampler.                                           *
+ * ------------------------------------------------------------------------ */
+
+/* Residual-stream steering add (aria, Section III; Chinese summary,
+ * activation steering): for every row m of h [M, ldh] fp16 with request
+ * r = row_req ? row_req[m] : (m / rows_per_req) % R,
+ *   h[m, :] = fp16(h[m, :] + (alpha[r] * resid_norm) * dir[:])   (fp32 math)
+ * alpha [R] fp32 is read on the device at execution time (a captured graph
+ * picks up new values without re-capture).  Rows with alpha[r] == 0 are not
+ * written at all, so the result is bit-identical to not calling.
+ * dir [H] fp32 unit direction.  mode: ALD_STEER_ADD only (ALD_STEER_PROJECT
+ * returns ALD_E_UNSUPPORTED).  H % 8 == 0. */
+int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R,
+              const int32_t* row_req, const float* alpha, float resid_norm,
+              const float* dir, int mode, hipStream_t stream);
+
+/* CFG merge (vLLM audio pipeline page, Section 2.4, Eq. (1)) on the model
+ * velocity: v [2 * n_tok, C] fp16 holds the cond rows [0, n_tok) then the
+ * uncond rows [n_tok, 2 n_tok); token i belongs to request
+ * r = row_req ? row_req[i] : i / rows_per_req, and
+ *   v_hat[i, c] = w[r] * cond + (1 - w[r]) * uncond   (fp32)
+ * w [R] fp32 device.  v_hat [n_tok, C] fp32 out. */
+int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req,
+              const int32_t* row_req, const float* w, float* v_hat,
+              hipStream_t stream);
+
+/* Sampler update on the fp32 latent x [n_tok, C]; token i -> request r as in
+ * cfg_merge; only requests with active[r] != 0 (or all, if active is NULL)
+ * are written.
+ *   ALD_EULER  : x += (t_next[r] - t_cur[r]) * v_hat       (flow-matching Euler)
+ *   ALD_RENOISE: x  = (1 - t_cur[r]) * x0 + t_cur[r] * eps (warm start,
+ *                SoundWeaver Section 2: forward-noise a cached clean latent
+ *                to the skip time; eps is supplied by the caller).
+ * Unused pointers (v_hat for RENOISE; x0, eps, t_next for EULER) may be NULL. */
+int sampler_update(int op, float* x, const float* v_hat, const float* x0,
+                   const float* eps, int64_t n_tok, int C, int rows_per_req,
+                   const int32_t* row_req, const float* t_cur,
+                   const float* t_next, const uint8_t* active,
+                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * The whole step.                                                         *
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+  int n_blocks;
+  int hidden;        /* H                              */
+  int n_heads;       /* H / 64                         */
+  int head_dim;      /* must be 64                     */
+  int mlp;           /* F                              */
+  int channels;      /* latent channels C              */
+  int text_tokens;   /* T                              */
+  int text_dim;      /* D_t                            */
+  int wmode;         /* ALD_W8A8 | ALD_F16 | ALD_Q4    */
+  int steer_block;   /* block whose output is steered; -1: none */
+  float ln_eps;
+} dit_config;
+
+/* One linear layer's weights in the precision of dit_config.wmode:
+ *   ALD_W8A8: w = int8 [N, K], scale = fp32 [N]
+ *   ALD_F16 : w = fp16 [N, K], scale = NULL
+ *   ALD_Q4  : w = uint8 [N, K/2], scale = fp16 [N, K/32]
+ * bias fp32 [N]. */
+typedef struct {
+  const void* w;
+  const void* scale;
+  const float* bias;
+} dit_linear;
+
+/* Pre-LN residual block (reading of the pages' DiT): self-attention,
+ * cross-attention to the text, GELU MLP, each h += f(LN(h)).
+ * Shapes (N x K): qkv 3H x H, o H x H, q H x H, kv 2H x D_t, ox H x H,
+ * up F x H, down H x F.  LayerNorm params fp32 [H]. */
+typedef struct {
+  const float *ln1_g, *ln1_b, *ln2_g, *ln2_b, *ln3_g, *ln3_b;
+  dit_linear qkv, o, q, kv, ox, up, down;
+} dit_block_weights;
+
+typedef struct {
+  const dit_block_weights* blocks; /* HOST array [n_blocks] of device pointers */
+  const uint16_t* w_in;  /* fp16 [H, C]  input projection            */
+  const float* b_in;     /* fp32 [H]                                  */
+  const float* lnf_g;    /* fp32 [H]     final LayerNorm             */
+  const float* lnf_b;
+  const uint16_t* w_out; /* fp16 [C, H]  output projection           */
+  const float* b_out;    /* fp32 [C]                                  */
+} dit_weights;
+
+/* Arguments of one step over R requests (2R CFG rows).
+ * Latent rows are request-packed: request r owns tokens
+ *   cu_seqlens ? [cu[r], cu[r+1]) : [r * seq, (r+1) * seq).
+ * The hidden state holds the cond rows of all tokens, then the uncond rows.
+ * All per-request arrays are device fp32 [R] read at execution time. */
+typedef struct {
+  float* x;                   /* fp32 [n_tok, C] latent state, updated in place */
+  const uint16_t* text_kv;    /* fp16 [n_blocks][2R * T, 2H] from dit_text_kv */
+  int R;
+  int seq;                    /* tokens per request when cu_seqlens == NULL     */
+  const int32_t* cu_seqlens;  /* int32 [R + 1] or NULL                          */
+  const int32_t* row_req;     /* int32 [n_tok] request of each token; required
+                                 with cu_seqlens, ignored otherwise             */
+  int64_t n_tok;              /* total latent tokens (host)                     */
+  int max_seq;                /* longest request (host); = seq when dense       */
+  const float* t_cur;
+  const float* t_next;
+  const float* guidance;      /* CFG weight w per request                       */
+  const float* alpha;         /* steering strength per request for this step    */
+  float resid_norm;           /* ||h_bar|| of the steered block (host)          */
+  const float* direction;     /* fp32 [H] unit steering direction               */
+  const uint8_t* active;      /* uint8 [R]: requests whose latent is updated, or NULL (all) */
+  const uint8_t* renoise;     /* uint8 [R]: requests re-noised at t_cur before the pass, or NULL */
+  const float* x0;            /* fp32 [n_tok, C] cached clean latent (renoise)  */
+  const float* eps;           /* fp32 [n_tok, C] re-noising draw (renoise)      */
+  uint16_t* v_out;            /* optional fp16 [2 n_tok, C]: model velocity     */
+  float* block_norms;         /* optional fp32 [2 n_tok]: per-row L2 norm of the
+                                 steered block's output before steering         */
+} dit_step_args;
+
+/* Workspace bytes needed by dit_step / dit_text_kv for up to max_tokens
+ * latent tokens (n_tok) and R requests. */
+size_t dit_workspace_size(const dit_config* cfg, int64_t max_tokens, int R);
+
+/* Step-invariant text keys/values: kv_out[l] = linear_kv_l(text) for every
+ * block l, fp16 [n_blocks][rows, 2H].  text [rows, D_t] fp16 (the 2R CFG
+ * rows x T tokens; the uncond rows are zeros, the null prompt). */
+int dit_text_kv(const dit_config* cfg, const dit_weights* w,
+                const uint16_t* text, int rows, uint16_t* kv_out, void* ws,
+                size_t ws_bytes, hipStream_t stream);
+
+/* One denoising step: input projection + time embedding, n_blocks DiT
+ * blocks (steering add after block steer_block), final LayerNorm + output
+ * projection, CFG merge, Euler update (with optional warm-start re-noise
+ * first).  Enqueues only; capturable. */
+int dit_step(const dit_config* cfg, const dit_weights* w,
+             const dit_step_args* args, void* ws, size_t ws_bytes,
+             hipStream_t stream);
+
+/* Capture n_steps consecutive dit_step calls (args: HOST array [n_steps])
+ * into one hipGraph on `stream` (aria: the per-step denoising loop is
+ * captured once and replayed as a single GPU graph; per-step t, alpha and w
+ * are read from device memory, so new values need no re-capture).
+ * *graph_out receives an opaque handle. */
+int dit_graph_capture(const dit_config* cfg, const dit_weights* w,
+                      const dit_step_args* args, int n_steps, void* ws,
+                      size_t ws_bytes, hipStream_t stream, void** graph_out);
+int dit_graph_launch(void* graph, hipStream_t stream);
+int dit_graph_destroy(void* graph);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ALD_H */

@@ -1,0 +1,150 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, and its host-side validation rejects bad arguments before any launch
+(no GPU needed: every call here fails validation, so nothing touches HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from audio_latent_diffusion_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ald.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-null "device" address, never dereferenced on the host
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_lists_the_binding_exports():
+    assert header_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.ald_version() == 100
+    assert lib.ald_strerror(L.ALD_E_WORKSPACE) == b"workspace too small"
+
+
+def test_gemm_validation():
+    lib = L.lib()
+    # null weights
+    assert lib.w8a8_linear(FAKE, 64, 4, 64, None, FAKE, 8, None, None, 0, 0, FAKE, 8, FAKE, FAKE, None, 0,
+                           None) == L.ALD_E_INVALID
+    # K not a multiple of 16
+    assert lib.w8a8_linear(FAKE, 72, 4, 24, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, FAKE, FAKE, None, 0,
+                           None) == L.ALD_E_INVALID
+    # misaligned activation pointer
+    assert lib.w8a8_linear(FAKE + 2, 64, 4, 64, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, FAKE, FAKE, None, 0,
+                           None) == L.ALD_E_INVALID
+    # unknown flag, bad activation
+    assert lib.w8a8_linear(FAKE, 64, 4, 64, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, FAKE, FAKE, None, 4,
+                           None) == L.ALD_E_INVALID
+    assert lib.w8a8_linear(FAKE, 64, 4, 64, FAKE, FAKE, 8, None, None, 0, 7, FAKE, 8, FAKE, FAKE, None, 0,
+                           None) == L.ALD_E_INVALID
+    # K beyond the register-resident quantizer
+    assert lib.w8a8_linear(FAKE, 16384, 4, 16384, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, FAKE, FAKE, None, 0,
+                           None) == L.ALD_E_UNSUPPORTED
+    # empty problems are a no-op success
+    assert lib.w8a8_linear(None, 64, 0, 64, None, None, 8, None, None, 0, 0, None, 8, None, None, None, 0,
+                           None) == L.ALD_OK
+    assert lib.q4_linear(FAKE, 64, 4, 48, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_UNSUPPORTED
+    assert lib.f16_linear(FAKE, 64, 4, 64, None, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_INVALID
+    assert lib.quantize_q4(FAKE, 4, 48, FAKE, FAKE, None) == L.ALD_E_UNSUPPORTED
+    assert lib.quantize_rows_q8(FAKE, 64, 4, 60, FAKE, 64, FAKE, None) == L.ALD_E_INVALID
+
+
+def test_attention_and_elementwise_validation():
+    lib = L.lib()
+    assert lib.attn_fwd(FAKE, FAKE, FAKE, 128, 128, 2, 128, 1, 8, 8, None, None, 0, 0, 0.1, FAKE, 128,
+                        None) == L.ALD_E_UNSUPPORTED  # head_dim 128
+    assert lib.attn_fwd(FAKE, FAKE, FAKE, 64, 64, 2, 64, 1, 8, 8, None, None, 0, 0, 0.1, FAKE, 128,
+                        None) == L.ALD_E_INVALID      # stride narrower than n_heads * 64
+    assert lib.attn_fwd(None, FAKE, FAKE, 128, 128, 2, 64, 1, 8, 8, None, None, 0, 0, 0.1, FAKE, 128,
+                        None) == L.ALD_E_INVALID
+    assert lib.steer_add(FAKE, 64, 4, 64, 4, 1, None, FAKE, 1.0, FAKE, L.ALD_STEER_PROJECT,
+                         None) == L.ALD_E_UNSUPPORTED
+    assert lib.steer_add(FAKE, 64, 4, 64, 4, 1, None, FAKE, 1.0, FAKE, 9, None) == L.ALD_E_INVALID
+    assert lib.steer_add(FAKE, 64, 4, 64, 0, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_INVALID
+    assert lib.cfg_merge(FAKE, 10, 64, 0, None, FAKE, FAKE, None) == L.ALD_E_INVALID
+    assert lib.sampler_update(5, FAKE, FAKE, None, None, 10, 64, 10, None, FAKE, FAKE, None, None) == L.ALD_E_INVALID
+    assert lib.sampler_update(L.ALD_RENOISE, FAKE, None, None, FAKE, 10, 64, 10, None, FAKE, None, None,
+                              None) == L.ALD_E_INVALID
+
+
+def _cfg(**kw):
+    d = dict(n_blocks=2, hidden=256, n_heads=4, head_dim=64, mlp=1024, channels=64, text_tokens=32, text_dim=256,
+             wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5)
+    d.update(kw)
+    return L.dit_config(**d)
+
+
+def _weights(n):
+    arr = (L.dit_block_weights * n)()
+    for i in range(n):
+        b = arr[i]
+        for nm in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "ln3_g", "ln3_b"):
+            setattr(b, nm, FAKE)
+        for nm in ("qkv", "o", "q", "kv", "ox", "up", "down"):
+            setattr(b, nm, L.dit_linear(FAKE, FAKE, FAKE))
+    w = L.dit_weights(ctypes.cast(arr, ctypes.POINTER(L.dit_block_weights)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    return w, arr
+
+
+def test_workspace_size():
+    lib = L.lib()
+    c = _cfg()
+    n = lib.dit_workspace_size(ctypes.byref(c), 64, 1)
+    M, H, F = 128, 256, 1024
+    assert n >= 2 * M * H + 2 * M * 3 * H + 2 * M * H * 2 + M * F
+    assert lib.dit_workspace_size(ctypes.byref(c), 128, 1) > n
+    bad = _cfg(head_dim=128)
+    assert lib.dit_workspace_size(ctypes.byref(bad), 64, 1) == 0
+
+
+def test_step_validation():
+    lib = L.lib()
+    c = _cfg()
+    w, arr = _weights(2)
+    a = L.dit_step_args(x=FAKE, text_kv=FAKE, R=1, seq=64, n_tok=64, max_seq=64, t_cur=FAKE, t_next=FAKE,
+                        guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE)
+    need = lib.dit_workspace_size(ctypes.byref(c), 64, 1)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), FAKE, need - 1,
+                        None) == L.ALD_E_WORKSPACE
+    bad = _cfg(head_dim=32, n_heads=8)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_UNSUPPORTED
+    bad = _cfg(steer_block=2)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    bad = _cfg(wmode=7)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    a2 = L.dit_step_args(x=FAKE, text_kv=FAKE, R=1, seq=60, n_tok=64, max_seq=64, t_cur=FAKE, t_next=FAKE,
+                         guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a2), FAKE, need, None) == L.ALD_E_INVALID
+    a3 = L.dit_step_args(x=FAKE, text_kv=FAKE, R=1, seq=64, n_tok=64, max_seq=64, t_cur=FAKE, t_next=FAKE,
+                         guidance=FAKE, alpha=None, resid_norm=1.0, direction=FAKE)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a3), FAKE, need, None) == L.ALD_E_INVALID
+    a4 = L.dit_step_args(x=FAKE, text_kv=FAKE, R=2, seq=0, cu_seqlens=FAKE, row_req=None, n_tok=64, max_seq=64,
+                         t_cur=FAKE, t_next=FAKE, guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a4), FAKE, need, None) == L.ALD_E_INVALID
+    arr[1].qkv = L.dit_linear(None, FAKE, FAKE)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    h = ctypes.c_void_p()
+    assert lib.dit_graph_capture(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), 0, FAKE, need, FAKE,
+                                 ctypes.byref(h)) == L.ALD_E_INVALID
+    assert lib.dit_graph_launch(None, None) == L.ALD_E_INVALID
+    assert lib.dit_graph_destroy(None) == L.ALD_E_INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        L.lib()

@@ -1,0 +1,286 @@
+"""Per-kernel parity of the HIP path (through the C ABI) against the oracle.
+
+Bit-exact: int8 codes, per-row scales, int32 accumulators, q4 codes/scales.
+Floating point: tolerances derived from one fp16 rounding after fp32
+accumulation (see tests/_gpu.py).  Shapes cover tiny, ragged (not a tile
+multiple in M, N or K), several tiles, and the mid/serve workload shapes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from audio_latent_diffusion_amd import binding as B
+from audio_latent_diffusion_amd import _lib as L
+from oracle import ald_oracle as O
+from tests._gpu import dev, f16_close, host, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------- quantizers
+
+@pytest.mark.parametrize("M,K", [(1, 8), (7, 136), (64, 256), (33, 1024), (5, 6144), (3, 8192)])
+def test_quantize_rows_bit_exact(M, K):
+    r = rng(M * 1000 + K)
+    x = (r.standard_normal((M, K)) * r.uniform(0.01, 30, (M, 1))).astype(np.float16)
+    x[0, : min(8, K)] = [0.5, 1.5, 2.5, -0.5, 3.5, -2.5, 126.5, 127][: min(8, K)]
+    if M > 2:
+        x[2] = 0
+    q, s = B.quantize_rows_q8(dev(x))
+    qo, so = O.quantize_rows_q8(x)
+    assert np.array_equal(host(q), qo)
+    assert host(s).tobytes() == so.tobytes()
+
+
+def test_quantize_rows_strided_input():
+    x = rng(1).standard_normal((20, 96)).astype(np.float16)
+    xt = dev(x)
+    q, s = B.quantize_rows_q8(xt[:, 16:80])
+    qo, so = O.quantize_rows_q8(x[:, 16:80])
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 96), (130, 256), (1536, 1536)])
+def test_quantize_q4_bit_exact(N, K):
+    w = (0.02 * rng(N + K).standard_normal((N, K))).astype(np.float16)
+    w[0, :32] = 0
+    p, s = B.quantize_q4(dev(w))
+    po, so = O.quantize_q4(w)
+    assert np.array_equal(host(p), po)
+    assert np.array_equal(host(s).view(np.uint16), so.view(np.uint16))
+
+
+@pytest.mark.parametrize("M,H", [(1, 64), (13, 256), (128, 1024), (40, 1536), (9, 2048)])
+def test_ln_quant(M, H):
+    r = rng(M + H)
+    x = (r.standard_normal((M, H)) * 2 + 0.5).astype(np.float16)
+    g = (1 + 0.02 * r.standard_normal(H)).astype(np.float32)
+    b = (0.02 * r.standard_normal(H)).astype(np.float32)
+    u = torch.empty((M, H), dtype=torch.float16, device="cuda")
+    q, s = B.ln_quant(dev(x), dev(g), dev(b), 1e-5, u_out=u)
+    uo = O.layer_norm(x, g, b, 1e-5)
+    ug = host(u)
+    f16_close(ug, uo, rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    # the codes are bit-exactly the quantization of the fp16 row they came from
+    qo, so = O.quantize_rows_q8(ug)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s), so)
+    y = B.ln_f16(dev(x), dev(g), dev(b), 1e-5)
+    assert np.array_equal(host(y), ug)
+
+
+# ------------------------------------------------------------- W8A8 GEMM
+
+W8A8_SHAPES = [(1, 16, 1), (3, 32, 7), (77, 272, 130), (128, 256, 768), (200, 1024, 257), (512, 1024, 3072),
+               (130, 6144, 96)]
+
+
+@pytest.mark.parametrize("M,K,N", W8A8_SHAPES)
+def test_w8a8_linear(M, K, N):
+    r = rng(M * 7 + K * 3 + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    wq, ws = O.quantize_rows_q8(w)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = B.w8a8_linear(dev(x), dev(wq), dev(ws), bias=dev(b), residual=dev(res), xq=xq, x_scale=xs, acc=acc)
+    ro = O.w8a8_linear(x, wq, ws, b, residual=res)
+    assert np.array_equal(host(xq), ro.xq)
+    assert np.array_equal(host(xs), ro.x_scale)
+    assert np.array_equal(host(acc).astype(np.int64), ro.acc)
+    f16_close(host(y), ro.y)
+
+
+def test_w8a8_gelu_inplace_residual_and_prequant():
+    r = rng(9)
+    M, K, N = 96, 512, 384
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.05 * r.standard_normal((N, K))).astype(np.float16)
+    wq, ws = O.quantize_rows_q8(w)
+    # GELU epilogue
+    y = B.w8a8_linear(dev(x), dev(wq), dev(ws), act=L.ALD_ACT_GELU)
+    f16_close(host(y), O.w8a8_linear(x, wq, ws, None, act=1).y)
+    # in-place residual (residual aliases y)
+    h = r.standard_normal((M, N)).astype(np.float16)
+    ht = dev(h)
+    B.w8a8_linear(dev(x), dev(wq), dev(ws), residual=ht, y=ht)
+    f16_close(host(ht), O.w8a8_linear(x, wq, ws, None, residual=h).y)
+    # pre-quantized input
+    xq, xs = O.quantize_rows_q8(x)
+    y2 = B.w8a8_linear(None, dev(wq), dev(ws), xq=dev(xq), x_scale=dev(xs), prequant=True)
+    assert np.array_equal(host(y2), host(B.w8a8_linear(dev(x), dev(wq), dev(ws))))
+
+
+@pytest.mark.parametrize("M,K,N", [(8192, 1536, 4608), (8192, 6144, 1536)])
+def test_w8a8_serve_shapes_sampled(M, K, N):
+    """Full serving-batch shapes in the launch configuration of the step;
+    accumulators checked on sampled rows against the exact integer GEMM."""
+    g = torch.Generator(device="cuda").manual_seed(M + K + N)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    xs = torch.rand(M, device="cuda", generator=g) * 0.01
+    ws = torch.rand(N, device="cuda", generator=g) * 0.001
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, acc=acc, prequant=True)
+    rows = np.sort(rng(0).choice(M, 48, replace=False))
+    rows = np.concatenate([rows, [0, M - 1]])
+    a = host(xq)[rows]
+    ref = O.int_gemm(a, host(wq))
+    assert np.array_equal(host(acc)[rows].astype(np.int64), ref)
+    yo = (ref * host(xs)[rows, None].astype(np.float64) * host(ws)[None, :].astype(np.float64)).astype(np.float16)
+    f16_close(host(y)[rows], yo)
+
+
+# ------------------------------------------------------------- fp16 and q4 GEMMs
+
+@pytest.mark.parametrize("M,K,N", [(1, 8, 1), (77, 264, 130), (256, 1024, 64), (300, 2048, 520)])
+def test_f16_linear(M, K, N):
+    r = rng(M + K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.05 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    y = B.f16_linear(dev(x), dev(w), dev(b), residual=dev(res))
+    f16_close(host(y), O.f16_linear(x, w, b, residual=res))
+    y = B.f16_linear(dev(x), dev(w), dev(b), act=L.ALD_ACT_GELU)
+    f16_close(host(y), O.f16_linear(x, w, b, act=1))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (77, 96, 130), (256, 2048, 64), (300, 1024, 520)])
+def test_q4_linear(M, K, N):
+    r = rng(M * 3 + K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    p, s = O.quantize_q4(w)
+    y = B.q4_linear(dev(x), dev(p), dev(s), dev(b), residual=dev(res))
+    f16_close(host(y), O.q4_linear(x, p, s, b, residual=res))
+
+
+# ------------------------------------------------------------- attention
+
+def _attn_ref(q, k, v, nh, cu_q, cu_k):
+    return O.attention_varlen(q, k, v, cu_q, cu_k, nh, 0.125)
+
+
+@pytest.mark.parametrize("B_,Sq,Sk,nh", [(1, 1, 1, 1), (2, 64, 32, 4), (2, 100, 77, 3), (1, 256, 256, 2),
+                                          (3, 130, 200, 2), (16, 512, 128, 1)])
+def test_attention_dense(B_, Sq, Sk, nh):
+    r = rng(B_ * 100 + Sq + Sk)
+    W = nh * 64
+    q = r.standard_normal((B_ * Sq, W)).astype(np.float16)
+    k = r.standard_normal((B_ * Sk, W)).astype(np.float16)
+    v = r.standard_normal((B_ * Sk, W)).astype(np.float16)
+    out = B.attn_fwd(dev(q), dev(k), dev(v), nh, B_, Sq, Sk)
+    ref = _attn_ref(q, k, v, nh, np.arange(B_ + 1) * Sq, np.arange(B_ + 1) * Sk)
+    f16_close(host(out), ref, rtol=2.0 ** -8, atol_frac=2.0 ** -8)
+
+
+def test_attention_strided_qkv_views():
+    r = rng(5)
+    S, nh = 96, 3
+    H = nh * 64
+    qkv = r.standard_normal((2 * S, 3 * H)).astype(np.float16)
+    t = dev(qkv)
+    out = B.attn_fwd(t[:, :H], t[:, H:2 * H], t[:, 2 * H:], nh, 2, S, S)
+    cu = np.arange(3) * S
+    ref = _attn_ref(qkv[:, :H], qkv[:, H:2 * H], qkv[:, 2 * H:], nh, cu, cu)
+    f16_close(host(out), ref, rtol=2.0 ** -8, atol_frac=2.0 ** -8)
+
+
+def test_attention_varlen_and_empty():
+    r = rng(6)
+    lens_q = [128, 1, 0, 577, 64, 200]
+    lens_k = [128, 1, 5, 577, 0, 33]
+    nh = 2
+    W = nh * 64
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = r.standard_normal((cq[-1], W)).astype(np.float16)
+    k = r.standard_normal((ck[-1], W)).astype(np.float16)
+    v = r.standard_normal((ck[-1], W)).astype(np.float16)
+    out = B.attn_fwd(dev(q), dev(k), dev(v), nh, len(lens_q), cu_seqlens_q=dev(cq), cu_seqlens_k=dev(ck),
+                     max_sq=max(lens_q), max_sk=max(lens_k))
+    ref = _attn_ref(q, k, v, nh, cq, ck)
+    f16_close(host(out), ref, rtol=2.0 ** -8, atol_frac=2.0 ** -8)
+
+
+def test_attention_single_key_and_uniform():
+    r = rng(7)
+    nh, S = 2, 70
+    q = r.standard_normal((S, nh * 64)).astype(np.float16)
+    k = r.standard_normal((1, nh * 64)).astype(np.float16)
+    v = r.standard_normal((1, nh * 64)).astype(np.float16)
+    out = host(B.attn_fwd(dev(q), dev(k), dev(v), nh, 1, S, 1))
+    assert np.array_equal(out, np.broadcast_to(v, out.shape))        # one key: weight exactly 1
+    kk = np.broadcast_to(k, (40, nh * 64)).copy()
+    vv = r.standard_normal((40, nh * 64)).astype(np.float16)
+    out = host(B.attn_fwd(dev(q), dev(kk), dev(vv), nh, 1, S, 40))
+    f16_close(out, np.broadcast_to(vv.astype(np.float64).mean(axis=0), out.shape), rtol=2.0 ** -9,
+              atol_frac=2.0 ** -9)
+
+
+# ------------------------------------------------------------- steering, CFG, sampler
+
+def test_steer_add():
+    r = rng(8)
+    M, H, S, R = 4 * 96, 256, 96, 2
+    h = r.standard_normal((M, H)).astype(np.float16)
+    h[5, 3] = np.float16(-0.0)
+    d = r.standard_normal(H)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    alpha = np.array([0.5, 0.0], np.float32)
+    ht = dev(h)
+    B.steer_add(ht, dev(alpha), 3.25, dev(d), rows_per_req=S, R=R)
+    got = host(ht)
+    row_req = (np.arange(M) // S) % R
+    ref = O.steer_add(h, alpha[row_req], 3.25, d)
+    f16_close(got, ref, rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    untouched = row_req == 1
+    assert got[untouched].tobytes() == h[untouched].tobytes()
+    # alpha = 0 everywhere: bit-identical
+    ht = dev(h)
+    B.steer_add(ht, dev(np.zeros(2, np.float32)), 3.25, dev(d), rows_per_req=S, R=R)
+    assert host(ht).tobytes() == h.tobytes()
+
+
+def test_cfg_merge_and_sampler():
+    r = rng(9)
+    R, S, C = 3, 50, 64
+    n = R * S
+    v = r.standard_normal((2 * n, C)).astype(np.float16)
+    w = np.array([3.0, 1.0, 0.0], np.float32)
+    vh = host(B.cfg_merge(dev(v), dev(w), rows_per_req=S))
+    req = np.arange(n) // S
+    ref = O.cfg_merge(v[:n], v[n:], w[req][:, None])
+    assert np.allclose(vh, ref, rtol=1e-6, atol=1e-6)
+    assert np.array_equal(vh[req == 1], v[:n][req == 1].astype(np.float32))   # w = 1: cond branch
+    assert np.array_equal(vh[req == 2], v[n:][req == 2].astype(np.float32))   # w = 0: uncond branch
+    x = r.standard_normal((n, C)).astype(np.float32)
+    tc = np.array([1.0, 0.5, 0.25], np.float32)
+    tn = np.array([0.875, 0.375, 0.0], np.float32)
+    act = np.array([1, 0, 1], np.uint8)
+    xt = dev(x)
+    B.sampler_update(L.ALD_EULER, xt, dev(tc), dev(tn), v_hat=dev(ref), rows_per_req=S, active=dev(act))
+    xe = O.euler_update(x, ref, tc[req][:, None], tn[req][:, None])
+    xe[req == 1] = x[req == 1]
+    assert np.allclose(host(xt), xe, rtol=1e-6, atol=1e-6)
+    x0 = r.standard_normal((n, C)).astype(np.float32)
+    eps = r.standard_normal((n, C)).astype(np.float32)
+    tt = np.array([0.0, 1.0, 0.4375], np.float32)
+    xt = dev(x)
+    B.sampler_update(L.ALD_RENOISE, xt, dev(tt), x0=dev(x0), eps=dev(eps), rows_per_req=S)
+    got = host(xt)
+    assert np.array_equal(got[req == 0], x0[req == 0])      # t = 0: the cached latent
+    assert np.array_equal(got[req == 1], eps[req == 1])     # t = 1: pure noise
+    assert np.allclose(got, O.renoise(x0, eps, tt[req][:, None]), rtol=1e-6, atol=1e-6)

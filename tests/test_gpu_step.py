@@ -1,0 +1,147 @@
+"""End-to-end parity of the denoise step (dit_step / hipGraph) against the oracle.
+
+Bar: the step's output latent within 2e-2 normwise relative error
+(max |g - o| / max |o|); alpha = 0 bit-identical to the unsteered pass;
+graph replay bit-identical to eager; packed varlen requests bit-identical to
+one request at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ald_inputs as I
+from audio_latent_diffusion_amd import runtime
+from oracle import ald_oracle as O
+from tests._gpu import host, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+TOL = 2e-2
+RESID = 5.0
+
+
+def _runner(model, inp, resid=RESID, **kw):
+    return runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
+                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps, **kw)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = I.TINY
+    p = I.make_params(cfg)
+    return cfg, p, runtime.DiTModel(cfg, p), O.prepare_model(cfg, p)
+
+
+def _oracle_steps(om, inp, steps, resid=RESID):
+    kv = O.text_kv(om, inp.text)
+    x, tr = O.run_sampler(om, inp, kv, resid_norm=resid, steps=steps)
+    return x, tr
+
+
+@pytest.mark.parametrize("wmode", ["w8a8", "f16", "q4"])
+def test_tiny_step_parity(wmode):
+    cfg = I.TINY.replace(wmode=wmode)
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    run = _runner(runtime.DiTModel(cfg, p), inp, keep_velocity=True)
+    run.step(0)
+    got = host(run.x)
+    ref, tr = _oracle_steps(O.prepare_model(cfg, p), inp, [0])
+    err = O.normwise_rel_err(got, ref)
+    verr = O.normwise_rel_err(host(run.v_out), tr[0].v)
+    print(f"tiny {wmode}: latent err {err:.2e}, velocity err {verr:.2e}")
+    assert err < TOL
+    assert verr < 5e-2
+
+
+def test_alpha_zero_bit_identical(tiny):
+    cfg, p, model, _ = tiny
+    inp = I.make_inputs(cfg)
+    inp.alpha[:] = 0
+    a = _runner(model, inp)
+    b = _runner(model.with_steer_block(-1), inp)
+    a.step(0)
+    b.step(0)
+    assert host(a.x).tobytes() == host(b.x).tobytes()
+    inp.alpha[:] = 0.5
+    c = _runner(model, inp)
+    c.step(0)
+    assert not np.array_equal(host(c.x), host(a.x))
+
+
+def test_graph_replay_equals_eager_and_no_recapture(tiny):
+    cfg, p, model, om = tiny
+    cfg8 = cfg.replace(steer_steps=(2, 3, 4, 5))
+    inp = I.make_inputs(cfg8)
+    eager = _runner(model, inp)
+    for i in range(8):
+        eager.step(i)
+    g = _runner(model, inp)
+    g.capture()
+    g.replay()
+    assert host(g.x).tobytes() == host(eager.x).tobytes()
+    # new steering strengths written into device memory, same graph
+    x_init = torch.from_numpy(inp.x).cuda()
+    g.x.copy_(x_init)
+    new_alpha = np.zeros_like(inp.alpha)
+    new_alpha[4:8] = 0.25
+    g.alpha.copy_(torch.from_numpy(new_alpha).cuda())
+    g.replay()
+    inp2 = I.make_inputs(cfg8)
+    inp2.alpha = new_alpha
+    e2 = _runner(model, inp2)
+    for i in range(8):
+        e2.step(i)
+    assert host(g.x).tobytes() == host(e2.x).tobytes()
+    # and the 8-step result matches the oracle sampler
+    ref, _ = _oracle_steps(om, inp2, None)
+    assert O.normwise_rel_err(host(g.x), ref) < TOL
+
+
+def test_varlen_warm_start_parity(tiny):
+    cfg, p, model, om = tiny
+    cfg3 = cfg.replace(requests=3, n_steps=4)
+    inp = I.make_mixed_inputs(cfg3, seqlens=np.array([16, 33, 64]), warm=np.array([False, True, True]))
+    inp.start_step = np.array([0, 1, 2])
+    run = _runner(model, inp)
+    for i in range(4):
+        run.step(i)
+    ref, _ = _oracle_steps(om, inp, None)
+    assert O.normwise_rel_err(host(run.x), ref) < TOL
+
+
+def test_packed_equals_single_requests(tiny):
+    cfg, p, model, _ = tiny
+    lens = np.array([40, 64, 17])
+    cfg3 = cfg.replace(requests=3, n_steps=2)
+    inp = I.make_mixed_inputs(cfg3, seqlens=lens, warm=np.zeros(3, bool))
+    inp.alpha[:] = 0.5
+    packed = _runner(model, inp)
+    packed.step(0)
+    got = host(packed.x)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = cfg.text_tokens
+    for r in range(3):
+        sl = slice(cu[r], cu[r + 1])
+        one = I.make_mixed_inputs(cfg.replace(requests=1, n_steps=2), seqlens=lens[r:r + 1], warm=np.zeros(1, bool))
+        one.x = inp.x[sl]
+        one.text = inp.text[[r, 3 + r]]
+        one.guidance = inp.guidance[r:r + 1]
+        one.alpha = inp.alpha[:, r:r + 1]
+        single = _runner(model, one)
+        single.step(0)
+        assert host(single.x).tobytes() == got[sl].tobytes(), f"request {r}"
+
+
+def test_mid_step_parity():
+    """The mid-size model (16 blocks, hidden 1024): one steered step, full size."""
+    cfg = I.MID
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, p)
+    run = _runner(model, inp)
+    run.step(2)  # inside the steering span
+    ref, _ = O.run_sampler(O.prepare_model(cfg, p), inp, resid_norm=RESID, steps=[2])
+    err = O.normwise_rel_err(host(run.x), ref)
+    print(f"mid step 2: err {err:.2e}")
+    assert err < TOL
