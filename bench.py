@@ -1,0 +1,232 @@
+"""Denoise-step throughput of the DiT hot path on one MI355X.
+
+Workload (mid-size DiT): 16 blocks, hidden 1024, 16 heads, MLP 4096 (GELU),
+latent 256 x 64, cross-attention to 128 text tokens of dim 768, one request
+as a CFG pair (batch 2, guidance 3), W8A8 weights with per-token dynamic
+activation scales, 8 Euler steps on the uniform t grid captured once as one
+hipGraph, steering (alpha 0.5 at block 12) active in steps 2-5 only.
+Synthetic seeded inputs and random weights of that shape.
+
+One timed unit is one replay of the 8-step graph (a whole sampler pass of a
+fresh request: the latent is reset from its initial noise first); `value` is
+denoise steps per second.  The JSON line also carries the roofline of the
+dominant kernel (the W8A8 GEMM, timed live with HIP events on its own launch
+stream at the step's shapes), the W8A8 GEMM at the serving-batch shapes
+(hidden 1536, 8192 tokens) as % of the int8 MFMA peak, and the CPU oracle
+timed on a bounded sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, TFLOP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+
+def _events_time(fn, iters, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters  # ms
+
+
+def gemm_mix_timing(cfg, iters=50):
+    """Average launch time of the W8A8 GEMM over the step's per-block launch
+    mix (qkv, o, q, ox, up, down at M = 2 R S tokens), on torch's current
+    stream, which is the stream the launches go to."""
+    import torch
+    from audio_latent_diffusion_amd import binding as B
+    H, F = cfg.hidden, cfg.mlp
+    M = cfg.tokens
+    shapes = [(H, 3 * H), (H, H), (H, H), (H, H), (H, F), (F, H)]  # (K, N)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    bufs = []
+    for K, N in shapes:
+        xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        xs = torch.rand(M, device="cuda", generator=g) * 1e-2
+        ws = torch.rand(N, device="cuda", generator=g) * 1e-3
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        bufs.append((xq, wq, xs, ws, y))
+
+    def run_mix():
+        for xq, wq, xs, ws, y in bufs:
+            B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, y=y, prequant=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        run_mix()
+    ms_mix = _events_time(run_mix, iters, stream)
+    ops = sum(2.0 * M * N * K for K, N in shapes)
+    byts = sum(M * K + N * K + 2 * M * N + 4 * (M + N) for K, N in shapes)
+    return ms_mix / len(shapes), ops / len(shapes), byts / len(shapes)
+
+
+def serve_gemm(iters=20):
+    """W8A8 GEMM at the serving-batch shapes (8192 tokens, hidden 1536)."""
+    import torch
+    from audio_latent_diffusion_amd import binding as B
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(1)
+    total_ops, total_ms = 0.0, 0.0
+    for name, (M, K, N) in {"qkv": (8192, 1536, 4608), "o": (8192, 1536, 1536), "up": (8192, 1536, 6144),
+                            "down": (8192, 6144, 1536)}.items():
+        xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        xs = torch.rand(M, device="cuda", generator=g) * 1e-2
+        ws = torch.rand(N, device="cuda", generator=g) * 1e-3
+        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        fn = lambda: B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, y=y, prequant=True)  # noqa: E731
+        for _ in range(3):
+            fn()
+        ms = _events_time(fn, iters, torch.cuda.current_stream())
+        ops = 2.0 * M * N * K
+        out[name] = {"M": M, "K": K, "N": N, "ms": round(ms, 4), "tops": round(ops / ms / 1e9, 1),
+                     "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4)}
+        total_ops += ops
+        total_ms += ms
+    tops = total_ops / total_ms / 1e9
+    return {"shapes": out, "tops": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+
+
+def cpu_baseline(cfg, params, inp, resid, budget_s=20.0):
+    """The oracle, as it stands, on the host cores: denoise steps of the same
+    workload, as many whole steps as fit the budget (at least one)."""
+    from oracle import ald_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    om = O.prepare_model(cfg, params)
+    kv = O.text_kv(om, inp.text)
+    x = inp.x
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        i = n % cfg.n_steps
+        x, _ = O.dit_step(om, x, inp.seqlens, kv, np.full(1, inp.t_grid[i], np.float32),
+                          np.full(1, inp.t_grid[i + 1], np.float32), inp.guidance, inp.alpha[i], resid,
+                          inp.direction)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s or n >= cfg.n_steps:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} denoise step(s) of the mid-size DiT (same shapes, CFG pair) in {dt:.1f} s; "
+                      f"fp64 numpy oracle with BLAS matmuls, text K/V and weight packing excluded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed replays of the 8-step graph")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests shard across GPUs with no per-step exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ald_inputs as I
+    from audio_latent_diffusion_amd import runtime
+
+    cfg = I.MID
+    params = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, params)
+
+    # steering unit: mean per-token residual norm at the steered block over the
+    # 8 steps of the alpha = 0 run (a calibration input, outside the timed region)
+    zero = I.make_inputs(cfg)
+    zero.alpha[:] = 0
+    cal = runtime.StepRunner(model, zero.x, zero.text, zero.seqlens, zero.t_grid, zero.guidance, zero.alpha,
+                             zero.direction, 0.0)
+    cal.collect_block_norms()
+    norms = []
+    for i in range(cfg.n_steps):
+        cal.step(i)
+        norms.append(cal.block_norms.double().mean().item())
+    resid = float(np.mean(norms))
+    del cal
+
+    run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
+                             inp.direction, resid)
+    x_init = run.x.clone()
+    run.capture()
+
+    def one_pass():
+        run.x.copy_(x_init)
+        run.replay()
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    ms_pass = _events_time(one_pass, args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_steps = cfg.n_steps * args.steps
+    steps_per_s = n_steps / wall
+    ev_steps_per_s = cfg.n_steps / (ms_pass / 1e3)
+    ok = bool(torch.isfinite(run.x).all().item())
+
+    ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
+    achieved = ops_launch / (ms_launch / 1e3) / 1e12
+    serve = serve_gemm()
+
+    line = {
+        "metric": "DiT denoise steps/s (CFG batch) + W8A8 GEMM % of int8 MFMA peak on 1 GPU",
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / n_steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "mid-size DiT, 16 blocks, hidden 1024, 16 heads, MLP 4096, latent 256x64, "
+                               "text 128x768, CFG batch 2, W8A8, 8 Euler steps as one hipGraph, "
+                               "steering alpha 0.5 at block 12 in steps 2-5",
+                   "global_batch": cfg.cfg_rows, "seq_len": cfg.seq, "parallelism": "none",
+                   "denoise_steps_per_replay": cfg.n_steps, "attention_dtype": "fp16"},
+        "event_steps_per_s": round(ev_steps_per_s, 2),
+        "finite": ok,
+        "roofline": {"bound": "mfma", "kernel": "w8a8 GEMM (int8 MFMA), step launch mix at M=512",
+                     "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "avg_launch_us": round(ms_launch * 1e3, 2),
+                     "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
+        "w8a8_gemm_serve": serve,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(cfg, params, inp, resid, args.cpu_budget)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

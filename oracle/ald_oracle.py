@@ -470,9 +470,8 @@ def run_sampler(model: PreparedModel, inp, kv=None, resid_norm: float = 0.0,
     re-noised to t_{start} just before its first step (SoundWeaver, Section 2).
     Returns the final latent and the per-step traces.
     """
-    cfg = model.cfg
-    N = cfg.n_steps
     tg = np.asarray(inp.t_grid, F32)
+    N = len(tg) - 1
     if kv is None:
         kv = text_kv(model, inp.text)
     x = np.array(inp.x, dtype=F32, copy=True)
