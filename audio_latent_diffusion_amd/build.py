@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libald.so")
-SOURCES = ["quant.hip", "gemm.hip", "attention.hip", "elementwise.hip", "abi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_dma.hip", "attention.hip", "elementwise.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 

@@ -350,6 +350,7 @@ static void set_lds() {
 }
 
 void gemm_prepare() {
+  gemm_dma_prepare();
   set_lds<A_I8, B_I8, 128, 128>();
   set_lds<A_I8, B_I8, 128, 64>();
   set_lds<A_F16, B_F16, 128, 128>();
@@ -361,6 +362,10 @@ void gemm_prepare() {
 
 void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return;
+  if (gemm_dma_applicable(akind, bkind, g)) {
+    launch_gemm_dma(akind, g, st);
+    return;
+  }
   const bool narrow = g.N <= 64;
   if (akind == A_I8 && bkind == B_I8) {
     if (narrow) launch_tile<A_I8, B_I8, 128, 64>(g, st);

@@ -1,0 +1,465 @@
+// Pipelined MFMA GEMM for the DiT linears: y[M, N] = epilogue(X[M, K] . W[N, K]^T)
+// with both operands K-contiguous, fed by direct global -> LDS loads.
+//
+//  * int8 x int8 -> int32 on v_mfma_i32_32x32x32_i8 (W8A8; epilogue
+//    acc * x_scale[m] * w_scale[n] + bias (+GELU) (+residual) -> fp16, and an
+//    optional raw int32 accumulator dump), or
+//  * fp16 x fp16 -> fp32 on v_mfma_f32_32x32x16_f16 (fp16 weights).
+//
+// Both MFMAs take, per operand, a 32-row x 32-byte fragment: lane l holds row
+// l % 32 and the 16 bytes at 16 (l / 32) of the 32-byte K slice.  Only the
+// pairing of K positions between the two operands matters for a dot product,
+// so any K order inside a slice is correct when both operands share it.
+// (The 32x32 shapes run at the full matrix rate with a few independent
+// accumulators; the 16x16 int8 shape needs many more to hide its latency.)
+//
+// A K stage is 128 bytes of every tile row (one cache line per row).  LDS
+// holds a stage as blocks of 8 rows x 128 bytes (1 KB), written by
+// global_load_lds_dwordx4: lane l of a wave fetches row l / 8 of the block and
+// the hardware stores its 16 bytes at slot l.  The lane picks which 16-byte
+// chunk of the row it fetches: slot p of row r holds chunk p ^ g(r) with
+// g(r) = (r & 7) ^ ((r >> 3) & 1), so that the 16 rows read together by an
+// MFMA operand load (same chunk, consecutive rows) fall on distinct banks.
+// Each operand fragment is then one ds_read_b128 per lane.  No VGPR staging:
+// a ring of STAGES buffers keeps STAGES - 1 stages in flight.
+//
+// Per K stage: wait until this wave's loads of stage kt have landed
+// (s_waitcnt vmcnt with the count of loads issued after them), barrier (every
+// wave's loads of stage kt visible, every wave done with stage kt - 1), issue
+// the loads of stage kt + STAGES - 1 into the buffer of stage kt - 1, then
+// run the four 32-byte K slices of the stage.  Fragment reads are double
+// buffered in registers: the reads of slice s + 1 are issued before the MFMAs
+// of slice s, so LDS latency hides behind matrix work.
+//
+// Operand roles are swapped in the MFMA (W fragment first): accumulator
+// register r of lane l then holds output row l % 32 and column
+// 8 (r / 4) + 4 (l / 32) + r % 4 of its 32x32 block.  The epilogue stages the
+// accumulators through LDS and writes 8 consecutive fp16 per lane (16-byte
+// stores); the epilogue kind (plain, residual, GELU) is a template parameter
+// so no kernel carries code it does not run.
+//
+// Workgroups are mapped XCD-aware: consecutive workgroup ids land on
+// different XCDs (round-robin), so tile ids are remapped to give each XCD one
+// contiguous run of row-major tiles (tiles sharing X rows share its L2).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace ald {
+namespace {
+
+constexpr int BLK = 1024;  // LDS block: one DMA instruction (64 lanes x 16 bytes)
+
+// epilogue kinds
+enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };
+
+template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
+  static constexpr int KB = 128;           // K bytes per stage and row (one cache line)
+  static constexpr int RPB = BLK / KB;     // rows per LDS block (8)
+  static constexpr int CPR = KB / 16;      // 16-byte chunks per row (8)
+  static constexpr int KS = KB / 32;       // 32-byte MFMA K slices per stage (4)
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int MI = WM / 32, NJ = WN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int BX = BM / RPB, BW = BN / RPB;  // LDS blocks per stage
+  static constexpr int STAGE_BYTES = (BX + BW) * BLK;
+  static constexpr int LDS = STAGES * STAGE_BYTES;
+  static constexpr int LOADS = (BX + BW) / WAVES;   // DMA instructions per wave per stage
+  // epilogue staging: PW columns per pass, rows padded by 4 words, plus the row scales
+  static constexpr int PW = WN < 64 ? WN : 64;
+  static constexpr int RS = PW + 4;
+  static constexpr int EPI_LDS = WAVES * WM * (RS + 1) * 4;
+  // per-row and per-column epilogue scalars (x_scale[BM], w_scale[BN], bias[BN])
+  static constexpr int SC_OFF = LDS > EPI_LDS ? LDS : EPI_LDS;
+  static constexpr int LDS_TOTAL = SC_OFF + (BM + 2 * BN) * 4;
+  static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per DMA instruction
+  static_assert((BX + BW) % WAVES == 0, "blocks must split evenly over the waves");
+  static_assert(MI >= 1 && NJ >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scalar loads cover whole tiles");
+};
+
+// s_waitcnt vmcnt(N): expcnt and lgkmcnt fields left at their maxima
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// wait until the oldest outstanding stage has landed: at most `ahead` later
+// stages (LOADS instructions each) may remain in flight (vector memory loads
+// retire in issue order)
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      vm_wait<LOADS * MAXA>();
+      return;
+    }
+    wait_stages<LOADS, MAXA - 1>(ahead);
+  } else {
+    vm_wait<0>();
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// bank swizzle: chunk c of tile row r sits at slot c ^ g(r) of its 128-byte
+// row, so that the 16 (or 8) consecutive rows read together with one chunk
+// index cover distinct banks
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <class C>
+struct Loader {
+  const uint8_t* src[C::LOADS];  // this lane's source at K offset 0
+  int dst[C::LOADS];             // LDS byte offset of the block within a stage
+
+  __device__ void init(const uint8_t* X, int64_t ldx_b, int M, const uint8_t* W, int64_t ldw_b, int N, int m0,
+                       int n0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int b = wave + C::WAVES * i;  // block index within the stage
+      const bool isx = b < C::BX;
+      const int bb = isx ? b : b - C::BX;
+      const int tr = bb * C::RPB + lane / C::CPR;  // tile row
+      const int rows = isx ? M : N;
+      int r = (isx ? m0 : n0) + tr;
+      r = r < rows ? r : rows - 1;  // rows past the edge re-read a valid row; their results are dropped
+      const int chunk = (lane % C::CPR) ^ swz(tr);
+      const uint8_t* base = isx ? X : W;
+      const int64_t ld = isx ? ldx_b : ldw_b;
+      src[i] = base + (int64_t)r * ld + chunk * 16;
+      dst[i] = b * BLK;
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* stage, int kbyte) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kbyte), (lds_void*)(stage + dst[i]), 16, 0,
+                                       0);
+  }
+};
+
+__device__ __forceinline__ int xcd_tile(int bid, int nt) {
+  const int q = nt >> 3, rem = nt & 7;
+  const int x = bid & 7, loc = bid >> 3;
+  return x * q + (x < rem ? x : rem) + loc;
+}
+
+// GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (|error of erf| <= 1.5e-7): erf(z) = 1 - poly(t) exp(-z^2),
+// t = 1 / (1 + p z), z >= 0, odd extension for z < 0.
+__device__ __forceinline__ float gelu_as(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float erf_abs = 1.0f - poly * __expf(-z * z);
+  return 0.5f * x * (1.0f + copysignf(erf_abs, x));
+}
+
+__device__ __forceinline__ void unpack_h8(uint4 raw, float f[8]) {
+  const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    f[2 * r] = h2f((uint16_t)(w4[r] & 0xFFFFu));
+    f[2 * r + 1] = h2f((uint16_t)(w4[r] >> 16));
+  }
+}
+
+template <class C, bool INT>
+__device__ __forceinline__ void mfma_slice(typename std::conditional<INT, v16i, v16f>::type (&acc)[C::NJ][C::MI],
+                                           const v4i (&xf)[C::MI], const v4i (&wf)[C::NJ]) {
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      if constexpr (INT) {
+        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], xf[i], acc[j][i], 0, 0, 0);
+      } else {
+        acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wf[j]),
+                                                           __builtin_bit_cast(v8h, xf[i]), acc[j][i], 0, 0, 0);
+      }
+    }
+}
+
+template <class C, bool INT, int EPI>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int nt = gridDim.x;
+  const int t = xcd_tile(blockIdx.x, nt);
+  const int m0 = (t / tiles_n) * C::BM, n0 = (t % tiles_n) * C::BN;
+
+  constexpr int EB = INT ? 1 : 2;  // bytes per element
+  const int nk = g.K * EB / C::KB;
+
+  Loader<C> ld;
+  ld.init(static_cast<const uint8_t*>(g.A), g.lda * EB, g.M, static_cast<const uint8_t*>(g.B), (int64_t)g.K * EB,
+          g.N, m0, n0, wave, lane);
+
+  typedef typename std::conditional<INT, v16i, v16f>::type Acc;
+  Acc acc[C::NJ][C::MI];
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+
+  // the epilogue's per-row / per-column scalars travel to LDS first; they
+  // are older than every stage copy, so the stage waits cover them too
+  {
+    const EpiArgs& e = g.epi;
+    float* sc = reinterpret_cast<float*>(smem + C::SC_OFF);
+#pragma unroll
+    for (int i = wave; i < C::SC_LOADS; i += C::WAVES) {
+      const int q = i * 64 + lane;  // x_scale rows, then w_scale columns, then bias columns
+      const float* src;
+      if (q < C::BM) src = e.x_scale ? e.x_scale + min(m0 + q, g.M - 1) : nullptr;
+      else if (q < C::BM + C::BN) src = e.w_scale ? e.w_scale + min(n0 + q - C::BM, g.N - 1) : nullptr;
+      else src = e.bias ? e.bias + min(n0 + q - C::BM - C::BN, g.N - 1) : nullptr;
+      if (src) {  // a missing operand (null pointer) is uniform over the wave
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(sc + i * 64), 4, 0, 0);
+      } else {
+        sc[q] = (q >= C::BM + C::BN) ? 0.0f : 1.0f;
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) ld.issue(smem + s * C::STAGE_BYTES, s * C::KB);
+
+  // fragment (32-row block, 32-byte slice ks) of lane l: row l % 32, chunk 2 ks + l / 32
+  const int lr = lane & 31;
+  const int lane_off = (lr / C::RPB) * BLK + (lr % C::RPB) * C::KB;
+  const int g_l = swz(lr);
+  int koff[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = lane_off + (((2 * ks + (lane >> 5)) ^ g_l) << 4);
+  constexpr int B32 = 32 / C::RPB * BLK;  // bytes of 32 tile rows
+  const int xbase = wm * C::MI * B32;
+  const int wbase = C::BX * BLK + wn * C::NJ * B32;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(C::STAGES - 2, nk - 1 - kt);
+    wait_stages<C::LOADS, C::STAGES - 2>(ahead);
+    __builtin_amdgcn_s_barrier();
+    const int kn = kt + C::STAGES - 1;
+    if (kn < nk) ld.issue(smem + (kn % C::STAGES) * C::STAGE_BYTES, kn * C::KB);
+    const uint8_t* sx = smem + (kt % C::STAGES) * C::STAGE_BYTES + xbase;
+    const uint8_t* sw = smem + (kt % C::STAGES) * C::STAGE_BYTES + wbase;
+    v4i xf[2][C::MI], wf[2][C::NJ];
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) xf[0][i] = *reinterpret_cast<const v4i*>(sx + i * B32 + koff[0]);
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j) wf[0][j] = *reinterpret_cast<const v4i*>(sw + j * B32 + koff[0]);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (ks + 1 < C::KS) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+          xf[(ks + 1) & 1][i] = *reinterpret_cast<const v4i*>(sx + i * B32 + koff[ks + 1]);
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+          wf[(ks + 1) & 1][j] = *reinterpret_cast<const v4i*>(sw + j * B32 + koff[ks + 1]);
+      }
+      mfma_slice<C, INT>(acc, xf[ks & 1], wf[ks & 1]);
+    }
+  }
+
+  // Epilogue through LDS, one wave-private region per wave: the raw
+  // accumulators of PW columns at a time go to LDS in [row][col] order (row
+  // stride padded by 16 bytes so the 32 rows written together fall on
+  // distinct banks); then each lane takes 8 consecutive columns of a row,
+  // for coalesced 16-byte loads and stores.  A pass issues all of its
+  // residual loads before any arithmetic, so their latency is paid once.
+  const EpiArgs& e = g.epi;
+  constexpr int PW = C::PW, RS = C::RS;
+  constexpr int LPR = PW / 8;       // lanes per row
+  constexpr int RPI = 64 / LPR;     // rows per iteration
+  constexpr int NIT = C::WM / RPI;  // iterations per pass
+  constexpr bool RES = EPI == EPI_RES || EPI == EPI_GELU_RES;
+  constexpr bool GELU = EPI == EPI_GELU || EPI == EPI_GELU_RES;
+  const bool vec = (g.N & 7) == 0 && (e.ldy & 7) == 0 && (!RES || (e.ldr & 7) == 0) && !e.acc;
+  const int cl = (lane % LPR) * 8;
+  const int rl0 = lane / LPR;
+  const int rbase = m0 + wm * C::WM;
+  uint4 resv[RES ? NIT : 1];
+  auto load_res = [&](int p) {
+    if constexpr (RES) {
+      const int col = n0 + wn * C::WN + p * PW + cl;
+      const int left = g.N - col;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int row = min(rbase + it * RPI + rl0, g.M - 1);
+        const uint16_t* rp = e.residual + (int64_t)row * e.ldr + min(col, g.N - 1);
+        if (vec && left >= 8) {
+          resv[it] = *reinterpret_cast<const uint4*>(rp);
+        } else {
+          uint16_t h[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) h[r] = r < left ? rp[r] : (uint16_t)0;
+          resv[it] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+      }
+    }
+  };
+  load_res(0);
+  __syncthreads();  // every wave is done with the operand stages; the scalars have landed
+  uint32_t* reg = reinterpret_cast<uint32_t*>(smem) + wave * (C::WM * (RS + 1));
+  const float* sc = reinterpret_cast<const float*>(smem + C::SC_OFF);
+#pragma unroll
+  for (int p = 0; p < C::WN / PW; ++p) {
+    if (p > 0) load_res(p);
+#pragma unroll
+    for (int jj = 0; jj < PW / 32; ++jj) {
+      const int j = p * (PW / 32) + jj;
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        // bit-cast the whole vector (a cast of one element lvalue reads element 0)
+        const v16i av = __builtin_bit_cast(v16i, acc[j][i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<v4i*>(reg + (i * 32 + lr) * RS + jj * 32 + q * 8 + (lane >> 5) * 4) =
+              v4i{av[q * 4], av[q * 4 + 1], av[q * 4 + 2], av[q * 4 + 3]};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int ct = wn * C::WN + p * PW + cl;  // column within the tile
+    const int col = n0 + ct;
+    const int left = g.N - col;
+    if (left > 0) {
+      float ws[8], bs[8];
+      {
+        const float4 w0 = *reinterpret_cast<const float4*>(sc + C::BM + ct);
+        const float4 w1 = *reinterpret_cast<const float4*>(sc + C::BM + ct + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(sc + C::BM + C::BN + ct);
+        const float4 b1 = *reinterpret_cast<const float4*>(sc + C::BM + C::BN + ct + 4);
+        ws[0] = w0.x; ws[1] = w0.y; ws[2] = w0.z; ws[3] = w0.w; ws[4] = w1.x; ws[5] = w1.y; ws[6] = w1.z; ws[7] = w1.w;
+        bs[0] = b0.x; bs[1] = b0.y; bs[2] = b0.z; bs[3] = b0.w; bs[4] = b1.x; bs[5] = b1.y; bs[6] = b1.z; bs[7] = b1.w;
+      }
+      const bool full = vec && left >= 8;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int rl = it * RPI + rl0;
+        const int row = rbase + rl;
+        if (row >= g.M) continue;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(reg + rl * RS + cl);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(reg + rl * RS + cl + 4);
+        const uint32_t a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        if constexpr (INT) {
+          if (e.acc) {
+            int32_t* ap = e.acc + (int64_t)row * g.N + col;
+            for (int r = 0; r < 8 && r < left; ++r) ap[r] = (int32_t)a[r];
+          }
+        }
+        if (!e.y) continue;
+        const float xs = sc[wm * C::WM + rl];
+        float res[8];
+        if constexpr (RES) unpack_h8(resv[it], res);
+        uint32_t o[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float x;
+          if constexpr (INT) x = __builtin_fmaf((float)(int32_t)a[r] * xs, ws[r], bs[r]);
+          else x = __builtin_bit_cast(float, a[r]) + bs[r];
+          if constexpr (GELU) x = gelu_as(x);
+          if constexpr (RES) x += res[r];
+          o[r] = f2h(x);
+        }
+        uint16_t* yp = e.y + (int64_t)row * e.ldy + col;
+        if (full) {
+          *reinterpret_cast<uint4*>(yp) = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+                                                     o[6] | (o[7] << 16));
+        } else {
+          for (int r = 0; r < 8 && r < left; ++r) yp[r] = (uint16_t)o[r];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <class C, bool INT, int EPI>
+void launch_cfg(const GemmArgs& g, hipStream_t st) {
+  const int tm = (g.M + C::BM - 1) / C::BM, tn = (g.N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((gemm_dma_kernel<C, INT, EPI>), dim3((unsigned)(tm * tn)), dim3(C::THREADS), C::LDS_TOTAL, st,
+                     g, tn);
+}
+
+template <class C, bool INT>
+void launch_epi(const GemmArgs& g, hipStream_t st) {
+  const bool res = g.epi.residual != nullptr, gelu = g.epi.act == 1;
+  if (gelu && res) launch_cfg<C, INT, EPI_GELU_RES>(g, st);
+  else if (gelu) launch_cfg<C, INT, EPI_GELU>(g, st);
+  else if (res) launch_cfg<C, INT, EPI_RES>(g, st);
+  else launch_cfg<C, INT, EPI_PLAIN>(g, st);
+}
+
+template <class C, bool INT>
+void prep_cfg() {
+  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_PLAIN>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_RES>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_GELU>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_GELU_RES>)};
+  for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
+}
+
+// tile configurations (BM, BN, waves M x N, stages)
+using C256x256 = Cfg<256, 256, 2, 2, 2>;
+using C128x128 = Cfg<128, 128, 2, 2, 4>;
+using C128x64 = Cfg<128, 64, 2, 2, 5>;
+using C64x64 = Cfg<64, 64, 2, 2, 8>;
+
+int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+
+template <bool INT>
+void dispatch(const GemmArgs& g, hipStream_t st) {
+  // largest tile that still fills most of the 256 CUs with one workgroup each
+  // (one round of 192 large tiles beats three rounds of smaller ones)
+  constexpr int64_t FILL = 180;
+  if (tiles(g.M, g.N, 256, 256) >= FILL) launch_epi<C256x256, INT>(g, st);
+  else if (tiles(g.M, g.N, 128, 128) >= FILL) launch_epi<C128x128, INT>(g, st);
+  else if (tiles(g.M, g.N, 128, 64) >= FILL) launch_epi<C128x64, INT>(g, st);
+  else launch_epi<C64x64, INT>(g, st);
+}
+
+}  // namespace
+
+void gemm_dma_prepare() {
+  prep_cfg<C256x256, true>();
+  prep_cfg<C128x128, true>();
+  prep_cfg<C128x64, true>();
+  prep_cfg<C64x64, true>();
+  prep_cfg<C256x256, false>();
+  prep_cfg<C128x128, false>();
+  prep_cfg<C128x64, false>();
+  prep_cfg<C64x64, false>();
+}
+
+bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
+  const bool i8 = akind == A_I8 && bkind == B_I8;
+  const bool f16 = akind == A_F16 && bkind == B_F16;
+  if (!(i8 || f16)) return false;
+  if (g.epi.temb_t) return false;
+  const int64_t kb = (int64_t)g.K * (i8 ? 1 : 2);
+  if (kb % 128 != 0) return false;  // whole 128-byte stages
+  const int64_t ldb = (int64_t)g.lda * (i8 ? 1 : 2);
+  if (ldb % 16 != 0) return false;
+  if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
+  return g.M > 0 && g.N > 0;
+}
+
+void launch_gemm_dma(int akind, const GemmArgs& g, hipStream_t st) {
+  if (akind == A_I8) dispatch<true>(g, st);
+  else dispatch<false>(g, st);
+}
+
+}  // namespace ald
