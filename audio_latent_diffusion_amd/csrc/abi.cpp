@@ -231,24 +231,7 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   if (a->renoise) launch_renoise(a->x, a->x0, a->eps, n_tok, C, map, a->t_cur, a->renoise, st);
 
   // input projection of the fp32 latent (both CFG rows read the same latent) + time embedding
-  {
-    GemmArgs g;
-    g.A = a->x;
-    g.lda = C;
-    g.a_mod = n_tok;
-    g.B = w->w_in;
-    g.M = M;
-    g.N = H;
-    g.K = C;
-    g.epi.bias = w->b_in;
-    g.epi.y = b.h;
-    g.epi.ldy = H;
-    g.epi.temb_t = a->t_cur;
-    g.epi.n_tok = n_tok;
-    g.epi.rows_per_req = map.rows_per_req;
-    g.epi.row_req = map.row_req;
-    launch_gemm(A_F32, B_F16, g, st);
-  }
+  launch_inproj(a->x, n_tok, M, C, w->w_in, H, w->b_in, a->t_cur, map, b.h, st);
 
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   for (int l = 0; l < c->n_blocks; ++l) {

@@ -168,6 +168,118 @@ __global__ void cu_pairs_kernel(const int32_t* __restrict__ cu, int R, int64_t n
   cu2[b] = b <= R ? cu[b] : (int32_t)(n_tok + cu[b - R]);
 }
 
+// Input projection of the fp32 latent with the sinusoidal time embedding:
+//   h[m, n] = fp16( sum_k fp16(x[m % n_tok, k]) w_in[n, k] + b_in[n] + temb(t_r, n) )
+// for both CFG rows of every token (row m reads latent token m % n_tok, request
+// r of that token).  K (the latent width) is tiny, so this is a VALU kernel:
+// 64 x 64 output tiles, operands staged through LDS as fp32 (the fp16 products
+// are exact in fp32), 4 x 4 outputs per thread.
+//   temb(t, n) = sin(1000 t w_j) for n < H/2, cos(1000 t w_j) after,
+//   w_j = exp(-ln(1e4) j / (H/2)), j = n mod H/2.
+// The argument reaches 1000 rad: it is reduced to a fraction of a turn here and
+// fed to the hardware sine (input in turns); the fp32 argument itself already
+// carries ~1e-4 rad of rounding error.
+__device__ __forceinline__ float temb_value(float t, int col, int H) {
+  const int half = H >> 1;
+  const int j = col < half ? col : col - half;
+  const float om = __expf(-9.210340371976184f * (float)j / (float)half);
+  float turns = 1000.0f * t * om * 0.15915494309189535f;
+  if (col >= half) turns += 0.25f;  // cos x = sin(x + pi/2)
+  turns -= floorf(turns);
+  return __builtin_amdgcn_sinf(turns);
+}
+
+constexpr int IP_T = 64;
+
+__global__ __launch_bounds__(256) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M, int C,
+                                                     const uint16_t* __restrict__ w, int H,
+                                                     const float* __restrict__ bias, const float* __restrict__ t_cur,
+                                                     RowMap map, uint16_t* __restrict__ h) {
+  __shared__ float xs[IP_T][IP_T + 1];
+  __shared__ float wsm[IP_T][IP_T + 1];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.y * IP_T, n0 = blockIdx.x * IP_T;
+  const int tr = (tid >> 4) * 4, tc = (tid & 15) * 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < C; k0 += IP_T) {
+    // every load of the stage is issued before any is used: 4 x 16 bytes of
+    // latent and 2 x 16 bytes of weights per thread (C % 8 == 0)
+    float4 xv[4];
+    v4i wv[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4, m = m0 + r;
+      xv[q] = (m < M && k0 + k < C) ? *reinterpret_cast<const float4*>(x + (m % n_tok) * C + k0 + k)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + 256 * q, r = i >> 3, k = (i & 7) * 8, n = n0 + r;
+      wv[q] = (n < H && k0 + k < C) ? ld16(w + (int64_t)n * C + k0 + k) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4;
+      xs[r][k] = h2f(f2h(xv[q].x));
+      xs[r][k + 1] = h2f(f2h(xv[q].y));
+      xs[r][k + 2] = h2f(f2h(xv[q].z));
+      xs[r][k + 3] = h2f(f2h(xv[q].w));
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + 256 * q, r = i >> 3, k = (i & 7) * 8;
+      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&wv[q]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wsm[r][k + e] = h2f(hv[e]);
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < IP_T; ++k) {
+      float xa[4], wb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = xs[tr + i][k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wb[j] = wsm[tc + j][k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wb[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tr + i;
+    if (m >= M) continue;
+    const float t = t_cur[req_of(map, m)];
+    uint16_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = min(n0 + tc + j, H - 1);
+      o[j] = f2h(acc[i][j] + bias[n] + temb_value(t, n, H));
+    }
+    uint16_t* hp = h + (int64_t)m * H + n0 + tc;
+    if (n0 + tc + 3 < H && (H & 3) == 0) {
+      *reinterpret_cast<uint2*>(hp) = *reinterpret_cast<const uint2*>(o);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (n0 + tc + j < H) hp[j] = o[j];
+    }
+  }
+}
+
+void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* w, int H, const float* bias,
+                   const float* t_cur, RowMap map, uint16_t* h, hipStream_t st) {
+  if (M <= 0 || H <= 0) return;
+  dim3 grid((unsigned)((H + IP_T - 1) / IP_T), (unsigned)((M + IP_T - 1) / IP_T));
+  hipLaunchKernelGGL(inproj_kernel, grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+}
+
 static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,

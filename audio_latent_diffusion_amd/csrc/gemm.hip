@@ -6,9 +6,6 @@
 //  * fp16   : fp16 x fp16 -> fp32 with v_mfma_f32_16x16x32_f16.
 //  * q4     : 4-bit weights + fp16 group scales dequantized to fp16(q * s)
 //             while staging B into LDS, then the fp16 MFMA.
-//  * fp32 A : the input projection reads the fp32 latent, rounds it to fp16
-//             while staging, and adds the sinusoidal time embedding in the
-//             epilogue.
 //
 // Both operands are K-contiguous, so every lane of an MFMA fragment reads
 // one 16-byte run of a row: the A (B) fragment of lane l is row (l % 16) of
@@ -83,37 +80,6 @@ struct AStage<A_F16, BM> {
       int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
       int m = m0 + row, k = k0 + col;
       r[i] = (m < g.M && k < g.K) ? ld16(A + (int64_t)m * g.lda + k) : v4i{0, 0, 0, 0};
-    }
-  }
-  __device__ void store(uint8_t* lds, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 16;
-      *reinterpret_cast<v4i*>(lds + row * LDS_STRIDE + col) = r[i];
-    }
-  }
-};
-
-// fp32 source rows (row index m % a_mod), rounded to fp16 when staged
-template <int BM>
-struct AStage<A_F32, BM> {
-  static constexpr int N = BM * 8 / 256;
-  v4i r[N];
-  __device__ void load(const GemmArgs& g, int m0, int k0, int tid) {
-    const float* A = static_cast<const float*>(g.A);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      int m = m0 + row, k = k0 + col;
-      if (m < g.M && k < g.K) {
-        const float* p = A + (int64_t)(m % g.a_mod) * g.lda + k;
-        float4 f0 = *reinterpret_cast<const float4*>(p);
-        float4 f1 = *reinterpret_cast<const float4*>(p + 4);
-        uint16_t h[8] = {f2h(f0.x), f2h(f0.y), f2h(f0.z), f2h(f0.w), f2h(f1.x), f2h(f1.y), f2h(f1.z), f2h(f1.w)};
-        r[i] = *reinterpret_cast<v4i*>(h);
-      } else {
-        r[i] = v4i{0, 0, 0, 0};
-      }
     }
   }
   __device__ void store(uint8_t* lds, int tid) {
@@ -221,19 +187,6 @@ struct BStage<B_Q4, BN> {
   }
 };
 
-// ----------------------------------------------------------------- epilogue
-
-__device__ __forceinline__ float temb_value(const EpiArgs& e, int row, int col, int N) {
-  int64_t i = row % e.n_tok;
-  int r = e.row_req ? e.row_req[i] : (int)(i / e.rows_per_req);
-  float t = e.temb_t[r];
-  int half = N >> 1;
-  int j = col < half ? col : col - half;
-  float om = expf(-9.210340371976184f * (float)j / (float)half);  // exp(-ln(1e4) j / half)
-  float a = 1000.0f * t * om;
-  return col < half ? sinf(a) : cosf(a);
-}
-
 // ----------------------------------------------------------------- kernel
 
 template <int AK, int BK, int BM, int BN>
@@ -326,7 +279,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
         if (!e.y) continue;
         v += bias;
-        if (e.temb_t) v += temb_value(e, row, col, g.N);
         if (e.act == 1) v = gelu_erf(v);
         if (e.residual) v += h2f(e.residual[(int64_t)row * e.ldr + col]);
         e.y[(int64_t)row * e.ldy + col] = f2h(v);
@@ -357,7 +309,6 @@ void gemm_prepare() {
   set_lds<A_F16, B_F16, 128, 64>();
   set_lds<A_F16, B_Q4, 128, 128>();
   set_lds<A_F16, B_Q4, 128, 64>();
-  set_lds<A_F32, B_F16, 128, 128>();
 }
 
 void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
@@ -376,8 +327,6 @@ void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
   } else if (akind == A_F16 && bkind == B_Q4) {
     if (narrow) launch_tile<A_F16, B_Q4, 128, 64>(g, st);
     else launch_tile<A_F16, B_Q4, 128, 128>(g, st);
-  } else if (akind == A_F32 && bkind == B_F16) {
-    launch_tile<A_F32, B_F16, 128, 128>(g, st);
   }
 }
 

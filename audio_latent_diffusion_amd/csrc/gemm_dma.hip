@@ -27,9 +27,14 @@
 // (s_waitcnt vmcnt with the count of loads issued after them), barrier (every
 // wave's loads of stage kt visible, every wave done with stage kt - 1), issue
 // the loads of stage kt + STAGES - 1 into the buffer of stage kt - 1, then
-// run the four 32-byte K slices of the stage.  Fragment reads are double
-// buffered in registers: the reads of slice s + 1 are issued before the MFMAs
-// of slice s, so LDS latency hides behind matrix work.
+// run the four 32-byte K slices of the stage.  The next stage's copies are
+// issued in four parts, one before each slice's MFMAs, and fragment reads
+// are double buffered in registers (slice s + 1 is read during slice s).
+//
+// Measured limits on MI355X that shape this: LDS serves ~128 B/clk per CU,
+// shared by the DMA writes and the fragment reads; a 256 x 256 tile at full
+// matrix rate needs ~94 B/clk of it (reads 64, copies 32), so LDS, not HBM,
+// bounds the main loop; a single CU's DMA copies stream ~66 B/clk from L2.
 //
 // Operand roles are swapped in the MFMA (W fragment first): accumulator
 // register r of lane l then holds output row l % 32 and column
@@ -40,7 +45,10 @@
 //
 // Workgroups are mapped XCD-aware: consecutive workgroup ids land on
 // different XCDs (round-robin), so tile ids are remapped to give each XCD one
-// contiguous run of row-major tiles (tiles sharing X rows share its L2).
+// contiguous run of tiles, and that run is a compact block of the output
+// (grouped order), so the X and W panels it touches stay few and in its L2.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -137,9 +145,14 @@ struct Loader {
       dst[i] = b * BLK;
     }
   }
-  __device__ __forceinline__ void issue(uint8_t* stage, int kbyte) {
+  __device__ __forceinline__ void issue(uint8_t* stage, int kbyte) { issue_part<0, 1>(stage, kbyte); }
+  // part P of PARTS of the stage's copies (spread over the K slices so the
+  // wave keeps feeding MFMAs while the memory pipeline accepts its loads)
+  template <int P, int PARTS>
+  __device__ __forceinline__ void issue_part(uint8_t* stage, int kbyte) {
+    constexpr int lo = C::LOADS * P / PARTS, hi = C::LOADS * (P + 1) / PARTS;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
+    for (int i = lo; i < hi; ++i)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kbyte), (lds_void*)(stage + dst[i]), 16, 0,
                                        0);
   }
@@ -149,6 +162,19 @@ __device__ __forceinline__ int xcd_tile(int bid, int nt) {
   const int q = nt >> 3, rem = nt & 7;
   const int x = bid & 7, loc = bid >> 3;
   return x * q + (x < rem ? x : rem) + loc;
+}
+
+// tile t -> (tm, tn): groups of gm tile rows, column-major inside a group, so
+// that the run of tiles one XCD receives covers a compact block of about
+// gm x (run / gm) tiles (few distinct X and W panels through its L2)
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  const int per_group = gm * tiles_n;
+  const int grp = t / per_group;
+  const int first = grp * gm;
+  const int rows = min(gm, tiles_m - first);
+  const int r = t - grp * per_group;
+  tm = first + r % rows;
+  tn = r / rows;
 }
 
 // GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
@@ -189,13 +215,14 @@ __device__ __forceinline__ void mfma_slice(typename std::conditional<INT, v16i, 
 }
 
 template <class C, bool INT, int EPI>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n) {
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int nt = gridDim.x;
-  const int t = xcd_tile(blockIdx.x, nt);
-  const int m0 = (t / tiles_n) * C::BM, n0 = (t % tiles_n) * C::BN;
+  int tm, tn;
+  tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
 
   constexpr int EB = INT ? 1 : 2;  // bytes per element
   const int nk = g.K * EB / C::KB;
@@ -247,12 +274,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   const int xbase = wm * C::MI * B32;
   const int wbase = C::BX * BLK + wn * C::NJ * B32;
 
+  // Per stage: wait for its copies, barrier, then four 32-byte K slices.  A
+  // quarter of the next stage's copies is issued before each slice's MFMAs
+  // (a long burst of copy issues stalls the wave while the matrix pipe
+  // idles), and the fragments of slice s + 1 are read during slice s.
   for (int kt = 0; kt < nk; ++kt) {
-    const int ahead = min(C::STAGES - 2, nk - 1 - kt);
-    wait_stages<C::LOADS, C::STAGES - 2>(ahead);
+    wait_stages<C::LOADS, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
     __builtin_amdgcn_s_barrier();
     const int kn = kt + C::STAGES - 1;
-    if (kn < nk) ld.issue(smem + (kn % C::STAGES) * C::STAGE_BYTES, kn * C::KB);
+    const bool more = kn < nk;
+    uint8_t* const snext = smem + (kn % C::STAGES) * C::STAGE_BYTES;
     const uint8_t* sx = smem + (kt % C::STAGES) * C::STAGE_BYTES + xbase;
     const uint8_t* sw = smem + (kt % C::STAGES) * C::STAGE_BYTES + wbase;
     v4i xf[2][C::MI], wf[2][C::NJ];
@@ -262,6 +293,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
     for (int j = 0; j < C::NJ; ++j) wf[0][j] = *reinterpret_cast<const v4i*>(sw + j * B32 + koff[0]);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
+      if (more) {
+        if (ks == 0) ld.template issue_part<0, C::KS>(snext, kn * C::KB);
+        if (ks == 1) ld.template issue_part<1, C::KS>(snext, kn * C::KB);
+        if (ks == 2) ld.template issue_part<2, C::KS>(snext, kn * C::KB);
+        if (ks == 3) ld.template issue_part<3, C::KS>(snext, kn * C::KB);
+      }
       if (ks + 1 < C::KS) {
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
@@ -390,8 +427,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
 template <class C, bool INT, int EPI>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + C::BM - 1) / C::BM, tn = (g.N + C::BN - 1) / C::BN;
+  // each XCD gets about tiles / 8 consecutive tiles; make that run a block of
+  // about sqrt(run) x sqrt(run) tiles, as tall as needed to fit tn columns
+  const int run = (tm * tn + 7) / 8;
+  int gm = (int)(sqrtf((float)run) + 0.5f);
+  gm = std::max(gm, (run + tn - 1) / tn);
+  gm = std::max(1, std::min(gm, tm));
   hipLaunchKernelGGL((gemm_dma_kernel<C, INT, EPI>), dim3((unsigned)(tm * tn)), dim3(C::THREADS), C::LDS_TOTAL, st,
-                     g, tn);
+                     g, tn, gm);
 }
 
 template <class C, bool INT>
@@ -448,7 +491,6 @@ bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
   const bool i8 = akind == A_I8 && bkind == B_I8;
   const bool f16 = akind == A_F16 && bkind == B_F16;
   if (!(i8 || f16)) return false;
-  if (g.epi.temb_t) return false;
   const int64_t kb = (int64_t)g.K * (i8 ? 1 : 2);
   if (kb % 128 != 0) return false;  // whole 128-byte stages
   const int64_t ldb = (int64_t)g.lda * (i8 ? 1 : 2);

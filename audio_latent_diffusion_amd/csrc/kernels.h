@@ -5,7 +5,7 @@
 
 namespace ald {
 
-enum AKind { A_I8 = 0, A_F16 = 1, A_F32 = 2 };
+enum AKind { A_I8 = 0, A_F16 = 1 };
 enum BKind { B_I8 = 0, B_F16 = 1, B_Q4 = 2 };
 
 struct EpiArgs {
@@ -18,17 +18,11 @@ struct EpiArgs {
   int64_t ldy = 0;
   int32_t* acc = nullptr;           // [M, N] raw accumulators (int8 path)
   int act = 0;
-  // time embedding added per (row, col) (input projection)
-  const float* temb_t = nullptr;    // t per request
-  int64_t n_tok = 1;                // row -> token: row % n_tok
-  int rows_per_req = 1;             // token -> request: token / rows_per_req
-  const int32_t* row_req = nullptr; //   ... or row_req[token]
 };
 
 struct GemmArgs {
   const void* A = nullptr;
   int64_t lda = 0;
-  int64_t a_mod = 1;                // fp32 A: source row = m % a_mod
   const void* B = nullptr;          // [N, K] int8/fp16, or packed q4 [N, K/2]
   const uint16_t* b_scale = nullptr;// q4 group scales [N, K/32]
   int M = 0, N = 0, K = 0;
@@ -86,5 +80,7 @@ void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap 
                       const float* t_cur, const float* t_next, const uint8_t* active, hipStream_t st);
 void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st);
 void launch_cu_pairs(const int32_t* cu, int R, int64_t n_tok, int32_t* cu2, hipStream_t st);
+void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* w, int H, const float* bias,
+                   const float* t_cur, RowMap map, uint16_t* h, hipStream_t st);
 
 }  // namespace ald

@@ -163,6 +163,7 @@ class StepRunner:
                       if keep_velocity else None)
         self.block_norms = None
         self.graph = None
+        self._graphs = []
         self._args = [self._make_args(i) for i in range(N)]
 
     def _make_args(self, i: int) -> L.dit_step_args:
@@ -202,12 +203,12 @@ class StepRunner:
                                              ctypes.byref(self._args[i]), self.ws.data_ptr(), self.ws_bytes,
                                              B._stream()))
 
-    def capture(self, steps: Optional[Sequence[int]] = None) -> None:
-        """Capture the given steps (default all) as one hipGraph on a side stream."""
-        steps = list(range(self.n_steps)) if steps is None else list(steps)
+    def capture_graph(self, steps: Sequence[int]) -> ctypes.c_void_p:
+        """Capture the given steps as one hipGraph on a side stream and return
+        its handle (owned by this runner, destroyed with it)."""
+        steps = list(steps)
         arr = (L.dit_step_args * len(steps))(*[self._args[i] for i in steps])
         m = self.model
-        self.destroy_graph()
         handle = ctypes.c_void_p()
         s = torch.cuda.Stream(device=self.x.device)
         s.wait_stream(torch.cuda.current_stream())
@@ -216,15 +217,24 @@ class StepRunner:
                 ctypes.byref(m.c_cfg), ctypes.byref(m.c_weights), arr, len(steps), self.ws.data_ptr(),
                 self.ws_bytes, s.cuda_stream, ctypes.byref(handle)))
         torch.cuda.current_stream().wait_stream(s)
-        self.graph = handle
-        self._graph_steps = steps
+        self._graphs.append(handle)
+        return handle
+
+    def launch_graph(self, handle: ctypes.c_void_p) -> None:
+        L.check("dit_graph_launch", L.lib().dit_graph_launch(handle, B._stream()))
+
+    def capture(self, steps: Optional[Sequence[int]] = None) -> None:
+        """Capture the given steps (default all) as the runner's graph."""
+        self.graph = self.capture_graph(range(self.n_steps) if steps is None else steps)
 
     def replay(self) -> None:
-        L.check("dit_graph_launch", L.lib().dit_graph_launch(self.graph, B._stream()))
+        self.launch_graph(self.graph)
 
     def destroy_graph(self) -> None:
-        if self.graph is not None and self.graph.value:
-            L.lib().dit_graph_destroy(self.graph)
+        for h in self._graphs:
+            if h.value:
+                L.lib().dit_graph_destroy(h)
+        self._graphs = []
         self.graph = None
 
     def __del__(self):

@@ -47,18 +47,19 @@ def _events_time(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
-def gemm_mix_timing(cfg, iters=50):
-    """Average launch time of the W8A8 GEMM over the step's per-block launch
-    mix (qkv, o, q, ox, up, down at M = 2 R S tokens), on torch's current
-    stream, which is the stream the launches go to."""
+MIX_SHAPES = lambda H, F: [(H, 3 * H), (H, H), (H, H), (H, H), (H, F), (F, H)]  # (K, N) per block
+
+
+def gemm_mix(cfg):
+    """The W8A8 GEMM launches of one DiT block at M = 2 R S tokens (qkv, o, q,
+    ox, up, down), pre-quantized inputs, each launched through the C ABI on
+    torch's current stream; returns a callable that enqueues the six."""
     import torch
     from audio_latent_diffusion_amd import binding as B
-    H, F = cfg.hidden, cfg.mlp
     M = cfg.tokens
-    shapes = [(H, 3 * H), (H, H), (H, H), (H, H), (H, F), (F, H)]  # (K, N)
     g = torch.Generator(device="cuda").manual_seed(0)
     bufs = []
-    for K, N in shapes:
+    for K, N in MIX_SHAPES(cfg.hidden, cfg.mlp):
         xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
         wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
         xs = torch.rand(M, device="cuda", generator=g) * 1e-2
@@ -69,11 +70,21 @@ def gemm_mix_timing(cfg, iters=50):
     def run_mix():
         for xq, wq, xs, ws, y in bufs:
             B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, y=y, prequant=True)
+    return run_mix
 
+
+def gemm_mix_timing(cfg, iters=50):
+    """Average launch time of the W8A8 GEMM over the step's per-block launch
+    mix, timed with HIP events on torch's current stream (the stream the
+    launches go to), with the algorithmic ops and bytes per launch."""
+    import torch
+    run_mix = gemm_mix(cfg)
     stream = torch.cuda.current_stream()
     for _ in range(3):
         run_mix()
     ms_mix = _events_time(run_mix, iters, stream)
+    M = cfg.tokens
+    shapes = MIX_SHAPES(cfg.hidden, cfg.mlp)
     ops = sum(2.0 * M * N * K for K, N in shapes)
     byts = sum(M * K + N * K + 2 * M * N + 4 * (M + N) for K, N in shapes)
     return ms_mix / len(shapes), ops / len(shapes), byts / len(shapes)
@@ -134,18 +145,79 @@ def cpu_baseline(cfg, params, inp, resid, budget_s=20.0):
                       f"fp64 numpy oracle with BLAS matmuls, text K/V and weight packing excluded"}
 
 
+GEMM_SOURCE = os.path.join(ROOT, "audio_latent_diffusion_amd", "csrc", "gemm_dma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_mid_launch_mix_traffic.txt")
+
+
+def _source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE of the launch-mix leg, each scaled by what the
+    same counter reads for a plain copy of known size); None when the file is
+    missing or the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            parts = ln.split()
+            if len(parts) == 2 and not ln.startswith("#"):
+                vals[parts[0]] = parts[1]
+    try:
+        if vals["source_sha256"] != _source_hash(GEMM_SOURCE):
+            return None
+        copy_bytes = float(vals["copy_bytes"])
+        fetch_factor = float(vals["copy_fetch_kib_per_dispatch"]) * 1024.0 / copy_bytes
+        write_factor = float(vals["copy_write_kib_per_dispatch"]) * 1024.0 / copy_bytes
+        return (float(vals["gemm_fetch_kib_per_dispatch"]) * 1024.0 / fetch_factor +
+                float(vals["gemm_write_kib_per_dispatch"]) * 1024.0 / write_factor)
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def counter_legs(legs, reps):
+    """Workloads for the rocprofv3 --pmc runs: the GEMM launch mix of the
+    step (same shapes and stream as the roofline timing) and a plain device
+    copy of known size that calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    import ald_inputs as I
+    if "gemm" in legs:
+        run_mix = gemm_mix(I.MID)
+        for _ in range(reps):
+            run_mix()
+    if "copy" in legs:
+        # an elementwise kernel that reads one buffer and writes another, both
+        # larger than the 256 MB last-level cache
+        n = 256 << 20  # 256 Mi fp32 = 1 GiB each way
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(reps):
+            torch.mul(a, 1.0, out=b)
+        print(f"copy leg: {n * 4} bytes read and written per dispatch")
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20, help="timed replays of the 8-step graph")
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=160, help="timed denoise steps")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed denoise steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--leg", default="", help="counter legs only (gemm,copy) for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requests shard across GPUs with no per-step exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
+    if args.leg:
+        counter_legs(args.leg.split(","), 20)
+        return
 
     import torch
     import ald_inputs as I
@@ -170,30 +242,44 @@ def main():
     resid = float(np.mean(norms))
     del cal
 
+    # the whole 8-step sampler loop is one graph; a partial graph of the first
+    # K mod 8 steps makes the timed count exactly K denoise steps
     run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
                              inp.direction, resid)
     x_init = run.x.clone()
-    run.capture()
+    full_graph = run.capture_graph(range(cfg.n_steps))
 
-    def one_pass():
-        run.x.copy_(x_init)
-        run.replay()
+    def replay(graph):
+        run.x.copy_(x_init)  # a fresh request: the latent restarts from its noise
+        run.launch_graph(graph)
 
-    for _ in range(args.warmup):
-        one_pass()
+    def schedule(k):
+        sched = [full_graph] * (k // cfg.n_steps)
+        if k % cfg.n_steps:
+            sched.append(run.capture_graph(range(k % cfg.n_steps)))
+        return sched
+
+    warm, timed = schedule(args.warmup), schedule(args.steps)
+    for gr in warm:
+        replay(gr)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ms_pass = _events_time(one_pass, args.steps, stream)
+    start.record(stream)
+    for gr in timed:
+        replay(gr)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    n_steps = cfg.n_steps * args.steps
-    steps_per_s = n_steps / wall
-    ev_steps_per_s = cfg.n_steps / (ms_pass / 1e3)
+    ev_ms = start.elapsed_time(end)
+    steps_per_s = args.steps / wall
     ok = bool(torch.isfinite(run.x).all().item())
 
     ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
     achieved = ops_launch / (ms_launch / 1e3) / 1e12
+    traffic = measured_traffic()
     serve = serve_gemm()
 
     line = {
@@ -203,7 +289,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / n_steps, 4),
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -214,11 +300,12 @@ def main():
                                "steering alpha 0.5 at block 12 in steps 2-5",
                    "global_batch": cfg.cfg_rows, "seq_len": cfg.seq, "parallelism": "none",
                    "denoise_steps_per_replay": cfg.n_steps, "attention_dtype": "fp16"},
-        "event_steps_per_s": round(ev_steps_per_s, 2),
+        "event_steps_per_s": round(args.steps / (ev_ms / 1e3), 2),
         "finite": ok,
-        "roofline": {"bound": "mfma", "kernel": "w8a8 GEMM (int8 MFMA), step launch mix at M=512",
+        "roofline": {"bound": "mfma", "kernel": "W8A8 GEMM (int8 MFMA), the step's launch mix at M = 512",
                      "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": None,
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
                      "avg_launch_us": round(ms_launch * 1e3, 2),
                      "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
         "w8a8_gemm_serve": serve,

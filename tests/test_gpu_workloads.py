@@ -1,0 +1,89 @@
+"""Parity of the denoise step at the serving, 4-bit and mixed warm-start
+workload shapes, and invariants at full serving size.
+
+The oracle finishes a reduced-depth model of the serving widths (hidden 1536,
+24 heads, MLP 6144, 8 requests x 512 latent tokens = 8192 CFG rows) and of
+the 4-bit widths (hidden 2048, MLP 8192, 4 requests x 1024 tokens) in
+seconds, so those are checked element by element on the step's output latent
+(bar 2e-2, max |g - o| / max |o|).  The mixed warm-start batch runs the full
+16-block mid-size model on a 4-request packed sub-batch (lengths 128, 129,
+577, 1024; two cold, two warm, one re-noised inside the checked steps).  At
+the full 24-block serving size the oracle is out of reach; there the graph
+replay must equal eager execution bit for bit and the latent stays finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ald_inputs as I
+from audio_latent_diffusion_amd import runtime
+from oracle import ald_oracle as O
+from tests._gpu import host, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+TOL = 2e-2
+RESID = 20.0
+
+
+def _runner(model, inp, resid=RESID, **kw):
+    return runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
+                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps, **kw)
+
+
+def _parity(cfg, steps, inp=None):
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg) if inp is None else inp
+    run = _runner(runtime.DiTModel(cfg, p), inp)
+    for i in steps:
+        run.step(i)
+    got = host(run.x)
+    ref, _ = O.run_sampler(O.prepare_model(cfg, p), inp, resid_norm=RESID, steps=steps)
+    err = O.normwise_rel_err(got, ref)
+    print(f"{cfg.name} {cfg.wmode} blocks={cfg.n_blocks} steps={list(steps)}: latent err {err:.2e}")
+    return err
+
+
+@pytest.mark.parametrize("wmode", ["w8a8", "f16"])
+def test_serve_widths_two_blocks(wmode):
+    """Serving widths, both weight arms on the same inputs; steering active."""
+    cfg = I.SERVE.replace(n_blocks=2, wmode=wmode, steer_block=1, steer_alpha=0.5, steer_steps=(0,))
+    assert _parity(cfg, [0]) < TOL
+
+
+def test_q4_widths_one_block():
+    """4-bit weights (group 32, fp16 scales) at hidden 2048, 1024 latent tokens."""
+    cfg = I.Q4.replace(n_blocks=1, steer_block=0, steer_alpha=0.5, steer_steps=(0,))
+    assert _parity(cfg, [0]) < TOL
+
+
+def test_mixed_warm_start_subbatch():
+    """Packed varlen requests of the mid-size model, two of them warm-started:
+    request 2 is re-noised to t_5 inside the checked steps, request 3 stays
+    inactive until step 7."""
+    cfg = I.MIXED
+    inp = I.make_mixed_inputs(cfg, seqlens=np.array([128, 129, 577, 1024]),
+                              warm=np.array([False, False, True, True]))
+    inp.start_step = np.array([0, 0, 5, 7])
+    err = _parity(cfg, [5, 6], inp)
+    assert err < TOL
+
+
+def test_serve_full_size_graph_equals_eager():
+    """The full 24-block serving model (8192 CFG rows, W8A8): two steps
+    replayed as one graph equal the same two steps run eagerly, bit for bit."""
+    cfg = I.SERVE
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, p)
+    eager = _runner(model, inp)
+    eager.step(0)
+    eager.step(1)
+    graph = _runner(model, inp)
+    graph.capture([0, 1])
+    graph.replay()
+    a, b = host(eager.x), host(graph.x)
+    assert np.all(np.isfinite(a))
+    assert a.tobytes() == b.tobytes()
+    # the step moved the latent by the guided velocity times the step size
+    assert not np.array_equal(a, inp.x)
