@@ -314,7 +314,7 @@ void gemm_prepare() {
 void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return;
   if (gemm_dma_applicable(akind, bkind, g)) {
-    launch_gemm_dma(akind, g, st);
+    launch_gemm_dma(akind, bkind, g, st);
     return;
   }
   const bool narrow = g.N <= 64;

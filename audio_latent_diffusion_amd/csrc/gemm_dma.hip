@@ -1,10 +1,13 @@
 // Pipelined MFMA GEMM for the DiT linears: y[M, N] = epilogue(X[M, K] . W[N, K]^T)
 // with both operands K-contiguous, fed by direct global -> LDS loads.
 //
-//  * int8 x int8 -> int32 on v_mfma_i32_32x32x32_i8 (W8A8; epilogue
+//  * W8A8: int8 x int8 -> int32 on v_mfma_i32_32x32x32_i8; epilogue
 //    acc * x_scale[m] * w_scale[n] + bias (+GELU) (+residual) -> fp16, and an
-//    optional raw int32 accumulator dump), or
-//  * fp16 x fp16 -> fp32 on v_mfma_f32_32x32x16_f16 (fp16 weights).
+//    optional raw int32 accumulator dump;
+//  * F16: fp16 x fp16 -> fp32 on v_mfma_f32_32x32x16_f16;
+//  * Q4: fp16 activations x 4-bit weights (groups of 32 along K with fp16
+//    scales): packed nibbles and scales travel to LDS, and each lane turns its
+//    weight fragment into fp16(q * s) in registers right before the fp16 MFMA.
 //
 // Both MFMAs take, per operand, a 32-row x 32-byte fragment: lane l holds row
 // l % 32 and the 16 bytes at 16 (l / 32) of the 32-byte K slice.  Only the
@@ -20,8 +23,11 @@
 // chunk of the row it fetches: slot p of row r holds chunk p ^ g(r) with
 // g(r) = (r & 7) ^ ((r >> 3) & 1), so that the 16 rows read together by an
 // MFMA operand load (same chunk, consecutive rows) fall on distinct banks.
-// Each operand fragment is then one ds_read_b128 per lane.  No VGPR staging:
-// a ring of STAGES buffers keeps STAGES - 1 stages in flight.
+// Each operand fragment is then one ds_read_b128 per lane.  A Q4 stage (64 K
+// values) holds the 32 packed bytes of each weight row as blocks of 32 rows
+// (the 16 bytes of group 0 of every row, then those of group 1) and the two
+// fp16 scales of each row (4-byte copies, 64 rows per instruction).  No VGPR
+// staging: a ring of STAGES buffers keeps STAGES - 1 stages in flight.
 //
 // Per K stage: wait until this wave's loads of stage kt have landed
 // (s_waitcnt vmcnt with the count of loads issued after them), barrier (every
@@ -57,39 +63,44 @@
 namespace ald {
 namespace {
 
-constexpr int BLK = 1024;  // LDS block: one DMA instruction (64 lanes x 16 bytes)
+constexpr int BLK = 1024;  // LDS block: one 16-byte copy instruction (64 lanes)
+constexpr int KB = 128;    // X bytes per stage and row (one cache line)
 
-// epilogue kinds
-enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };
+enum { M_I8 = 0, M_F16 = 1, M_Q4 = 2 };                              // operand modes
+enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };  // epilogue kinds
 
-template <int BM_, int BN_, int WGM_, int WGN_, int STAGES_>
+template <int BM_, int BN_, int STAGES_, int MODE_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, STAGES = STAGES_;
-  static constexpr int KB = 128;           // K bytes per stage and row (one cache line)
-  static constexpr int RPB = BLK / KB;     // rows per LDS block (8)
-  static constexpr int CPR = KB / 16;      // 16-byte chunks per row (8)
-  static constexpr int KS = KB / 32;       // 32-byte MFMA K slices per stage (4)
-  static constexpr int WAVES = WGM * WGN;
-  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, MODE = MODE_;
+  static constexpr bool INT = MODE == M_I8, Q4 = MODE == M_Q4;
+  static constexpr int WGM = 2, WGN = 2, WAVES = 4, THREADS = 256;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;  // 32x32 MFMA blocks per wave
-  static constexpr int BX = BM / RPB, BW = BN / RPB;  // LDS blocks per stage
-  static constexpr int STAGE_BYTES = (BX + BW) * BLK;
+  static constexpr int KS = 4;                      // 32-byte X slices per stage
+  static constexpr int BX = BM / 8;                 // X blocks per stage (8 rows x 128 B)
+  static constexpr int BW = Q4 ? BN / 32 : BN / 8;  // W blocks per stage
+  // Q4 scale copies (64 rows each), padded so that the copies split evenly
+  static constexpr int SC0 = Q4 ? BN / 64 : 0;
+  static constexpr int SCL = Q4 ? SC0 + (WAVES - (BX + BW + SC0) % WAVES) % WAVES : 0;
+  static constexpr int LOADS = (BX + BW + SCL) / WAVES;  // copy instructions per wave and stage
+  static constexpr int W_OFF = BX * BLK;                 // offsets within a stage
+  static constexpr int S_OFF = (BX + BW) * BLK;
+  static constexpr int STAGE_BYTES = S_OFF + SCL * 256;
   static constexpr int LDS = STAGES * STAGE_BYTES;
-  static constexpr int LOADS = (BX + BW) / WAVES;   // DMA instructions per wave per stage
-  // epilogue staging: PW columns per pass, rows padded by 4 words, plus the row scales
+  // epilogue staging: PW columns per pass, rows padded by 4 words
   static constexpr int PW = WN < 64 ? WN : 64;
   static constexpr int RS = PW + 4;
   static constexpr int EPI_LDS = WAVES * WM * (RS + 1) * 4;
   // per-row and per-column epilogue scalars (x_scale[BM], w_scale[BN], bias[BN])
   static constexpr int SC_OFF = LDS > EPI_LDS ? LDS : EPI_LDS;
   static constexpr int LDS_TOTAL = SC_OFF + (BM + 2 * BN) * 4;
-  static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per DMA instruction
-  static_assert((BX + BW) % WAVES == 0, "blocks must split evenly over the waves");
-  static_assert(MI >= 1 && NJ >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per copy instruction
+  static_assert((BX + BW + SCL) % WAVES == 0, "copies must split evenly over the waves");
+  static_assert(BX % WAVES == 0, "X copies take whole rounds over the waves");
+  static_assert(MI >= 1 && NJ >= 1, "wave tile");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "scalar loads cover whole tiles");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "scalar copies cover whole tiles");
 };
 
 // s_waitcnt vmcnt(N): expcnt and lgkmcnt fields left at their maxima
@@ -116,46 +127,77 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 // bank swizzle: chunk c of tile row r sits at slot c ^ g(r) of its 128-byte
 // row, so that the 16 (or 8) consecutive rows read together with one chunk
 // index cover distinct banks
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// The copies of one stage, dealt round-robin to the waves: X blocks, then W
+// blocks, then (Q4) scale copies.  Each lane keeps its source at K stage 0
+// and the source step per stage.
 template <class C>
 struct Loader {
-  const uint8_t* src[C::LOADS];  // this lane's source at K offset 0
-  int dst[C::LOADS];             // LDS byte offset of the block within a stage
+  const uint8_t* src[C::LOADS];
+  int step[C::LOADS];  // source bytes per stage
+  int dst[C::LOADS];   // LDS byte offset within a stage
+  int wave;
 
-  __device__ void init(const uint8_t* X, int64_t ldx_b, int M, const uint8_t* W, int64_t ldw_b, int N, int m0,
-                       int n0, int wave, int lane) {
+  __device__ void init(const GemmArgs& g, int m0, int n0, int wave_, int lane) {
+    constexpr int EB = C::INT ? 1 : 2;  // bytes per X (and int8 / fp16 W) element
+    const uint8_t* X = static_cast<const uint8_t*>(g.A);
+    const uint8_t* W = static_cast<const uint8_t*>(g.B);
+    const int64_t ldx = (int64_t)g.lda * EB;
+    wave = wave_;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int b = wave + C::WAVES * i;  // block index within the stage
-      const bool isx = b < C::BX;
-      const int bb = isx ? b : b - C::BX;
-      const int tr = bb * C::RPB + lane / C::CPR;  // tile row
-      const int rows = isx ? M : N;
-      int r = (isx ? m0 : n0) + tr;
-      r = r < rows ? r : rows - 1;  // rows past the edge re-read a valid row; their results are dropped
-      const int chunk = (lane % C::CPR) ^ swz(tr);
-      const uint8_t* base = isx ? X : W;
-      const int64_t ld = isx ? ldx_b : ldw_b;
-      src[i] = base + (int64_t)r * ld + chunk * 16;
-      dst[i] = b * BLK;
+      const int b = wave + C::WAVES * i;  // copy index within the stage
+      if (b < C::BX) {  // X: lane l fetches row l / 8 of the block, swizzled chunk
+        const int tr = b * 8 + (lane >> 3);
+        const int r = min(m0 + tr, g.M - 1);  // rows past the edge re-read a valid row; results dropped
+        src[i] = X + (int64_t)r * ldx + ((lane & 7) ^ swz(tr)) * 16;
+        step[i] = KB;
+        dst[i] = b * BLK;
+      } else if (b < C::BX + C::BW) {
+        const int bw = b - C::BX;
+        if constexpr (!C::Q4) {  // int8 / fp16 W: same layout as X
+          const int tr = bw * 8 + (lane >> 3);
+          const int r = min(n0 + tr, g.N - 1);
+          src[i] = W + (int64_t)r * ((int64_t)g.K * EB) + ((lane & 7) ^ swz(tr)) * 16;
+          step[i] = KB;
+        } else {  // packed W: lane l fetches group l / 32 of the stage of row l % 32
+          const int tr = bw * 32 + (lane & 31);
+          const int r = min(n0 + tr, g.N - 1);
+          src[i] = W + (int64_t)r * (g.K / 2) + (lane >> 5) * 16;
+          step[i] = 32;
+        }
+        dst[i] = C::W_OFF + bw * BLK;
+      } else {  // Q4 scales: both fp16 group scales of a row (4 bytes); padding repeats the last copy
+        const int s = min(b - C::BX - C::BW, C::SC0 - 1);
+        const int r = min(n0 + s * 64 + lane, g.N - 1);
+        src[i] = reinterpret_cast<const uint8_t*>(g.b_scale) + (int64_t)r * (g.K / 32) * 2;
+        step[i] = 4;
+        dst[i] = C::S_OFF + (b - C::BX - C::BW) * 256;
+      }
     }
   }
-  __device__ __forceinline__ void issue(uint8_t* stage, int kbyte) { issue_part<0, 1>(stage, kbyte); }
   // part P of PARTS of the stage's copies (spread over the K slices so the
-  // wave keeps feeding MFMAs while the memory pipeline accepts its loads)
+  // wave keeps feeding MFMAs while the memory pipeline accepts its copies)
   template <int P, int PARTS>
-  __device__ __forceinline__ void issue_part(uint8_t* stage, int kbyte) {
+  __device__ __forceinline__ void issue_part(uint8_t* stage, int kt) {
     constexpr int lo = C::LOADS * P / PARTS, hi = C::LOADS * (P + 1) / PARTS;
 #pragma unroll
-    for (int i = lo; i < hi; ++i)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[i] + kbyte), (lds_void*)(stage + dst[i]), 16, 0,
-                                       0);
+    for (int i = lo; i < hi; ++i) {
+      const void* s = static_cast<const void*>(src[i] + (int64_t)kt * step[i]);
+      lds_void* d = (lds_void*)(stage + dst[i]);
+      if (C::Q4 && wave + C::WAVES * i >= C::BX + C::BW)  // uniform over the wave
+        __builtin_amdgcn_global_load_lds(s, d, 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(s, d, 16, 0, 0);
+    }
   }
+  __device__ __forceinline__ void issue(uint8_t* stage, int kt) { issue_part<0, 1>(stage, kt); }
 };
 
 __device__ __forceinline__ int xcd_tile(int bid, int nt) {
@@ -198,14 +240,40 @@ __device__ __forceinline__ void unpack_h8(uint4 raw, float f[8]) {
   }
 }
 
-template <class C, bool INT>
-__device__ __forceinline__ void mfma_slice(typename std::conditional<INT, v16i, v16f>::type (&acc)[C::NJ][C::MI],
-                                           const v4i (&xf)[C::MI], const v4i (&wf)[C::NJ]) {
+// 8 packed two's-complement nibbles (value e in bits 4e..4e+3) -> 8 x
+// fp16(q * s).  With the sign bit flipped a nibble is q + 8; the fp16 with
+// bit pattern 0x6400 | (q + 8) is 1024 + q + 8, so subtracting 1032 gives q
+// exactly, and the product with s is rounded once.  v_perm_b32 pairs
+// value 2i (byte i of the even nibbles) with value 2i + 1 (byte i of the odd
+// ones) as the two halves of register i.
+__device__ __forceinline__ v4i dequant8(uint32_t packed, v2h s2) {
+  const uint32_t w = packed ^ 0x88888888u;
+  const uint32_t ev = w & 0x0F0F0F0Fu;
+  const uint32_t od = (w >> 4) & 0x0F0F0F0Fu;
+  const v2h off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  v4i out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // selector bytes: ev byte i, zero, od byte i, zero
+    const uint32_t sel = (uint32_t)i | (0x0Cu << 8) | ((uint32_t)(4 + i) << 16) | (0x0Cu << 24);
+    const uint32_t h = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
+    const v2h q = __builtin_bit_cast(v2h, h) + off;
+    out[i] = __builtin_bit_cast(int, q * s2);
+  }
+  return out;
+}
+
+template <class C>
+using AccT = typename std::conditional<C::INT, v16i, v16f>::type;
+
+template <class C>
+__device__ __forceinline__ void mfma_slice(AccT<C> (&acc)[C::NJ][C::MI], const v4i (&xf)[C::MI],
+                                           const v4i (&wf)[C::NJ]) {
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) {
-      if constexpr (INT) {
+      if constexpr (C::INT) {
         acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j], xf[i], acc[j][i], 0, 0, 0);
       } else {
         acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, wf[j]),
@@ -214,25 +282,65 @@ __device__ __forceinline__ void mfma_slice(typename std::conditional<INT, v16i, 
     }
 }
 
-template <class C, bool INT, int EPI>
+// Operand fragments of K slice ks from a stage.  X (and int8 / fp16 W): 16
+// swizzled bytes per lane.  Q4 W: slice ks covers values 16 ks .. 16 ks + 15
+// of the stage, i.e. bytes 8 (ks % 2) .. 8 (ks % 2) + 7 of group ks / 2; lane
+// l takes the 4 bytes at 4 (l / 32) of those and its row's scale.
+template <class C>
+struct Frags {
+  int off[C::KS];  // lane's byte offset of slice ks in a 32-row block (8-row blocks of 128 B)
+  int qoff;        // Q4: lane's packed word in a 32-row block
+  int soff;        // Q4: lane's scale pair in the stage's scale area
+
+  __device__ void init(int lane, int wn) {
+    const int lr = lane & 31;
+    const int lane_off = (lr >> 3) * BLK + (lr & 7) * KB;
+    const int g_l = swz(lr);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) off[ks] = lane_off + (((2 * ks + (lane >> 5)) ^ g_l) << 4);
+    qoff = lr * 16 + (lane >> 5) * 4;
+    soff = (wn * C::WN + lr) * 4;
+  }
+  __device__ __forceinline__ void read(const uint8_t* stage, int wm, int wn, int ks, v4i (&xf)[C::MI],
+                                       v4i (&wf)[C::NJ]) const {
+    constexpr int B32 = 4 * BLK;  // 32 rows of 8-row blocks
+    const uint8_t* sx = stage + wm * C::MI * B32;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) xf[i] = *reinterpret_cast<const v4i*>(sx + i * B32 + off[ks]);
+    if constexpr (!C::Q4) {
+      const uint8_t* sw = stage + C::W_OFF + wn * C::NJ * B32;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) wf[j] = *reinterpret_cast<const v4i*>(sw + j * B32 + off[ks]);
+    } else {
+      const uint8_t* sw = stage + C::W_OFF + wn * C::NJ * BLK + (ks >> 1) * 512 + (ks & 1) * 8 + qoff;
+      const uint8_t* ss = stage + C::S_OFF + soff + (ks >> 1) * 2;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const uint32_t packed = *reinterpret_cast<const uint32_t*>(sw + j * BLK);
+        const _Float16 s = *reinterpret_cast<const _Float16*>(ss + j * 32 * 4);
+        wf[j] = dequant8(packed, v2h{s, s});
+      }
+    }
+  }
+};
+
+template <class C, int EPI>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const int nt = gridDim.x;
   int tm, tn;
   tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
-
-  constexpr int EB = INT ? 1 : 2;  // bytes per element
-  const int nk = g.K * EB / C::KB;
+  constexpr bool INT = C::INT;
+  const int nk = g.K * (INT ? 1 : 2) / KB;
 
   Loader<C> ld;
-  ld.init(static_cast<const uint8_t*>(g.A), g.lda * EB, g.M, static_cast<const uint8_t*>(g.B), (int64_t)g.K * EB,
-          g.N, m0, n0, wave, lane);
+  ld.init(g, m0, n0, wave, lane);
 
-  typedef typename std::conditional<INT, v16i, v16f>::type Acc;
-  Acc acc[C::NJ][C::MI];
+  AccT<C> acc[C::NJ][C::MI];
 #pragma unroll
   for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
@@ -261,18 +369,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   }
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) ld.issue(smem + s * C::STAGE_BYTES, s * C::KB);
+    if (s < nk) ld.issue(smem + s * C::STAGE_BYTES, s);
 
-  // fragment (32-row block, 32-byte slice ks) of lane l: row l % 32, chunk 2 ks + l / 32
-  const int lr = lane & 31;
-  const int lane_off = (lr / C::RPB) * BLK + (lr % C::RPB) * C::KB;
-  const int g_l = swz(lr);
-  int koff[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = lane_off + (((2 * ks + (lane >> 5)) ^ g_l) << 4);
-  constexpr int B32 = 32 / C::RPB * BLK;  // bytes of 32 tile rows
-  const int xbase = wm * C::MI * B32;
-  const int wbase = C::BX * BLK + wn * C::NJ * B32;
+  Frags<C> fr;
+  fr.init(lane, wn);
 
   // Per stage: wait for its copies, barrier, then four 32-byte K slices.  A
   // quarter of the next stage's copies is issued before each slice's MFMAs
@@ -284,30 +384,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
     const int kn = kt + C::STAGES - 1;
     const bool more = kn < nk;
     uint8_t* const snext = smem + (kn % C::STAGES) * C::STAGE_BYTES;
-    const uint8_t* sx = smem + (kt % C::STAGES) * C::STAGE_BYTES + xbase;
-    const uint8_t* sw = smem + (kt % C::STAGES) * C::STAGE_BYTES + wbase;
+    const uint8_t* const stage = smem + (kt % C::STAGES) * C::STAGE_BYTES;
     v4i xf[2][C::MI], wf[2][C::NJ];
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) xf[0][i] = *reinterpret_cast<const v4i*>(sx + i * B32 + koff[0]);
-#pragma unroll
-    for (int j = 0; j < C::NJ; ++j) wf[0][j] = *reinterpret_cast<const v4i*>(sw + j * B32 + koff[0]);
+    fr.read(stage, wm, wn, 0, xf[0], wf[0]);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (more) {
-        if (ks == 0) ld.template issue_part<0, C::KS>(snext, kn * C::KB);
-        if (ks == 1) ld.template issue_part<1, C::KS>(snext, kn * C::KB);
-        if (ks == 2) ld.template issue_part<2, C::KS>(snext, kn * C::KB);
-        if (ks == 3) ld.template issue_part<3, C::KS>(snext, kn * C::KB);
+        if (ks == 0) ld.template issue_part<0, C::KS>(snext, kn);
+        if (ks == 1) ld.template issue_part<1, C::KS>(snext, kn);
+        if (ks == 2) ld.template issue_part<2, C::KS>(snext, kn);
+        if (ks == 3) ld.template issue_part<3, C::KS>(snext, kn);
       }
-      if (ks + 1 < C::KS) {
-#pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          xf[(ks + 1) & 1][i] = *reinterpret_cast<const v4i*>(sx + i * B32 + koff[ks + 1]);
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j)
-          wf[(ks + 1) & 1][j] = *reinterpret_cast<const v4i*>(sw + j * B32 + koff[ks + 1]);
-      }
-      mfma_slice<C, INT>(acc, xf[ks & 1], wf[ks & 1]);
+      if (ks + 1 < C::KS) fr.read(stage, wm, wn, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
+      mfma_slice<C>(acc, xf[ks & 1], wf[ks & 1]);
     }
   }
 
@@ -328,6 +417,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   const int cl = (lane % LPR) * 8;
   const int rl0 = lane / LPR;
   const int rbase = m0 + wm * C::WM;
+  const int lr = lane & 31;
   uint4 resv[RES ? NIT : 1];
   auto load_res = [&](int p) {
     if constexpr (RES) {
@@ -424,7 +514,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   }
 }
 
-template <class C, bool INT, int EPI>
+template <class C, int EPI>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + C::BM - 1) / C::BM, tn = (g.N + C::BN - 1) / C::BN;
   // each XCD gets about tiles / 8 consecutive tiles; make that run a block of
@@ -433,75 +523,87 @@ void launch_cfg(const GemmArgs& g, hipStream_t st) {
   int gm = (int)(sqrtf((float)run) + 0.5f);
   gm = std::max(gm, (run + tn - 1) / tn);
   gm = std::max(1, std::min(gm, tm));
-  hipLaunchKernelGGL((gemm_dma_kernel<C, INT, EPI>), dim3((unsigned)(tm * tn)), dim3(C::THREADS), C::LDS_TOTAL, st,
-                     g, tn, gm);
+  hipLaunchKernelGGL((gemm_dma_kernel<C, EPI>), dim3((unsigned)(tm * tn)), dim3(C::THREADS), C::LDS_TOTAL, st, g,
+                     tn, gm);
 }
 
-template <class C, bool INT>
+template <class C>
 void launch_epi(const GemmArgs& g, hipStream_t st) {
   const bool res = g.epi.residual != nullptr, gelu = g.epi.act == 1;
-  if (gelu && res) launch_cfg<C, INT, EPI_GELU_RES>(g, st);
-  else if (gelu) launch_cfg<C, INT, EPI_GELU>(g, st);
-  else if (res) launch_cfg<C, INT, EPI_RES>(g, st);
-  else launch_cfg<C, INT, EPI_PLAIN>(g, st);
+  if (gelu && res) launch_cfg<C, EPI_GELU_RES>(g, st);
+  else if (gelu) launch_cfg<C, EPI_GELU>(g, st);
+  else if (res) launch_cfg<C, EPI_RES>(g, st);
+  else launch_cfg<C, EPI_PLAIN>(g, st);
 }
 
-template <class C, bool INT>
+template <class C>
 void prep_cfg() {
-  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_PLAIN>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_RES>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_GELU>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, INT, EPI_GELU_RES>)};
+  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES>)};
   for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
 }
 
-// tile configurations (BM, BN, waves M x N, stages)
-using C256x256 = Cfg<256, 256, 2, 2, 2>;
-using C128x128 = Cfg<128, 128, 2, 2, 4>;
-using C128x64 = Cfg<128, 64, 2, 2, 5>;
-using C64x64 = Cfg<64, 64, 2, 2, 8>;
+// tile configurations per mode (BM, BN, stages): a Q4 stage is smaller, so
+// its 256 x 256 tile keeps three stages in flight
+template <int MODE>
+struct Tiles {
+  using T256 = Cfg<256, 256, MODE == M_Q4 ? 3 : 2, MODE>;
+  using T128 = Cfg<128, 128, 4, MODE>;
+  using T128x64 = Cfg<128, 64, 5, MODE>;
+  using T64 = Cfg<64, 64, 8, MODE>;
+};
 
 int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-template <bool INT>
+template <int MODE>
 void dispatch(const GemmArgs& g, hipStream_t st) {
   // largest tile that still fills most of the 256 CUs with one workgroup each
   // (one round of 192 large tiles beats three rounds of smaller ones)
   constexpr int64_t FILL = 180;
-  if (tiles(g.M, g.N, 256, 256) >= FILL) launch_epi<C256x256, INT>(g, st);
-  else if (tiles(g.M, g.N, 128, 128) >= FILL) launch_epi<C128x128, INT>(g, st);
-  else if (tiles(g.M, g.N, 128, 64) >= FILL) launch_epi<C128x64, INT>(g, st);
-  else launch_epi<C64x64, INT>(g, st);
+  using T = Tiles<MODE>;
+  if (tiles(g.M, g.N, 256, 256) >= FILL) launch_epi<typename T::T256>(g, st);
+  else if (tiles(g.M, g.N, 128, 128) >= FILL) launch_epi<typename T::T128>(g, st);
+  else if (tiles(g.M, g.N, 128, 64) >= FILL) launch_epi<typename T::T128x64>(g, st);
+  else launch_epi<typename T::T64>(g, st);
+}
+
+template <int MODE>
+void prep_mode() {
+  using T = Tiles<MODE>;
+  prep_cfg<typename T::T256>();
+  prep_cfg<typename T::T128>();
+  prep_cfg<typename T::T128x64>();
+  prep_cfg<typename T::T64>();
 }
 
 }  // namespace
 
 void gemm_dma_prepare() {
-  prep_cfg<C256x256, true>();
-  prep_cfg<C128x128, true>();
-  prep_cfg<C128x64, true>();
-  prep_cfg<C64x64, true>();
-  prep_cfg<C256x256, false>();
-  prep_cfg<C128x128, false>();
-  prep_cfg<C128x64, false>();
-  prep_cfg<C64x64, false>();
+  prep_mode<M_I8>();
+  prep_mode<M_F16>();
+  prep_mode<M_Q4>();
 }
 
 bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
   const bool i8 = akind == A_I8 && bkind == B_I8;
   const bool f16 = akind == A_F16 && bkind == B_F16;
-  if (!(i8 || f16)) return false;
+  const bool q4 = akind == A_F16 && bkind == B_Q4;
+  if (!(i8 || f16 || q4)) return false;
   const int64_t kb = (int64_t)g.K * (i8 ? 1 : 2);
-  if (kb % 128 != 0) return false;  // whole 128-byte stages
+  if (kb % KB != 0) return false;  // whole 128-byte X stages (Q4: whole pairs of groups)
   const int64_t ldb = (int64_t)g.lda * (i8 ? 1 : 2);
   if (ldb % 16 != 0) return false;
   if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
+  if (q4 && (reinterpret_cast<uintptr_t>(g.b_scale) & 3)) return false;
   return g.M > 0 && g.N > 0;
 }
 
-void launch_gemm_dma(int akind, const GemmArgs& g, hipStream_t st) {
-  if (akind == A_I8) dispatch<true>(g, st);
-  else dispatch<false>(g, st);
+void launch_gemm_dma(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
+  if (akind == A_I8) dispatch<M_I8>(g, st);
+  else if (bkind == B_Q4) dispatch<M_Q4>(g, st);
+  else dispatch<M_F16>(g, st);
 }
 
 }  // namespace ald

@@ -60,10 +60,10 @@ void launch_q4_pack(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* 
 void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st);
 void gemm_prepare();  // one-time kernel attributes (large dynamic LDS)
 
-// pipelined direct-to-LDS MFMA GEMM (gemm_dma.hip): int8 x int8 or fp16 x fp16
-// with K-contiguous operands whose K bytes are a multiple of 128
+// pipelined direct-to-LDS MFMA GEMM (gemm_dma.hip): int8 x int8, fp16 x fp16 or
+// fp16 x 4-bit with K-contiguous operands whose X row bytes are a multiple of 128
 bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g);
-void launch_gemm_dma(int akind, const GemmArgs& g, hipStream_t st);
+void launch_gemm_dma(int akind, int bkind, const GemmArgs& g, hipStream_t st);
 void gemm_dma_prepare();
 
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st);

@@ -155,7 +155,7 @@ def test_f16_linear(M, K, N):
     f16_close(host(y), O.f16_linear(x, w, b, act=1))
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (77, 96, 130), (256, 2048, 64), (300, 1024, 520)])
+@pytest.mark.parametrize("M,K,N", [(1, 32, 1), (77, 96, 130), (256, 2048, 64), (300, 1024, 520), (200, 640, 203)])
 def test_q4_linear(M, K, N):
     r = rng(M * 3 + K + N)
     x = r.standard_normal((M, K)).astype(np.float16)
@@ -165,6 +165,22 @@ def test_q4_linear(M, K, N):
     p, s = O.quantize_q4(w)
     y = B.q4_linear(dev(x), dev(p), dev(s), dev(b), residual=dev(res))
     f16_close(host(y), O.q4_linear(x, p, s, b, residual=res))
+
+
+@pytest.mark.parametrize("M,K,N", [(8192, 2048, 6144), (8192, 8192, 2048)])
+def test_q4_full_shapes_sampled(M, K, N):
+    """4-bit weight GEMMs at the full 4-request x 1024-token CFG batch (8192
+    rows, hidden 2048, MLP 8192) in the step's launch configuration, checked
+    on sampled rows against the oracle."""
+    r = rng(M + K + N)
+    g = torch.Generator(device="cuda").manual_seed(K + N)
+    x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    p, s = O.quantize_q4(w)
+    y = B.q4_linear(x, dev(p), dev(s), dev(b), act=L.ALD_ACT_GELU)
+    rows = np.concatenate([np.sort(rng(1).choice(M, 40, replace=False)), [0, M - 1]])
+    f16_close(host(y)[rows], O.q4_linear(host(x)[rows], p, s, b, act=1))
 
 
 # ------------------------------------------------------------- attention
