@@ -12,8 +12,10 @@ fresh request: the latent is reset from its initial noise first); `value` is
 denoise steps per second.  The JSON line also carries the roofline of the
 dominant kernel (the W8A8 GEMM, timed live with HIP events on its own launch
 stream at the step's shapes), the W8A8 GEMM at the serving-batch shapes
-(hidden 1536, 8192 tokens) as % of the int8 MFMA peak, and the CPU oracle
-timed on a bounded sample on the host cores.
+(hidden 1536, 8192 tokens) as % of the int8 MFMA peak, per-kernel rooflines
+(attention, fp16- and 4-bit-weight GEMMs at the large workload shapes; the
+HBM-bound kernels on stress shapes beyond the last-level cache), and the CPU
+oracle timed on a bounded sample on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -117,6 +119,111 @@ def serve_gemm(iters=20):
     return {"shapes": out, "tops": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
 
 
+def _timed(fn, iters=10):
+    import torch
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    return _events_time(fn, iters, torch.cuda.current_stream())
+
+
+def _entry(kind, ms, work, peak, unit, **extra):
+    """One kernel's roofline: algorithmic work per launch over the launch time."""
+    achieved = work / (ms / 1e3) / (1e9 if unit == "GB/s" else 1e12)
+    d = {"bound": kind, "avg_launch_us": round(ms * 1e3, 2), "achieved": round(achieved, 1), "peak": peak,
+         "unit": unit, "frac": round(achieved / peak, 4)}
+    d.update(extra)
+    return d
+
+
+def kernel_rooflines():
+    """Per-kernel rooflines at the large workload shapes, each kernel launched
+    through the C ABI on torch's current stream and timed there with HIP
+    events: flash attention (serving and 4-bit-model shapes), the fp16- and
+    4-bit-weight GEMMs (serving and 4-bit-model launch mixes), and the
+    HBM-bound kernels on stress shapes larger than the 256 MB last-level
+    cache (same row widths as the serving model)."""
+    import torch
+    from audio_latent_diffusion_amd import binding as B
+    from audio_latent_diffusion_amd import _lib as L
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {}
+
+    # attention: self-attention of the serving batch (16 rows x 512 tokens,
+    # 24 heads) and of the 4-bit model (8 rows x 1024 tokens, 32 heads)
+    for name, (Bn, S, nh) in {"attn_serve": (16, 512, 24), "attn_q4": (8, 1024, 32)}.items():
+        qkv = torch.randn((Bn * S, 3 * nh * 64), dtype=torch.float16, device="cuda", generator=g)
+        o = torch.empty((Bn * S, nh * 64), dtype=torch.float16, device="cuda")
+        q, k, v = qkv[:, :nh * 64], qkv[:, nh * 64:2 * nh * 64], qkv[:, 2 * nh * 64:]
+        ms = _timed(lambda: B.attn_fwd(q, k, v, nh, Bn, S, S, out=o))
+        out[name] = _entry("mfma", ms, 4.0 * Bn * nh * S * S * 64, FP16_PEAK_TFLOPS, "TFLOP/s",
+                           shape=f"batch {Bn} x {S} tokens x {nh} heads, head dim 64")
+        del qkv, o
+
+    # fp16-weight GEMMs (serving block mix) and 4-bit-weight GEMMs (4-bit model mix)
+    for name, M, shapes, q4 in (("f16_gemm_serve", 8192, MIX_SHAPES(1536, 6144), False),
+                                ("q4_gemm", 8192, MIX_SHAPES(2048, 8192), True)):
+        launches, flops = [], 0.0
+        for K, N in shapes:
+            x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+            w = (0.02 * torch.randn((N, K), device="cuda", generator=g)).half()
+            b = torch.zeros(N, device="cuda")
+            y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            if q4:
+                p, sc = B.quantize_q4(w)
+                launches.append(lambda x=x, p=p, sc=sc, b=b, y=y: B.q4_linear(x, p, sc, b, y=y))
+            else:
+                launches.append(lambda x=x, w=w, b=b, y=y: B.f16_linear(x, w, b, y=y))
+            flops += 2.0 * M * N * K
+
+        def mix(launches=launches):
+            for f in launches:
+                f()
+        ms = _timed(mix, 5) / len(shapes)
+        out[name] = _entry("mfma", ms, flops / len(shapes), FP16_PEAK_TFLOPS, "TFLOP/s",
+                           shape=f"M {M}, per-block launch mix (K, N) {shapes}")
+        del launches
+
+    # HBM-bound kernels on stress shapes
+    M, H, F = 1 << 18, 1536, 6144
+    x = torch.randn((M, H), dtype=torch.float16, device="cuda", generator=g)
+    gam = torch.ones(H, device="cuda")
+    bet = torch.zeros(H, device="cuda")
+    q = torch.empty((M, H), dtype=torch.int8, device="cuda")
+    s = torch.empty(M, device="cuda")
+    ms = _timed(lambda: B.ln_quant(x, gam, bet, q=q, scale=s))
+    out["ln_quant"] = _entry("hbm", ms, 3.0 * M * H + 4.0 * M, HBM_PEAK_GBS, "GB/s", shape=f"{M} x {H}")
+    alpha = torch.full((1,), 0.5, device="cuda")
+    d = torch.randn(H, device="cuda", generator=g)
+    d /= d.norm()
+    ms = _timed(lambda: B.steer_add(x, alpha, 1.0, d))
+    out["steer_add"] = _entry("hbm", ms, 4.0 * M * H, HBM_PEAK_GBS, "GB/s", shape=f"{M} x {H}")
+    del x, q
+    Mf = M // 4
+    xf = torch.randn((Mf, F), dtype=torch.float16, device="cuda", generator=g)
+    qf = torch.empty((Mf, F), dtype=torch.int8, device="cuda")
+    sf = torch.empty(Mf, device="cuda")
+    ms = _timed(lambda: B.quantize_rows_q8(xf, q=qf, scale=sf))
+    out["act_quant"] = _entry("hbm", ms, 3.0 * Mf * F + 4.0 * Mf, HBM_PEAK_GBS, "GB/s", shape=f"{Mf} x {F}")
+    del xf, qf
+    n_tok, C = 1 << 22, 64
+    v = torch.randn((2 * n_tok, C), dtype=torch.float16, device="cuda", generator=g)
+    w = torch.full((1,), 3.0, device="cuda")
+    vh = torch.empty((n_tok, C), device="cuda")
+    ms = _timed(lambda: B.cfg_merge(v, w, rows_per_req=n_tok, v_hat=vh))
+    out["cfg_merge"] = _entry("hbm", ms, 8.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
+    del v
+    xs = torch.randn((n_tok, C), device="cuda", generator=g)
+    tc = torch.full((1,), 1.0, device="cuda")
+    tn = torch.full((1,), 0.875, device="cuda")
+    ms = _timed(lambda: B.sampler_update(L.ALD_EULER, xs, tc, tn, v_hat=vh, rows_per_req=n_tok))
+    out["sampler_euler"] = _entry("hbm", ms, 12.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
+    del xs, vh
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, params, inp, resid, budget_s=20.0):
     """The oracle, as it stands, on the host cores: denoise steps of the same
     workload, as many whole steps as fit the budget (at least one)."""
@@ -190,6 +297,8 @@ def counter_legs(legs, reps):
         run_mix = gemm_mix(I.MID)
         for _ in range(reps):
             run_mix()
+    if "kernels" in legs:
+        kernel_rooflines()
     if "copy" in legs:
         # an elementwise kernel that reads one buffer and writes another, both
         # larger than the 256 MB last-level cache
@@ -209,7 +318,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16, help="untimed denoise steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--leg", default="", help="counter legs only (gemm,copy) for rocprofv3 --pmc runs")
+    ap.add_argument("--leg", default="", help="counter legs only (gemm,kernels,copy) for rocprofv3 runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -281,6 +390,7 @@ def main():
     achieved = ops_launch / (ms_launch / 1e3) / 1e12
     traffic = measured_traffic()
     serve = serve_gemm()
+    kernels = kernel_rooflines()
 
     line = {
         "metric": "DiT denoise steps/s (CFG batch) + W8A8 GEMM % of int8 MFMA peak on 1 GPU",
@@ -309,6 +419,7 @@ def main():
                      "avg_launch_us": round(ms_launch * 1e3, 2),
                      "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
         "w8a8_gemm_serve": serve,
+        "kernels": kernels,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(cfg, params, inp, resid, args.cpu_budget)
