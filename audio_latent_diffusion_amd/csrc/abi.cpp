@@ -483,6 +483,7 @@ int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req, const i
   if (n_tok == 0) return ALD_OK;
   CHECK(v && w && v_hat && al16(v) && al16(v_hat), ALD_E_INVALID);
   CHECK(C % 8 == 0, ALD_E_INVALID);
+  CHECK(n_tok * (C / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
   if (!row_req) CHECK(rows_per_req > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, INT32_MAX, row_req};
   launch_cfg_merge(v, n_tok, C, map, w, v_hat, stream);
@@ -496,6 +497,7 @@ int sampler_update(int op, float* x, const float* v_hat, const float* x0, const 
   CHECK(n_tok >= 0 && C > 0, ALD_E_INVALID);
   if (n_tok == 0) return ALD_OK;
   CHECK(x && t_cur && al16(x) && C % 4 == 0, ALD_E_INVALID);
+  CHECK(n_tok * (C / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
   if (!row_req) CHECK(rows_per_req > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, INT32_MAX, row_req};
   if (op == ALD_EULER) {

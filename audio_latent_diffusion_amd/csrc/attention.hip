@@ -147,6 +147,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int kc = 0; kc < 2; ++kc)
         vf[db][kc] = *reinterpret_cast<const v8h*>(&sV[s][(db * 16 + ql) * SROW + 32 * kc + 8 * g]);
 
+    // scores of a full tile need no key mask; only the last tile can be partial
+    const bool full = kbase + KT <= k_len;
 #pragma unroll
     for (int qb = 0; qb < QW; ++qb) {
       v4f sc[4];
@@ -157,35 +159,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][1], qf[qb][1], z, 0, 0, 0);
         sc[kb] = z;
       }
-      float mx = -INFINITY;
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kbase + kb * 16 + g * 4 + r >= k_len) sc[kb][r] = -INFINITY;
+      }
+      // running maximum of the raw scores (the softmax scale c > 0 commutes
+      // with max), then p = 2^(c s - c m) with one fused multiply-add
+      float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int kv = kbase + kb * 16 + g * 4 + r;
-          float v = kv < k_len ? sc[kb][r] * a.scale_log2 : -INFINITY;
-          sc[kb][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float corr = exp2f(m_run[qb] - m_new);
+      const float m_old = m_run[qb];
+      const float m_new = fmaxf(m_old, mx);
       m_run[qb] = m_new;
+      const float c = a.scale_log2;
+      const float cm = -c * m_new;
       float psum = 0.0f;
       v8h pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float p = exp2f(sc[kb][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, cm));
           psum += p;
           pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)p;
         }
-      l_run[qb] = l_run[qb] * corr + psum;
+      // the output and the row sum are rescaled only when some row's maximum
+      // moved (a factor of exactly 1 otherwise, so skipping is exact)
+      if (__any(m_new != m_old)) {
+        const float corr = __builtin_amdgcn_exp2f(c * (m_old - m_new));
+        l_run[qb] = l_run[qb] * corr + psum;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[qb][db] *= corr;
+      } else {
+        l_run[qb] += psum;
+      }
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        v4f o = oacc[qb][db] * corr;
+        v4f o = oacc[qb][db];
         o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db][0], pf[0], o, 0, 0, 0);
         o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db][1], pf[1], o, 0, 0, 0);
         oacc[qb][db] = o;

@@ -1,143 +1,169 @@
 // Bandwidth-bound elementwise kernels: steering add, CFG merge, sampler
 // updates (Euler, warm-start re-noise), their fusion used inside the step,
 // per-row L2 norms (steering calibration) and the CFG-pair sequence offsets.
-// Every thread moves one 16-byte (fp16 x 8) or 16-byte (fp32 x 4) vector.
+//
+// Latent kernels: one thread per vector of 4 consecutive latent values,
+// streamed with nontemporal loads and stores (data touched once); measured on
+// MI355X, more vectors per thread or grid-stride loops only lowered the
+// achieved bandwidth.  Index arithmetic is 32-bit (the C ABI bounds the vector
+// count).  Steering: one wave per row, the direction held in registers, rows
+// walked with the grid's stride.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace ald {
 
-__device__ __forceinline__ int req_of(const RowMap& m, int64_t row) {
-  int64_t i = m.n_tok_mod ? row % m.n_tok_mod : row;
-  return m.row_req ? m.row_req[i] : (int)((i / m.rows_per_req) % m.R);
+__device__ __forceinline__ int req_of(const RowMap& m, uint32_t row) {
+  const uint32_t i = m.n_tok_mod ? row % (uint32_t)m.n_tok_mod : row;
+  return m.row_req ? m.row_req[i] : (int)((i / (uint32_t)m.rows_per_req) % (uint32_t)m.R);
 }
 
 // h[m, :] += (alpha[r] * resid_norm) * dir  -- rows with alpha == 0 untouched
+template <int NV>
 __global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, int64_t ldh, int M, int H, RowMap map,
                                                     const float* __restrict__ alpha, float resid_norm,
                                                     const float* __restrict__ dir) {
-  const int cpr = H >> 3;  // 8-element chunks per row
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)M * cpr) return;
-  const int64_t row = idx / cpr;
-  const int c = (int)(idx - row * cpr) * 8;
-  const float a = alpha[req_of(map, row)];
-  if (a == 0.0f) return;  // exact no-op: no write at all
-  const float coef = a * resid_norm;
-  uint16_t* p = h + row * ldh + c;
-  v4i raw = ld16(p);
-  uint16_t* hv = reinterpret_cast<uint16_t*>(&raw);
-  const float4 d0 = *reinterpret_cast<const float4*>(dir + c);
-  const float4 d1 = *reinterpret_cast<const float4*>(dir + c + 4);
-  const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x * 4;
+  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  float dv[NV][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) hv[i] = f2h(h2f(hv[i]) + coef * dd[i]);
-  st16(p, raw);
+  for (int j = 0; j < NV; ++j) {
+    const int e = (lane + WAVE * j) * 8;
+    if (e < H) {
+      const float4 d0 = *reinterpret_cast<const float4*>(dir + e);
+      const float4 d1 = *reinterpret_cast<const float4*>(dir + e + 4);
+      dv[j][0] = d0.x; dv[j][1] = d0.y; dv[j][2] = d0.z; dv[j][3] = d0.w;
+      dv[j][4] = d1.x; dv[j][5] = d1.y; dv[j][6] = d1.z; dv[j][7] = d1.w;
+    }
+  }
+  for (; m < M; m += stride) {
+    const float a = alpha[req_of(map, (uint32_t)m)];
+    if (a == 0.0f) continue;  // exact no-op: no write at all (uniform over the wave)
+    const float coef = a * resid_norm;
+    uint16_t* row = h + (int64_t)m * ldh;
+    v4i raw[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 8;
+      if (e < H) raw[j] = ld16_nt(row + e);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 8;
+      if (e < H) {
+        uint16_t* hv = reinterpret_cast<uint16_t*>(&raw[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = f2h(h2f(hv[i]) + coef * dv[j][i]);
+        st16_nt(row + e, raw[j]);
+      }
+    }
+  }
 }
 
-__device__ __forceinline__ void load4h(const uint16_t* p, float f[4]) {
-  uint2 r = *reinterpret_cast<const uint2*>(p);
-  const uint16_t* h = reinterpret_cast<const uint16_t*>(&r);
+__device__ __forceinline__ void load4h_nt(const uint16_t* p, float f[4]) {
+  const v2i r = ld8_nt(p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = h2f(h[i]);
+  for (int i = 0; i < 2; ++i) {
+    f[2 * i] = h2f((uint16_t)((uint32_t)r[i] & 0xFFFFu));
+    f[2 * i + 1] = h2f((uint16_t)((uint32_t)r[i] >> 16));
+  }
+}
+__device__ __forceinline__ v4f ld4f_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ void st4f_nt(float* p, v4f v) { __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p)); }
+
+// this thread's vector: token and column (false past the end)
+__device__ __forceinline__ bool lat_vec(uint32_t n_tok, int C, uint32_t& tok, int& c) {
+  const uint32_t cq = (uint32_t)C >> 2;
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  tok = i / cq;
+  c = (int)(i - tok * cq) * 4;
+  return tok < n_tok;
 }
 
 // v_hat = w * cond + (1 - w) * uncond, fp32
-__global__ __launch_bounds__(256) void cfg_merge_kernel(const uint16_t* __restrict__ v, int64_t n_tok, int C,
+__global__ __launch_bounds__(256) void cfg_merge_kernel(const uint16_t* __restrict__ v, uint32_t n_tok, int C,
                                                         RowMap map, const float* __restrict__ w,
                                                         float* __restrict__ v_hat) {
-  const int cq = C >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_tok * cq) return;
-  const int64_t tok = idx / cq;
-  const int c = (int)(idx - tok * cq) * 4;
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  float fc[4], fu[4];
+  load4h_nt(v + (int64_t)tok * C + c, fc);
+  load4h_nt(v + ((int64_t)n_tok + tok) * C + c, fu);
   const float wr = w[req_of(map, tok)];
   const float wu = 1.0f - wr;
-  float fc[4], fu[4];
-  load4h(v + tok * C + c, fc);
-  load4h(v + (n_tok + tok) * C + c, fu);
-  float4 o;
-  o.x = wr * fc[0] + wu * fu[0];
-  o.y = wr * fc[1] + wu * fu[1];
-  o.z = wr * fc[2] + wu * fu[2];
-  o.w = wr * fc[3] + wu * fu[3];
-  *reinterpret_cast<float4*>(v_hat + tok * C + c) = o;
+  v4f o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = wr * fc[i] + wu * fu[i];
+  st4f_nt(v_hat + (int64_t)tok * C + c, o);
 }
 
 __global__ __launch_bounds__(256) void euler_kernel(float* __restrict__ x, const float* __restrict__ v_hat,
-                                                    int64_t n_tok, int C, RowMap map, const float* __restrict__ t_cur,
-                                                    const float* __restrict__ t_next,
+                                                    uint32_t n_tok, int C, RowMap map,
+                                                    const float* __restrict__ t_cur, const float* __restrict__ t_next,
                                                     const uint8_t* __restrict__ active) {
-  const int cq = C >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_tok * cq) return;
-  const int64_t tok = idx / cq;
-  const int c = (int)(idx - tok * cq) * 4;
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  v4f xv = ld4f_nt(x + o);
+  const v4f vv = ld4f_nt(v_hat + o);
   const int r = req_of(map, tok);
   if (active && !active[r]) return;
   const float dt = t_next[r] - t_cur[r];
-  float4* px = reinterpret_cast<float4*>(x + tok * C + c);
-  float4 xv = *px;
-  const float4 vv = *reinterpret_cast<const float4*>(v_hat + tok * C + c);
-  xv.x += dt * vv.x;
-  xv.y += dt * vv.y;
-  xv.z += dt * vv.z;
-  xv.w += dt * vv.w;
-  *px = xv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xv[i] += dt * vv[i];
+  st4f_nt(x + o, xv);
 }
 
 __global__ __launch_bounds__(256) void renoise_kernel(float* __restrict__ x, const float* __restrict__ x0,
-                                                      const float* __restrict__ eps, int64_t n_tok, int C, RowMap map,
+                                                      const float* __restrict__ eps, uint32_t n_tok, int C, RowMap map,
                                                       const float* __restrict__ t_cur,
                                                       const uint8_t* __restrict__ active) {
-  const int cq = C >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_tok * cq) return;
-  const int64_t tok = idx / cq;
-  const int c = (int)(idx - tok * cq) * 4;
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  const v4f av = ld4f_nt(x0 + o);
+  const v4f ev = ld4f_nt(eps + o);
   const int r = req_of(map, tok);
   if (active && !active[r]) return;
   const float t = t_cur[r];
   const float s = 1.0f - t;
-  const float4 a = *reinterpret_cast<const float4*>(x0 + tok * C + c);
-  const float4 e = *reinterpret_cast<const float4*>(eps + tok * C + c);
-  float4 o;
-  o.x = s * a.x + t * e.x;
-  o.y = s * a.y + t * e.y;
-  o.z = s * a.z + t * e.z;
-  o.w = s * a.w + t * e.w;
-  *reinterpret_cast<float4*>(x + tok * C + c) = o;
+  v4f out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = s * av[i] + t * ev[i];
+  st4f_nt(x + o, out);
 }
 
 // fused CFG merge + Euler for the step: v_hat never touches memory
 __global__ __launch_bounds__(256) void cfg_euler_kernel(const uint16_t* __restrict__ v, float* __restrict__ x,
-                                                        int64_t n_tok, int C, RowMap map, const float* __restrict__ w,
+                                                        uint32_t n_tok, int C, RowMap map, const float* __restrict__ w,
                                                         const float* __restrict__ t_cur,
                                                         const float* __restrict__ t_next,
                                                         const uint8_t* __restrict__ active) {
-  const int cq = C >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n_tok * cq) return;
-  const int64_t tok = idx / cq;
-  const int c = (int)(idx - tok * cq) * 4;
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  float fc[4], fu[4];
+  load4h_nt(v + o, fc);
+  load4h_nt(v + (int64_t)n_tok * C + o, fu);
+  v4f xv = ld4f_nt(x + o);
   const int r = req_of(map, tok);
   if (active && !active[r]) return;
   const float wr = w[r];
   const float wu = 1.0f - wr;
   const float dt = t_next[r] - t_cur[r];
-  float fc[4], fu[4];
-  load4h(v + tok * C + c, fc);
-  load4h(v + (n_tok + tok) * C + c, fu);
-  float4* px = reinterpret_cast<float4*>(x + tok * C + c);
-  float4 xv = *px;
-  float vh[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vh[i] = wr * fc[i] + wu * fu[i];
-  xv.x += dt * vh[0];
-  xv.y += dt * vh[1];
-  xv.z += dt * vh[2];
-  xv.w += dt * vh[3];
-  *px = xv;
+  for (int i = 0; i < 4; ++i) xv[i] += dt * (wr * fc[i] + wu * fu[i]);
+  st4f_nt(x + o, xv);
 }
 
 // per-row L2 norm (fp32), one wave per row
@@ -281,41 +307,46 @@ void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* 
 }
 
 static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+static inline dim3 grid_lat(int64_t n_tok, int C) { return grid_for(n_tok * (C / 4)); }
 
 void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
                   const float* dir, hipStream_t st) {
-  int64_t n = (int64_t)M * (H / 8);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(steer_kernel, grid_for(n), dim3(256), 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  if (M <= 0 || H <= 0) return;
+  dim3 grid((unsigned)std::min<int64_t>((M + 3) / 4, 2048)), block(256);
+  const int nv = (H + 511) / 512;
+  if (nv <= 1) hipLaunchKernelGGL(steer_kernel<1>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 2) hipLaunchKernelGGL(steer_kernel<2>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 3) hipLaunchKernelGGL(steer_kernel<3>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 4) hipLaunchKernelGGL(steer_kernel<4>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 8) hipLaunchKernelGGL(steer_kernel<8>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else hipLaunchKernelGGL(steer_kernel<16>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
 }
 
 void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,
                       hipStream_t st) {
-  int64_t n = n_tok * (C / 4);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(cfg_merge_kernel, grid_for(n), dim3(256), 0, st, v, n_tok, C, map, w, v_hat);
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(cfg_merge_kernel, grid_lat(n_tok, C), dim3(256), 0, st, v, (uint32_t)n_tok, C, map, w, v_hat);
 }
 
 void launch_euler(float* x, const float* v_hat, int64_t n_tok, int C, RowMap map, const float* t_cur,
                   const float* t_next, const uint8_t* active, hipStream_t st) {
-  int64_t n = n_tok * (C / 4);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(euler_kernel, grid_for(n), dim3(256), 0, st, x, v_hat, n_tok, C, map, t_cur, t_next, active);
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(euler_kernel, grid_lat(n_tok, C), dim3(256), 0, st, x, v_hat, (uint32_t)n_tok, C, map, t_cur,
+                     t_next, active);
 }
 
 void launch_renoise(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
                     const float* t_cur, const uint8_t* active, hipStream_t st) {
-  int64_t n = n_tok * (C / 4);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(renoise_kernel, grid_for(n), dim3(256), 0, st, x, x0, eps, n_tok, C, map, t_cur, active);
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(renoise_kernel, grid_lat(n_tok, C), dim3(256), 0, st, x, x0, eps, (uint32_t)n_tok, C, map,
+                     t_cur, active);
 }
 
 void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
                       const float* t_cur, const float* t_next, const uint8_t* active, hipStream_t st) {
-  int64_t n = n_tok * (C / 4);
-  if (n <= 0) return;
-  hipLaunchKernelGGL(cfg_euler_kernel, grid_for(n), dim3(256), 0, st, v, x, n_tok, C, map, w, t_cur, t_next,
-                     active);
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(cfg_euler_kernel, grid_lat(n_tok, C), dim3(256), 0, st, v, x, (uint32_t)n_tok, C, map, w,
+                     t_cur, t_next, active);
 }
 
 void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st) {

@@ -1,9 +1,14 @@
 // Bandwidth-bound row kernels: per-token int8 quantization, fused LayerNorm
 // (+ quantization), 4-bit weight packing.
 //
-// One wave (64 lanes) owns one row; the row is read once with 16-byte
-// coalesced loads into registers, reduced with cross-lane shuffles, and
-// written once.  Four rows per 256-thread workgroup.
+// One wave (64 lanes) owns one row at a time; the row is read once with
+// 16-byte coalesced loads into registers, reduced with DPP lane moves, and
+// written once.  Four waves per 256-thread workgroup; the grid is capped near
+// what the chip keeps resident and each wave walks rows with the grid's
+// stride, loading its next row before it reduces the current one, so the
+// loads of one row overlap the reductions and stores of the previous.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -19,7 +24,7 @@ __device__ __forceinline__ void load_row(RowRegs<NV>& r, const uint16_t* row, in
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     int e = (lane + WAVE * j) * 8;
-    if (e < K) r.c[j] = ld16(row + e);
+    if (e < K) r.c[j] = ld16_nt(row + e);
     else r.c[j] = v4i{0, 0, 0, 0};
   }
 }
@@ -30,14 +35,28 @@ __device__ __forceinline__ void unpack8(v4i c, float f[8]) {
   for (int i = 0; i < 8; ++i) f[i] = h2f(h[i]);
 }
 
-// codes of 8 fp16 values packed into two 32-bit words
-__device__ __forceinline__ uint2 quant8(const float f[8], float inv) {
-  uint32_t lo = 0, hi = 0;
+// Codes of 8 values packed into two 32-bit words.  Each code is the
+// round-half-even of the rounded fp32 product u * inv; adding 1.5 * 2^23
+// performs that rounding and leaves the code, in two's complement, in the
+// low byte of the sum's bits.  No clamp is needed: every u of the row has
+// |u| <= amax and inv = fp32(127 / amax), so |fp32(u * inv)| <= 127 (1 + 2^-24)^2
+// < 127.5 and the code stays within [-127, 127].  The product and the add
+// are kept apart (no fused multiply-add: the product is rounded first).
+__device__ __forceinline__ uint32_t code_bits(float u, float inv) {
+#pragma clang fp contract(off)
+  const float p = u * inv;
+  return __builtin_bit_cast(uint32_t, p + 12582912.0f);
+}
+__device__ __forceinline__ uint32_t pack4_codes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);  // a.byte0, b.byte0, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return lo | (hi << 16);
+}
+__device__ __forceinline__ v2i quant8(const float f[8], float inv) {
+  uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= (uint32_t)(q8_code(f[i], inv) & 0xFF) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= (uint32_t)(q8_code(f[4 + i], inv) & 0xFF) << (8 * i);
-  return make_uint2(lo, hi);
+  for (int i = 0; i < 8; ++i) c[i] = code_bits(f[i], inv);
+  return v2i{(int)pack4_codes(c[0], c[1], c[2], c[3]), (int)pack4_codes(c[4], c[5], c[6], c[7])};
 }
 
 // amax -> (scale, reciprocal); amax == 0 -> (0, 0) so every code is 0
@@ -51,139 +70,176 @@ __device__ __forceinline__ void q8_scale(float amax, float& s, float& inv) {
   }
 }
 
-template <int NV>
-__global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
-                                                        int K, int8_t* __restrict__ q, int64_t ldq,
-                                                        float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  RowRegs<NV> r;
-  load_row<NV>(r, x + (int64_t)m * ldx, K, lane);
+// codes and scale of one row held in registers
+template <int NV, bool FULL>
+__device__ __forceinline__ void quant_row_regs(const RowRegs<NV>& r, int K, int lane, int8_t* __restrict__ qrow,
+                                               float* __restrict__ scale_m) {
+  float f[NV][8];
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    float f[8];
-    unpack8(r.c[j], f);
+    unpack8(r.c[j], f[j]);  // padding chunks are zero
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
   }
-  amax = wave_max(amax);
+  amax = wave_max_nonneg(amax);
   float s, inv;
   q8_scale(amax, s, inv);
-  int8_t* qrow = q + (int64_t)m * ldq;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    int e = (lane + WAVE * j) * 8;
-    if (e < K) {
-      float f[8];
-      unpack8(r.c[j], f);
-      *reinterpret_cast<uint2*>(qrow + e) = quant8(f, inv);
-    }
+    const int e = (lane + WAVE * j) * 8;
+    if (FULL || e < K) st8_nt(qrow + e, quant8(f[j], inv));
   }
-  if (lane == 0) scale[m] = s;
+  if (lane == 0) *scale_m = s;
 }
 
-// LayerNorm of one row held in registers; result rounded to fp16 in place
-template <int NV>
-__device__ __forceinline__ void layer_norm_regs(RowRegs<NV>& r, int H, int lane, const float* __restrict__ g,
-                                                const float* __restrict__ b, float eps) {
+// rows of up to 6 x 512 values prefetch the next row; longer rows already
+// keep NV 16-byte loads per lane in flight and need the registers
+template <int NV, bool FULL>
+__global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
+                                                        int K, int8_t* __restrict__ q, int64_t ldq,
+                                                        float* __restrict__ scale) {
+  constexpr bool PREFETCH = NV <= 6;
+  const int lane = threadIdx.x & 63;
+  const int stride = gridDim.x * 4;
+  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  RowRegs<NV> r;
+  load_row<NV>(r, x + (int64_t)m * ldx, K, lane);
+  for (;;) {
+    const int mn = m + stride;
+    RowRegs<NV> nx;
+    if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, K, lane);
+    quant_row_regs<NV, FULL>(r, K, lane, q + (int64_t)m * ldq, scale + m);
+    if (mn >= M) break;
+    if (PREFETCH) r = nx;
+    else load_row<NV>(r, x + (int64_t)mn * ldx, K, lane);
+    m = mn;
+  }
+}
+
+// LayerNorm of one row held in registers (FULL: every chunk lies inside the
+// row): statistics in fp32 over the values converted once, output rounded to
+// fp16 into `out` (which may be `r` itself: r is read only before the first
+// write); u receives the fp16 result converted back to fp32 and the function
+// returns max |u| of this lane.
+template <int NV, bool FULL>
+__device__ __forceinline__ float layer_norm_row(const RowRegs<NV>& r, int H, int lane, const float* __restrict__ g,
+                                                const float* __restrict__ b, float eps, float (&u)[NV][8],
+                                                RowRegs<NV>& out) {
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    float f[8];
-    unpack8(r.c[j], f);
+    unpack8(r.c[j], u[j]);  // padding chunks are zero
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sum += f[i];
+    for (int i = 0; i < 8; ++i) sum += u[j][i];
   }
-  const float mean = wave_sum(sum) / (float)H;
+  const float inv_h = 1.0f / (float)H;  // loop-invariant: hoisted out of the row loop
+  const float mean = wave_sum(sum) * inv_h;
   float sq = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    int e = (lane + WAVE * j) * 8;
-    if (e < H) {
-      float f[8];
-      unpack8(r.c[j], f);
+    const int e = (lane + WAVE * j) * 8;
+    if (FULL || e < H) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float d = f[i] - mean;
-        sq += d * d;
+        u[j][i] -= mean;
+        sq = fmaf(u[j][i], u[j][i], sq);
       }
     }
   }
-  const float var = wave_sum(sq) / (float)H;
-  const float rstd = 1.0f / sqrtf(var + eps);
+  const float var = wave_sum(sq) * inv_h;
+  const float rstd = __builtin_amdgcn_rsqf(var + eps);  // hardware 1/sqrt (1 ulp)
+  float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    int e = (lane + WAVE * j) * 8;
-    if (e < H) {
-      float f[8];
-      unpack8(r.c[j], f);
+    const int e = (lane + WAVE * j) * 8;
+    if (FULL || e < H) {
       const float4 g0 = *reinterpret_cast<const float4*>(g + e);
       const float4 g1 = *reinterpret_cast<const float4*>(g + e + 4);
       const float4 b0 = *reinterpret_cast<const float4*>(b + e);
       const float4 b1 = *reinterpret_cast<const float4*>(b + e + 4);
       const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      uint16_t* h = reinterpret_cast<uint16_t*>(&r.c[j]);
+      uint16_t* h = reinterpret_cast<uint16_t*>(&out.c[j]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = f2h((f[i] - mean) * rstd * gg[i] + bb[i]);
+      for (int i = 0; i < 8; ++i) {
+        h[i] = f2h(fmaf(u[j][i] * rstd, gg[i], bb[i]));
+        u[j][i] = h2f(h[i]);
+        amax = fmaxf(amax, fabsf(u[j][i]));
+      }
     }
   }
+  return amax;
 }
 
-template <int NV>
+template <int NV, bool FULL>
 __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M, int H,
                                                        const float* __restrict__ g, const float* __restrict__ b,
                                                        float eps, uint16_t* __restrict__ u_out,
                                                        int8_t* __restrict__ q, float* __restrict__ scale) {
+  constexpr bool PREFETCH = NV <= 6;
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int stride = gridDim.x * 4;
+  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
   RowRegs<NV> r;
   load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
-  layer_norm_regs<NV>(r, H, lane, g, b, eps);
-  float amax = 0.0f;
+  for (;;) {
+    const int mn = m + stride;
+    RowRegs<NV> nx;
+    if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
+    float u[NV][8];
+    RowRegs<NV>& y = r;  // the normalized row replaces the input row
+    const float amax = wave_max_nonneg(layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, u, y));
+    float s, inv;
+    q8_scale(amax, s, inv);
+    int8_t* qrow = q + (int64_t)m * H;
+    uint16_t* urow = u_out ? u_out + (int64_t)m * H : nullptr;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float f[8];
-    unpack8(r.c[j], f);  // padding chunks are zero
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  }
-  amax = wave_max(amax);
-  float s, inv;
-  q8_scale(amax, s, inv);
-  int8_t* qrow = q + (int64_t)m * H;
-  uint16_t* urow = u_out ? u_out + (int64_t)m * H : nullptr;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    int e = (lane + WAVE * j) * 8;
-    if (e < H) {
-      float f[8];
-      unpack8(r.c[j], f);
-      *reinterpret_cast<uint2*>(qrow + e) = quant8(f, inv);
-      if (urow) st16(urow + e, r.c[j]);
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 8;
+      if (FULL || e < H) {
+        st8_nt(qrow + e, quant8(u[j], inv));
+        if (urow) st16_nt(urow + e, y.c[j]);
+      }
     }
+    if (lane == 0) scale[m] = s;
+    if (mn >= M) break;
+    if (PREFETCH) r = nx;
+    else load_row<NV>(r, x + (int64_t)mn * ldx, H, lane);
+    m = mn;
   }
-  if (lane == 0) scale[m] = s;
 }
 
-template <int NV>
+template <int NV, bool FULL>
 __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M, int H,
                                                      const float* __restrict__ g, const float* __restrict__ b,
                                                      float eps, uint16_t* __restrict__ y, int64_t ldy) {
+  constexpr bool PREFETCH = NV <= 6;
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int stride = gridDim.x * 4;
+  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
   RowRegs<NV> r;
   load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
-  layer_norm_regs<NV>(r, H, lane, g, b, eps);
-  uint16_t* yrow = y + (int64_t)m * ldy;
+  for (;;) {
+    const int mn = m + stride;
+    RowRegs<NV> nx;
+    if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
+    float u[NV][8];
+    RowRegs<NV>& o = r;  // the normalized row replaces the input row
+    (void)layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, u, o);
+    uint16_t* yrow = y + (int64_t)m * ldy;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    int e = (lane + WAVE * j) * 8;
-    if (e < H) st16(yrow + e, r.c[j]);
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 8;
+      if (FULL || e < H) st16_nt(yrow + e, o.c[j]);
+    }
+    if (mn >= M) break;
+    if (PREFETCH) r = nx;
+    else load_row<NV>(r, x + (int64_t)mn * ldx, H, lane);
+    m = mn;
   }
 }
 
@@ -225,15 +281,28 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------- launchers
 
+// at most this many 4-row workgroups: about what the 256 CUs keep resident
+constexpr int64_t ROW_GRID_CAP = 2048;
+
+#define ALD_ROW_LAUNCH(KERNEL, NV, K, GRID, ST, ...)                                                 \
+  do {                                                                                               \
+    if ((K) == (NV) * 512) hipLaunchKernelGGL((KERNEL<NV, true>), GRID, dim3(256), 0, ST, __VA_ARGS__); \
+    else hipLaunchKernelGGL((KERNEL<NV, false>), GRID, dim3(256), 0, ST, __VA_ARGS__);               \
+  } while (0)
+
+// one wave per row: NV 16-byte chunks per lane cover K values (NV * 512 >= K)
 #define ALD_ROW_DISPATCH(KERNEL, K, M, ST, ...)                                                      \
   do {                                                                                               \
-    dim3 grid((unsigned)(((M) + 3) / 4)), block(256);                                                \
-    int nv = ((K) + 511) / 512;                                                                      \
-    if (nv <= 1) hipLaunchKernelGGL(KERNEL<1>, grid, block, 0, ST, __VA_ARGS__);                     \
-    else if (nv <= 2) hipLaunchKernelGGL(KERNEL<2>, grid, block, 0, ST, __VA_ARGS__);                \
-    else if (nv <= 4) hipLaunchKernelGGL(KERNEL<4>, grid, block, 0, ST, __VA_ARGS__);                \
-    else if (nv <= 8) hipLaunchKernelGGL(KERNEL<8>, grid, block, 0, ST, __VA_ARGS__);                \
-    else hipLaunchKernelGGL(KERNEL<16>, grid, block, 0, ST, __VA_ARGS__);                            \
+    dim3 grid_((unsigned)std::min<int64_t>(((M) + 3) / 4, ROW_GRID_CAP));                            \
+    const int nv_ = ((K) + 511) / 512;                                                               \
+    if (nv_ <= 1) ALD_ROW_LAUNCH(KERNEL, 1, K, grid_, ST, __VA_ARGS__);                              \
+    else if (nv_ <= 2) ALD_ROW_LAUNCH(KERNEL, 2, K, grid_, ST, __VA_ARGS__);                         \
+    else if (nv_ <= 3) ALD_ROW_LAUNCH(KERNEL, 3, K, grid_, ST, __VA_ARGS__);                         \
+    else if (nv_ <= 4) ALD_ROW_LAUNCH(KERNEL, 4, K, grid_, ST, __VA_ARGS__);                         \
+    else if (nv_ <= 6) ALD_ROW_LAUNCH(KERNEL, 6, K, grid_, ST, __VA_ARGS__);                         \
+    else if (nv_ <= 8) ALD_ROW_LAUNCH(KERNEL, 8, K, grid_, ST, __VA_ARGS__);                         \
+    else if (nv_ <= 12) ALD_ROW_LAUNCH(KERNEL, 12, K, grid_, ST, __VA_ARGS__);                       \
+    else ALD_ROW_LAUNCH(KERNEL, 16, K, grid_, ST, __VA_ARGS__);                                      \
   } while (0)
 
 void launch_row_quant(const uint16_t* x, int64_t ldx, int M, int K, int8_t* q, int64_t ldq, float* scale,

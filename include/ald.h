@@ -194,7 +194,8 @@ int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R,
  * uncond rows [n_tok, 2 n_tok); token i belongs to request
  * r = row_req ? row_req[i] : i / rows_per_req, and
  *   v_hat[i, c] = w[r] * cond + (1 - w[r]) * uncond   (fp32)
- * w [R] fp32 device.  v_hat [n_tok, C] fp32 out. */
+ * w [R] fp32 device.  v_hat [n_tok, C] fp32 out.  C % 8 == 0; n_tok * C / 4
+ * below 2^31 (else ALD_E_UNSUPPORTED). */
 int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req,
               const int32_t* row_req, const float* w, float* v_hat,
               hipStream_t stream);
@@ -206,7 +207,8 @@ int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req,
  *   ALD_RENOISE: x  = (1 - t_cur[r]) * x0 + t_cur[r] * eps (warm start,
  *                SoundWeaver Section 2: forward-noise a cached clean latent
  *                to the skip time; eps is supplied by the caller).
- * Unused pointers (v_hat for RENOISE; x0, eps, t_next for EULER) may be NULL. */
+ * Unused pointers (v_hat for RENOISE; x0, eps, t_next for EULER) may be NULL.
+ * C % 4 == 0; n_tok * C / 4 below 2^31 (else ALD_E_UNSUPPORTED). */
 int sampler_update(int op, float* x, const float* v_hat, const float* x0,
                    const float* eps, int64_t n_tok, int C, int rows_per_req,
                    const int32_t* row_req, const float* t_cur,

@@ -78,6 +78,11 @@ def test_attention_and_elementwise_validation():
     assert lib.sampler_update(5, FAKE, FAKE, None, None, 10, 64, 10, None, FAKE, FAKE, None, None) == L.ALD_E_INVALID
     assert lib.sampler_update(L.ALD_RENOISE, FAKE, None, None, FAKE, 10, 64, 10, None, FAKE, None, None,
                               None) == L.ALD_E_INVALID
+    # latent kernels index vectors of 4 values with 32-bit arithmetic
+    big = 1 << 27  # 2^27 tokens x 64 channels = 2^31 vectors of 4
+    assert lib.cfg_merge(FAKE, big, 64, big, None, FAKE, FAKE, None) == L.ALD_E_UNSUPPORTED
+    assert lib.sampler_update(L.ALD_EULER, FAKE, FAKE, None, None, big, 64, big, None, FAKE, FAKE, None,
+                              None) == L.ALD_E_UNSUPPORTED
 
 
 def _cfg(**kw):
