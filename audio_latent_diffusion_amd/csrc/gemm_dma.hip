@@ -42,6 +42,14 @@
 // matrix rate needs ~94 B/clk of it (reads 64, copies 32), so LDS, not HBM,
 // bounds the main loop; a single CU's DMA copies stream ~66 B/clk from L2.
 //
+// A persistent variant (one workgroup per CU walking its tiles, the next
+// tile's first stages in flight during the epilogue, stores straight from the
+// accumulators) measured 10-25% slower: in the MFMA layout a store
+// instruction covers 16 contiguous bytes of each of 32 rows, four times the
+// memory requests of the 128-byte rows the LDS-staged epilogue writes, and at
+// 256 x 256 the staging area and a prefetched stage do not fit in LDS
+// together.
+//
 // Operand roles are swapped in the MFMA (W fragment first): accumulator
 // register r of lane l then holds output row l % 32 and column
 // 8 (r / 4) + 4 (l / 32) + r % 4 of its 32x32 block.  The epilogue stages the
@@ -135,69 +143,74 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // The copies of one stage, dealt round-robin to the waves: X blocks, then W
-// blocks, then (Q4) scale copies.  Each lane keeps its source at K stage 0
-// and the source step per stage.
+// blocks, then (Q4) scale copies.  Each lane keeps a 32-bit byte offset of
+// its source at K stage 0 from the operand's base pointer (uniform, so the
+// copy can address as scalar base + vector offset); sources advance by a
+// fixed step per stage.
 template <class C>
 struct Loader {
-  const uint8_t* src[C::LOADS];
-  int step[C::LOADS];  // source bytes per stage
-  int dst[C::LOADS];   // LDS byte offset within a stage
-  int wave;
+  uint32_t off[C::LOADS];
 
-  __device__ void init(const GemmArgs& g, int m0, int n0, int wave_, int lane) {
+  // kind of copy i of a wave: 0 = X, 1 = W, 2 = Q4 scales (uniform)
+  __device__ __forceinline__ static int kind(int wave, int i) {
+    const int b = wave + C::WAVES * i;
+    return b < C::BX ? 0 : (b < C::BX + C::BW ? 1 : 2);
+  }
+  __device__ __forceinline__ static int step(int k) { return k == 0 ? KB : (C::Q4 ? (k == 1 ? 32 : 4) : KB); }
+  __device__ __forceinline__ static int dst(int b) {
+    return b < C::BX + C::BW ? b * BLK : C::S_OFF + (b - C::BX - C::BW) * 256;
+  }
+
+  __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0, int wave, int lane) {
     constexpr int EB = C::INT ? 1 : 2;  // bytes per X (and int8 / fp16 W) element
-    const uint8_t* X = static_cast<const uint8_t*>(g.A);
-    const uint8_t* W = static_cast<const uint8_t*>(g.B);
-    const int64_t ldx = (int64_t)g.lda * EB;
-    wave = wave_;
+    const uint32_t ldx = (uint32_t)g.lda * EB;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
       const int b = wave + C::WAVES * i;  // copy index within the stage
       if (b < C::BX) {  // X: lane l fetches row l / 8 of the block, swizzled chunk
         const int tr = b * 8 + (lane >> 3);
         const int r = min(m0 + tr, g.M - 1);  // rows past the edge re-read a valid row; results dropped
-        src[i] = X + (int64_t)r * ldx + ((lane & 7) ^ swz(tr)) * 16;
-        step[i] = KB;
-        dst[i] = b * BLK;
+        off[i] = (uint32_t)r * ldx + ((lane & 7) ^ swz(tr)) * 16;
       } else if (b < C::BX + C::BW) {
         const int bw = b - C::BX;
         if constexpr (!C::Q4) {  // int8 / fp16 W: same layout as X
           const int tr = bw * 8 + (lane >> 3);
           const int r = min(n0 + tr, g.N - 1);
-          src[i] = W + (int64_t)r * ((int64_t)g.K * EB) + ((lane & 7) ^ swz(tr)) * 16;
-          step[i] = KB;
+          off[i] = (uint32_t)r * (uint32_t)(g.K * EB) + ((lane & 7) ^ swz(tr)) * 16;
         } else {  // packed W: lane l fetches group l / 32 of the stage of row l % 32
           const int tr = bw * 32 + (lane & 31);
           const int r = min(n0 + tr, g.N - 1);
-          src[i] = W + (int64_t)r * (g.K / 2) + (lane >> 5) * 16;
-          step[i] = 32;
+          off[i] = (uint32_t)r * (uint32_t)(g.K / 2) + (lane >> 5) * 16;
         }
-        dst[i] = C::W_OFF + bw * BLK;
       } else {  // Q4 scales: both fp16 group scales of a row (4 bytes); padding repeats the last copy
-        const int s = min(b - C::BX - C::BW, C::SC0 - 1);
-        const int r = min(n0 + s * 64 + lane, g.N - 1);
-        src[i] = reinterpret_cast<const uint8_t*>(g.b_scale) + (int64_t)r * (g.K / 32) * 2;
-        step[i] = 4;
-        dst[i] = C::S_OFF + (b - C::BX - C::BW) * 256;
+        const int sidx = min(b - C::BX - C::BW, C::SC0 - 1);
+        const int r = min(n0 + sidx * 64 + lane, g.N - 1);
+        off[i] = (uint32_t)r * (uint32_t)(g.K / 32) * 2;
       }
     }
   }
   // part P of PARTS of the stage's copies (spread over the K slices so the
   // wave keeps feeding MFMAs while the memory pipeline accepts its copies)
   template <int P, int PARTS>
-  __device__ __forceinline__ void issue_part(uint8_t* stage, int kt) {
+  __device__ __forceinline__ void issue_part(const uint8_t* xb, const uint8_t* wb, const uint8_t* sb, int wave,
+                                             uint8_t* stage, int kt) const {
     constexpr int lo = C::LOADS * P / PARTS, hi = C::LOADS * (P + 1) / PARTS;
 #pragma unroll
     for (int i = lo; i < hi; ++i) {
-      const void* s = static_cast<const void*>(src[i] + (int64_t)kt * step[i]);
-      lds_void* d = (lds_void*)(stage + dst[i]);
-      if (C::Q4 && wave + C::WAVES * i >= C::BX + C::BW)  // uniform over the wave
+      const int k = (C::WAVES * i < C::BX) ? 0 : kind(wave, i);  // X copies are static
+      const uint8_t* base = k == 0 ? xb : (k == 1 ? wb : sb);
+      const void* s = static_cast<const void*>(base + (off[i] + (uint32_t)(kt * step(k))));
+      lds_void* d = (lds_void*)(stage + dst(wave + C::WAVES * i));
+      if (C::Q4 && k == 2)
         __builtin_amdgcn_global_load_lds(s, d, 4, 0, 0);
       else
         __builtin_amdgcn_global_load_lds(s, d, 16, 0, 0);
     }
   }
-  __device__ __forceinline__ void issue(uint8_t* stage, int kt) { issue_part<0, 1>(stage, kt); }
+  __device__ __forceinline__ void issue(const uint8_t* xb, const uint8_t* wb, const uint8_t* sb, int wave,
+                                        uint8_t* stage, int kt) const {
+    issue_part<0, 1>(xb, wb, sb, wave, stage, kt);
+  }
 };
 
 __device__ __forceinline__ int xcd_tile(int bid, int nt) {
@@ -292,7 +305,7 @@ struct Frags {
   int qoff;        // Q4: lane's packed word in a 32-row block
   int soff;        // Q4: lane's scale pair in the stage's scale area
 
-  __device__ void init(int lane, int wn) {
+  __device__ __forceinline__ void init(int lane, int wn) {
     const int lr = lane & 31;
     const int lane_off = (lr >> 3) * BLK + (lr & 7) * KB;
     const int g_l = swz(lr);
@@ -330,6 +343,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const uint8_t* const xb = static_cast<const uint8_t*>(g.A);  // operand bases
+  const uint8_t* const wb = static_cast<const uint8_t*>(g.B);
+  const uint8_t* const sb = reinterpret_cast<const uint8_t*>(g.b_scale);
   const int nt = gridDim.x;
   int tm, tn;
   tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
@@ -369,7 +385,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   }
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) ld.issue(smem + s * C::STAGE_BYTES, s);
+    if (s < nk) ld.issue(xb, wb, sb, wave, smem + s * C::STAGE_BYTES, s);
 
   Frags<C> fr;
   fr.init(lane, wn);
@@ -390,10 +406,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (more) {
-        if (ks == 0) ld.template issue_part<0, C::KS>(snext, kn);
-        if (ks == 1) ld.template issue_part<1, C::KS>(snext, kn);
-        if (ks == 2) ld.template issue_part<2, C::KS>(snext, kn);
-        if (ks == 3) ld.template issue_part<3, C::KS>(snext, kn);
+        if (ks == 0) ld.template issue_part<0, C::KS>(xb, wb, sb, wave, snext, kn);
+        if (ks == 1) ld.template issue_part<1, C::KS>(xb, wb, sb, wave, snext, kn);
+        if (ks == 2) ld.template issue_part<2, C::KS>(xb, wb, sb, wave, snext, kn);
+        if (ks == 3) ld.template issue_part<3, C::KS>(xb, wb, sb, wave, snext, kn);
       }
       if (ks + 1 < C::KS) fr.read(stage, wm, wn, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
       mfma_slice<C>(acc, xf[ks & 1], wf[ks & 1]);
@@ -597,6 +613,9 @@ bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
   if (ldb % 16 != 0) return false;
   if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
   if (q4 && (reinterpret_cast<uintptr_t>(g.b_scale) & 3)) return false;
+  // copy sources are 32-bit byte offsets from the operand base pointers
+  const int64_t wbytes = (int64_t)g.N * (q4 ? g.K / 2 : kb);
+  if ((int64_t)g.M * ldb >= ((int64_t)1 << 32) || wbytes >= ((int64_t)1 << 32)) return false;
   return g.M > 0 && g.N > 0;
 }
 
