@@ -19,6 +19,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libald.so")
 SOURCES = ["quant.hip", "gemm.hip", "gemm_dma.hip", "attention.hip", "elementwise.hip", "abi.cpp"]
 ARCH = "gfx950"
+# per-file code-generation options: attention keeps its MFMA accumulators in
+# ordinary VGPRs (the online-softmax rescale multiplies them on the VALU every
+# tile; in AGPRs each tile would copy them out and back)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -36,7 +40,7 @@ def flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

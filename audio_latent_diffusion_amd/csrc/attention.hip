@@ -2,40 +2,67 @@
 // softmax, on v_mfma_f32_16x16x32_f16.  Dense and packed varlen sequences.
 //
 // Workgroup = 4 waves; wave w owns 16 * QW queries of one (sequence, head).
-// Keys/values stream through LDS in tiles of 64 (two stages: tile t+1 is
-// fetched from HBM while tile t is consumed).
+// Keys and values stream through LDS in tiles of 64 rows, copied straight
+// from global memory by global_load_lds_dwordx4 (each instruction fills 8 rows
+// x 128 bytes; a lane picks which 16-byte chunk of its row it fetches, which
+// gives the swizzles below), in a ring of three stages: tiles t + 1 and t + 2
+// are in flight while tile t is consumed.
 //
 // Scores are computed transposed, S^T = K Q^T: the K fragment is the MFMA row
 // operand (lane l: key l % 16, 8 dims at 8 (l / 16)), Q stays in registers as
 // the column operand.  The accumulator of lane l then holds query l % 16 and
-// keys 4 (l / 16) + r, which is exactly the column-operand layout the second
-// product O^T = V^T P^T needs (the pairing of k-positions between the two
-// operands is free as long as both use the same one), so P never leaves the
-// registers.  V is stored transposed in LDS with the matching key order, so
-// each V^T fragment is one 16-byte LDS read.  Row statistics reduce over the
-// 4 lanes that share a query (xor 16, xor 32).
+// keys 4 (l / 16) + r of each 16-key block, which is the column-operand
+// layout the second product O^T = V^T P^T needs once the 8 K positions of a
+// lane are taken as keys 32 c + 4 (l / 16) + {0..3} and 32 c + 16 + 4 (l / 16)
+// + {0..3} (any pairing of K positions is exact as long as both operands use
+// it), so P never leaves the registers.
+//
+// V stays row-major in LDS ([key][dim], as loaded) and each V^T fragment is
+// two LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane group, slot
+// k of lane j receives element j % 4 of the 8 bytes addressed by lane
+// 4 k + j / 4, so lanes 4 k + q point at key k, dims 4 q .. 4 q + 3 and lane j
+// gets dim j of four consecutive keys.
+//
+// LDS swizzles (16-byte chunk c of row r stored at slot c ^ f(r)):
+//   K: f(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows of one fragment read,
+//      same chunk, fall on distinct banks per 8-lane phase;
+//   V: f(r) = 2 (r & 3): the four keys of one transpose read land in four
+//      different 32-byte bank groups.
+//
+// Softmax: scores stay in raw units (the scale c > 0 commutes with max);
+// p = 2^(c s - c m) is one FMA and one v_exp_f32 against a reference m that
+// moves only when a row maximum passes it by more than a factor 2^8 (so
+// p < 256, and the output rescale is rare).  Row statistics reduce over the 4
+// lanes that share a query (xor 16, xor 32).
 #include "common.h"
 #include "kernels.h"
 
 namespace ald {
 
-constexpr int KT = 64;          // keys per tile
-constexpr int HD = 64;          // head dim
-constexpr int SROW = 72;        // LDS row stride in halves (144 bytes)
+constexpr int KT = 64;                   // keys per tile
+constexpr int HD = 64;                   // head dim
+constexpr int TILE_BYTES = KT * HD * 2;  // one K or V tile (8 KB)
+constexpr int ASTAGES = 3;
 
-// position of key kv (within a 64-key tile) in the transposed V row
-__device__ __forceinline__ int vperm(int kv) {
-  int kc = kv >> 5, kl = kv & 31;
-  int hh = kl >> 4, g = (kl & 15) >> 2, r = kl & 3;
-  return kc * 32 + g * 8 + hh * 4 + r;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+// s_waitcnt vmcnt(N)
+template <int N>
+__device__ __forceinline__ void attn_vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int QW>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][KT * SROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * SROW];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // ASTAGES x (K tile, V tile)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z, h = blockIdx.y;
   const int q_begin = a.cu_q ? a.cu_q[b] : b * a.Sq;
   const int q_len = a.cu_q ? a.cu_q[b + 1] - q_begin : a.Sq;
@@ -85,67 +112,107 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     for (int d = 0; d < 4; ++d) oacc[qb][d] = v4f{0, 0, 0, 0};
   }
 
-  // staging registers: K as 2 x 16 B chunks, V as 4 keys x 4 dims
-  v4i kreg[2];
-  uint64_t vreg[4];
   const int n_tiles = (k_len + KT - 1) / KT;
-
-  auto load_tile = [&](int t) {
-    const int kbase = t * KT;
+  // Tile copies: wave w fills rows 16 w .. 16 w + 15 of the K tile (two
+  // instructions) and of the V tile (two more); lane l of instruction i
+  // covers row 16 w + 8 i + l / 8, slot l % 8.
+  // Each lane's two rows (r0, r0 + 8) and chunks are fixed; a tile adds
+  // t * 64 rows.  Only the last tile clamps rows past the end (they repeat a
+  // valid key; their scores are masked).
+  const int slot = lane & 7;
+  const int r0 = wave * 16 + (lane >> 3);
+  const int64_t rstep = (int64_t)KT * a.kv_stride;
+  const uint16_t* ksrc[2];
+  const uint16_t* vsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = r0 + 8 * i;
+    const int64_t ro = (int64_t)(k_begin + r) * a.kv_stride + h * HD;
+    ksrc[i] = a.k + ro + 8 * (slot ^ kswz(r));
+    vsrc[i] = a.v + ro + 8 * (slot ^ vswz(r));
+  }
+  auto issue_tile = [&](int t, int s) {
+    uint8_t* base = smem + s * 2 * TILE_BYTES + (wave * 16) * 128;
+    const bool whole = (t + 1) * KT <= k_len;  // uniform
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      int kv = kbase + row;
-      kreg[i] = kv < k_len ? ld16(a.k + (int64_t)(k_begin + kv) * a.kv_stride + h * HD + col) : v4i{0, 0, 0, 0};
-    }
-    const int kvg = tid >> 4, dg = tid & 15;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int kv = kbase + kvg * 4 + r;
-      vreg[r] = kv < k_len ? *reinterpret_cast<const uint64_t*>(a.v + (int64_t)(k_begin + kv) * a.kv_stride + h * HD + dg * 4)
-                           : 0ull;
-    }
-  };
-  auto store_tile = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<v4i*>(&sK[s][row * SROW + col]) = kreg[i];
-    }
-    const int kvg = tid >> 4, dg = tid & 15;
-    const int p0 = vperm(kvg * 4);
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      // gather dim dd of the 4 keys into one 8-byte word
-      uint64_t w = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w |= ((vreg[r] >> (16 * dd)) & 0xFFFFull) << (16 * r);
-      *reinterpret_cast<uint64_t*>(&sV[s][(dg * 4 + dd) * SROW + p0]) = w;
+      int64_t off = (int64_t)t * rstep;
+      if (!whole) {
+        const int r = r0 + 8 * i;
+        off = (int64_t)(min(t * KT + r, k_len - 1) - r) * a.kv_stride;
+      }
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ksrc[i] + off), (lds_void_t*)(base + i * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vsrc[i] + off),
+                                       (lds_void_t*)(base + TILE_BYTES + i * 1024), 16, 0, 0);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  attn_vm_wait<0>();  // Q fragments in registers before any tile copy is in flight
+  issue_tile(0, 0);
+  if (n_tiles > 1) issue_tile(1, 1);
 
-  int s = 0;
+  // K fragment of lane (ql, g): row kb * 16 + ql, chunk 4 c + g (dims 32 c + 8 g)
+  int koff[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) koff[c] = ql * 128 + (((4 * c + g) ^ kswz(ql)) << 4);
+  // V^T transpose reads: lane j = 4 tk + tq of group g points at key
+  // 32 c + 16 h2 + 4 g + tk, dims 16 db + 4 tq .. + 3
+  const int tk = ql >> 2, tq = ql & 3;
+  int voff[2][2][4];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int r = 32 * c + 16 * h2 + 4 * g + tk;
+        const int chunk = 2 * db + (tq >> 1);
+        voff[c][h2][db] = r * 128 + ((chunk ^ vswz(r)) << 4) + 8 * (tq & 1);
+      }
+
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    // this wave's copies of tile t have landed (4 per tile; tile t + 1's are newer)
+    if (t + 1 < n_tiles) attn_vm_wait<4>();
+    else attn_vm_wait<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's copies visible; tile t - 1 fully consumed
+    if (t + 2 < n_tiles) issue_tile(t + 2, (t + 2) % ASTAGES);
+    const uint8_t* sK = smem + (t % ASTAGES) * 2 * TILE_BYTES;
+    const uint8_t* sV = sK + TILE_BYTES;
     const int kbase = t * KT;
-    // K fragments (row operand): key kb * 16 + ql, dims 32 c + 8 g
+
     v8h kf[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
+      for (int c = 0; c < 2; ++c) kf[kb][c] = *reinterpret_cast<const v8h*>(sK + kb * 16 * 128 + koff[c]);
+    // V^T fragments: 16 transpose reads.  They are issued as inline assembly
+    // because the compiler, seeing an LDS read it cannot relate to the
+    // direct-to-LDS copies, would wait for every copy in flight (the
+    // prefetched tiles too); tile t's copies are already complete here.  One
+    // lgkmcnt(0) tied to all results makes them available.
+    const uint32_t vbase = (uint32_t)(uintptr_t)((lds_u8*)smem + (sV - smem));
+    v2i vr[4][2][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
       for (int c = 0; c < 2; ++c)
-        kf[kb][c] = *reinterpret_cast<const v8h*>(&sK[s][(kb * 16 + ql) * SROW + 32 * c + 8 * g]);
-    // V^T fragments (row operand): dim db * 16 + ql, permuted keys 32 kc + 8 g
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[db][c][h2]) : "v"(vbase + voff[c][h2][db]) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(vr[0][0][0]), "+v"(vr[0][0][1]), "+v"(vr[0][1][0]), "+v"(vr[0][1][1]), "+v"(vr[1][0][0]),
+                   "+v"(vr[1][0][1]), "+v"(vr[1][1][0]), "+v"(vr[1][1][1]), "+v"(vr[2][0][0]), "+v"(vr[2][0][1]),
+                   "+v"(vr[2][1][0]), "+v"(vr[2][1][1]), "+v"(vr[3][0][0]), "+v"(vr[3][0][1]), "+v"(vr[3][1][0]),
+                   "+v"(vr[3][1][1])
+                 :
+                 : "memory");
     v8h vf[4][2];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-        vf[db][kc] = *reinterpret_cast<const v8h*>(&sV[s][(db * 16 + ql) * SROW + 32 * kc + 8 * g]);
+      for (int c = 0; c < 2; ++c)
+        vf[db][c] = __builtin_bit_cast(v8h, v4i{vr[db][c][0][0], vr[db][c][0][1], vr[db][c][1][0], vr[db][c][1][1]});
 
     // scores of a full tile need no key mask; only the last tile can be partial
     const bool full = kbase + KT <= k_len;
@@ -166,8 +233,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           for (int r = 0; r < 4; ++r)
             if (kbase + kb * 16 + g * 4 + r >= k_len) sc[kb][r] = -INFINITY;
       }
-      // running maximum of the raw scores (the softmax scale c > 0 commutes
-      // with max), then p = 2^(c s - c m) with one fused multiply-add
       float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -175,10 +240,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_old = m_run[qb];
-      const float m_new = fmaxf(m_old, mx);
-      m_run[qb] = m_new;
+      // The exponent reference m_run moves only when a row's maximum exceeds
+      // it by more than 8 / c (a factor 2^8): p then stays below 256, exact
+      // enough in fp16, and the output/sum rescale (which moves the
+      // accumulators through the VALU) is rare after the first tile.
       const float c = a.scale_log2;
+      const float m_old = m_run[qb];
+      const bool move = mx > m_old + 8.0f / c;
+      const float m_new = move ? mx : m_old;
+      if (__any(move)) {
+        const float corr = __builtin_amdgcn_exp2f(c * (m_old - m_new));  // 1 where the row did not move
+        l_run[qb] *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[qb][db] *= corr;
+        m_run[qb] = m_new;
+      }
       const float cm = -c * m_new;
       float psum = 0.0f;
       v8h pf[2];
@@ -190,16 +266,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           psum += p;
           pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)p;
         }
-      // the output and the row sum are rescaled only when some row's maximum
-      // moved (a factor of exactly 1 otherwise, so skipping is exact)
-      if (__any(m_new != m_old)) {
-        const float corr = __builtin_amdgcn_exp2f(c * (m_old - m_new));
-        l_run[qb] = l_run[qb] * corr + psum;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[qb][db] *= corr;
-      } else {
-        l_run[qb] += psum;
-      }
+      l_run[qb] += psum;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         v4f o = oacc[qb][db];
@@ -208,9 +275,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         oacc[qb][db] = o;
       }
     }
-    if (t + 1 < n_tiles) store_tile(s ^ 1);
-    __syncthreads();
-    s ^= 1;
   }
 
   // normalise and store: lane holds query ql, dims 16 db + 4 g + r
@@ -233,16 +297,18 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
+constexpr int ATTN_LDS = ASTAGES * 2 * TILE_BYTES;
+
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st) {
   if (batch <= 0 || max_sq <= 0) return;
   // two query blocks per wave when there is enough parallelism, else one
   const int64_t wgs2 = (int64_t)((max_sq + 127) / 128) * a.n_heads * batch;
   if (wgs2 >= 512) {
     dim3 grid((unsigned)((max_sq + 127) / 128), (unsigned)a.n_heads, (unsigned)batch);
-    hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), ATTN_LDS, st, a);
   } else {
     dim3 grid((unsigned)((max_sq + 63) / 64), (unsigned)a.n_heads, (unsigned)batch);
-    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), ATTN_LDS, st, a);
   }
 }
 
