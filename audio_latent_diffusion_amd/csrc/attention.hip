@@ -1,7 +1,7 @@
 // Flash-style non-causal attention, head_dim 64, fp16 in/out, fp32 online
 // softmax, on v_mfma_f32_16x16x32_f16.  Dense and packed varlen sequences.
 //
-// Workgroup = 4 waves; wave w owns 16 * QW queries of one (sequence, head).
+// Workgroup = NW waves; wave w owns 16 * QW queries of one (sequence, head).
 // Keys and values stream through LDS in tiles of 64 rows, copied straight
 // from global memory by global_load_lds_dwordx4 (each instruction fills 8 rows
 // x 128 bytes; a lane picks which 16-byte chunk of its row it fetches, which
@@ -32,8 +32,9 @@
 // Softmax: scores stay in raw units (the scale c > 0 commutes with max);
 // p = 2^(c s - c m) is one FMA and one v_exp_f32 against a reference m that
 // moves only when a row maximum passes it by more than a factor 2^8 (so
-// p < 256, and the output rescale is rare).  Row statistics reduce over the 4
-// lanes that share a query (xor 16, xor 32).
+// p < 256, and the output rescale is rare).  The row maximum reduces over the
+// 4 lanes that share a query (xor 16, xor 32); the row sum of the fp16
+// weights comes out of the MFMA against a block of ones.
 #include "common.h"
 #include "kernels.h"
 
@@ -57,8 +58,10 @@ __device__ __forceinline__ void attn_vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int QW>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+template <int QW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
+  constexpr int RPW = KT / NW;  // tile rows each wave copies
+  constexpr int CI = RPW / 8;   // copy instructions per wave and operand
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // ASTAGES x (K tile, V tile)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int q_len = a.cu_q ? a.cu_q[b + 1] - q_begin : a.Sq;
   const int k_begin = a.cu_k ? a.cu_k[b] : b * a.Sk;
   const int k_len = a.cu_k ? a.cu_k[b + 1] - k_begin : a.Sk;
-  const int QT = 64 * QW;
+  const int QT = 16 * QW * NW;
   const int tq0 = blockIdx.x * QT;
   if (tq0 >= q_len) return;  // whole workgroup exits together
 
@@ -102,40 +105,46 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
   }
 
-  v4f oacc[QW][4];
-  float m_run[QW], l_run[QW];
+  // oacc[qb][0..3]: O^T blocks of 16 dims; oacc[qb][4]: the row sums of P,
+  // accumulated by the same MFMA against a block of ones (every element of
+  // that block is the sum of the fp16 weights over the keys, for the lane's
+  // query), so the sum needs no VALU adds and no cross-lane reduction
+  v4f oacc[QW][5];
+  float m_run[QW];
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
     m_run[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) oacc[qb][d] = v4f{0, 0, 0, 0};
+    for (int d = 0; d < 5; ++d) oacc[qb][d] = v4f{0, 0, 0, 0};
   }
+  v8h ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
   const int n_tiles = (k_len + KT - 1) / KT;
-  // Tile copies: wave w fills rows 16 w .. 16 w + 15 of the K tile (two
-  // instructions) and of the V tile (two more); lane l of instruction i
-  // covers row 16 w + 8 i + l / 8, slot l % 8.
-  // Each lane's two rows (r0, r0 + 8) and chunks are fixed; a tile adds
+  // Tile copies: wave w fills rows RPW w .. RPW (w + 1) - 1 of the K tile
+  // and of the V tile (CI instructions each); lane l of instruction i covers
+  // row RPW w + 8 i + l / 8, slot l % 8.
+  // Each lane's rows (r0 + 8 i) and chunks are fixed; a tile adds
   // t * 64 rows.  Only the last tile clamps rows past the end (they repeat a
   // valid key; their scores are masked).
   const int slot = lane & 7;
-  const int r0 = wave * 16 + (lane >> 3);
+  const int r0 = wave * RPW + (lane >> 3);
   const int64_t rstep = (int64_t)KT * a.kv_stride;
-  const uint16_t* ksrc[2];
-  const uint16_t* vsrc[2];
+  const uint16_t* ksrc[CI];
+  const uint16_t* vsrc[CI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < CI; ++i) {
     const int r = r0 + 8 * i;
     const int64_t ro = (int64_t)(k_begin + r) * a.kv_stride + h * HD;
     ksrc[i] = a.k + ro + 8 * (slot ^ kswz(r));
     vsrc[i] = a.v + ro + 8 * (slot ^ vswz(r));
   }
   auto issue_tile = [&](int t, int s) {
-    uint8_t* base = smem + s * 2 * TILE_BYTES + (wave * 16) * 128;
+    uint8_t* base = smem + s * 2 * TILE_BYTES + (wave * RPW) * 128;
     const bool whole = (t + 1) * KT <= k_len;  // uniform
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < CI; ++i) {
       int64_t off = (int64_t)t * rstep;
       if (!whole) {
         const int r = r0 + 8 * i;
@@ -172,8 +181,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
 
   for (int t = 0; t < n_tiles; ++t) {
-    // this wave's copies of tile t have landed (4 per tile; tile t + 1's are newer)
-    if (t + 1 < n_tiles) attn_vm_wait<4>();
+    // this wave's copies of tile t have landed (2 CI per tile; tile t + 1's are newer)
+    if (t + 1 < n_tiles) attn_vm_wait<2 * CI>();
     else attn_vm_wait<0>();
     __builtin_amdgcn_s_barrier();  // every wave's copies visible; tile t - 1 fully consumed
     if (t + 2 < n_tiles) issue_tile(t + 2, (t + 2) % ASTAGES);
@@ -214,64 +223,64 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int c = 0; c < 2; ++c)
         vf[db][c] = __builtin_bit_cast(v8h, v4i{vr[db][c][0][0], vr[db][c][0][1], vr[db][c][1][0], vr[db][c][1][1]});
 
-    // scores of a full tile need no key mask; only the last tile can be partial
-    const bool full = kbase + KT <= k_len;
+    // scores of every query block first (independent MFMA chains the matrix
+    // core works through while the softmax of the first block runs)
+    v4f sc[QW][4];
 #pragma unroll
-    for (int qb = 0; qb < QW; ++qb) {
-      v4f sc[4];
+    for (int qb = 0; qb < QW; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         v4f z = {0, 0, 0, 0};
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][0], qf[qb][0], z, 0, 0, 0);
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kb][1], qf[qb][1], z, 0, 0, 0);
-        sc[kb] = z;
+        sc[qb][kb] = z;
       }
-      if (!full) {
+    // only the last tile can be partial: mask its keys past the end
+    if (kbase + KT > k_len) {
+#pragma unroll
+      for (int qb = 0; qb < QW; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (kbase + kb * 16 + g * 4 + r >= k_len) sc[kb][r] = -INFINITY;
-      }
-      float mx = sc[0][0];
+            if (kbase + kb * 16 + g * 4 + r >= k_len) sc[qb][kb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QW; ++qb) {
+      float mx = sc[qb][0][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // The exponent reference m_run moves only when a row's maximum exceeds
       // it by more than 8 / c (a factor 2^8): p then stays below 256, exact
-      // enough in fp16, and the output/sum rescale (which moves the
-      // accumulators through the VALU) is rare after the first tile.
+      // enough in fp16, and the output/sum rescale is rare after the first
+      // tile.
       const float c = a.scale_log2;
       const float m_old = m_run[qb];
       const bool move = mx > m_old + 8.0f / c;
       const float m_new = move ? mx : m_old;
       if (__any(move)) {
         const float corr = __builtin_amdgcn_exp2f(c * (m_old - m_new));  // 1 where the row did not move
-        l_run[qb] *= corr;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[qb][db] *= corr;
+        for (int db = 0; db < 5; ++db) oacc[qb][db] *= corr;
         m_run[qb] = m_new;
       }
       const float cm = -c * m_new;
-      float psum = 0.0f;
       v8h pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c, cm));
-          psum += p;
-          pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)p;
-        }
-      l_run[qb] += psum;
+        for (int r = 0; r < 4; ++r)
+          pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[qb][kb][r], c, cm));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 5; ++db) {
+        const v8h* vv = db < 4 ? vf[db] : nullptr;
         v4f o = oacc[qb][db];
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db][0], pf[0], o, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[db][1], pf[1], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(db < 4 ? vv[0] : ones, pf[0], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(db < 4 ? vv[1] : ones, pf[1], o, 0, 0, 0);
         oacc[qb][db] = o;
       }
     }
@@ -280,10 +289,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // normalise and store: lane holds query ql, dims 16 db + 4 g + r
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
-    float l = l_run[qb];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / oacc[qb][4][0];
     const int qi = wq0 + qb * 16 + ql;
     if (qi >= q_len) continue;
     uint16_t* o = a.out + (int64_t)(q_begin + qi) * a.o_stride + h * HD;
@@ -305,10 +311,10 @@ void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st) {
   const int64_t wgs2 = (int64_t)((max_sq + 127) / 128) * a.n_heads * batch;
   if (wgs2 >= 512) {
     dim3 grid((unsigned)((max_sq + 127) / 128), (unsigned)a.n_heads, (unsigned)batch);
-    hipLaunchKernelGGL(attn_kernel<2>, grid, dim3(256), ATTN_LDS, st, a);
+    hipLaunchKernelGGL((attn_kernel<2, 4>), grid, dim3(256), ATTN_LDS, st, a);
   } else {
     dim3 grid((unsigned)((max_sq + 63) / 64), (unsigned)a.n_heads, (unsigned)batch);
-    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(256), ATTN_LDS, st, a);
+    hipLaunchKernelGGL((attn_kernel<1, 4>), grid, dim3(256), ATTN_LDS, st, a);
   }
 }
 
