@@ -33,8 +33,8 @@
 // p = 2^(c s - c m) is one FMA and one v_exp_f32 against a reference m that
 // moves only when a row maximum passes it by more than a factor 2^8 (so
 // p < 256, and the output rescale is rare).  The row maximum reduces over the
-// 4 lanes that share a query (xor 16, xor 32); the row sum of the fp16
-// weights comes out of the MFMA against a block of ones.
+// 4 lanes that share a query with two lane-swap instructions; the row sum of
+// the fp16 weights comes out of the MFMA against a block of ones.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,6 +50,19 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+// maximum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's keys):
+// v_permlane16_swap / v_permlane32_swap with both operands v leave v of the
+// partner lane (xor 16, resp. xor 32) in one of the two results, the lane's
+// own value in the other
+__device__ __forceinline__ float max_over_query_lanes(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  v = fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
 
 // s_waitcnt vmcnt(N)
 template <int N>
@@ -252,8 +265,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_over_query_lanes(mx);
       // The exponent reference m_run moves only when a row's maximum exceeds
       // it by more than 8 / c (a factor 2^8): p then stays below 256, exact
       // enough in fp16, and the output/sum rescale is rare after the first
