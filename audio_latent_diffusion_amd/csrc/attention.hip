@@ -72,7 +72,7 @@ __device__ __forceinline__ void attn_vm_wait() {
 }
 
 template <int QW, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
   constexpr int RPW = KT / NW;  // tile rows each wave copies
   constexpr int CI = RPW / 8;   // copy instructions per wave and operand
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];  // ASTAGES x (K tile, V tile)
@@ -179,19 +179,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) koff[c] = ql * 128 + (((4 * c + g) ^ kswz(ql)) << 4);
   // V^T transpose reads: lane j = 4 tk + tq of group g points at key
-  // 32 c + 16 h2 + 4 g + tk, dims 16 db + 4 tq .. + 3
+  // 32 c + 16 h2 + 4 g + tk, dims 16 db + 4 tq .. + 3.  With the V swizzle
+  // (chunk ^ 2 (row & 3), row & 3 = tk) the byte offset is
+  //   4096 c + 2048 h2 + (4 g + tk) 128 + 32 (db ^ tk) + 16 (tq >> 1) + 8 (tq & 1),
+  // a per-lane part for each db plus an immediate for (c, h2).
   const int tk = ql >> 2, tq = ql & 3;
-  int voff[2][2][4];
+  int vlane[4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int r = 32 * c + 16 * h2 + 4 * g + tk;
-        const int chunk = 2 * db + (tq >> 1);
-        voff[c][h2][db] = r * 128 + ((chunk ^ vswz(r)) << 4) + 8 * (tq & 1);
-      }
+  for (int db = 0; db < 4; ++db) vlane[db] = (4 * g + tk) * 128 + 32 * (db ^ tk) + 16 * (tq >> 1) + 8 * (tq & 1);
 
   for (int t = 0; t < n_tiles; ++t) {
     // this wave's copies of tile t have landed (2 CI per tile; tile t + 1's are newer)
@@ -216,12 +211,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a) {
     const uint32_t vbase = (uint32_t)(uintptr_t)((lds_u8*)smem + (sV - smem));
     v2i vr[4][2][2];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[db][c][h2]) : "v"(vbase + voff[c][h2][db]) : "memory");
+    for (int db = 0; db < 4; ++db) {
+      const uint32_t va = vbase + vlane[db];
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[db][0][0]) : "v"(va) : "memory");
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(vr[db][0][1]) : "v"(va) : "memory");
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:4096" : "=v"(vr[db][1][0]) : "v"(va) : "memory");
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:6144" : "=v"(vr[db][1][1]) : "v"(va) : "memory");
+    }
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(vr[0][0][0]), "+v"(vr[0][0][1]), "+v"(vr[0][1][0]), "+v"(vr[0][1][1]), "+v"(vr[1][0][0]),
                    "+v"(vr[1][0][1]), "+v"(vr[1][1][0]), "+v"(vr[1][1][1]), "+v"(vr[2][0][0]), "+v"(vr[2][0][1]),
