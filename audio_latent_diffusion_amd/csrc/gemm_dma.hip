@@ -39,8 +39,11 @@
 //
 // Measured limits on MI355X that shape this: LDS serves ~128 B/clk per CU,
 // shared by the DMA writes and the fragment reads; a 256 x 256 tile at full
-// matrix rate needs ~94 B/clk of it (reads 64, copies 32), so LDS, not HBM,
+// matrix rate needs ~94 B/clk of it with 4 waves of 128 x 128 (reads 64,
+// copies 32) and ~128 B/clk with 8 waves of 128 x 64, so LDS, not HBM,
 // bounds the main loop; a single CU's DMA copies stream ~66 B/clk from L2.
+// The 256 x 256 tile still runs 8 waves (two per SIMD): the second wave
+// covers the first one's stalls and measured faster on every serving shape.
 //
 // A persistent variant (one workgroup per CU walking its tiles, the next
 // tile's first stages in flight during the epilogue, stores straight from the
@@ -77,11 +80,11 @@ constexpr int KB = 128;    // X bytes per stage and row (one cache line)
 enum { M_I8 = 0, M_F16 = 1, M_Q4 = 2 };                              // operand modes
 enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };  // epilogue kinds
 
-template <int BM_, int BN_, int STAGES_, int MODE_>
+template <int BM_, int BN_, int STAGES_, int MODE_, int WGN_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, MODE = MODE_;
   static constexpr bool INT = MODE == M_I8, Q4 = MODE == M_Q4;
-  static constexpr int WGM = 2, WGN = 2, WAVES = 4, THREADS = 256;
+  static constexpr int WGM = 2, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int KS = 4;                      // 32-byte X slices per stage
@@ -96,7 +99,7 @@ struct Cfg {
   static constexpr int STAGE_BYTES = S_OFF + SCL * 256;
   static constexpr int LDS = STAGES * STAGE_BYTES;
   // epilogue staging: PW columns per pass, rows padded by 4 words
-  static constexpr int PW = WN < 64 ? WN : 64;
+  static constexpr int PW = WN < 64 ? WN : (WAVES > 4 ? 32 : 64);
   static constexpr int RS = PW + 4;
   static constexpr int EPI_LDS = WAVES * WM * (RS + 1) * 4;
   // per-row and per-column epilogue scalars (x_scale[BM], w_scale[BN], bias[BN])
@@ -561,11 +564,16 @@ void prep_cfg() {
   for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
 }
 
-// tile configurations per mode (BM, BN, stages): a Q4 stage is smaller, so
-// its 256 x 256 tile keeps three stages in flight
+// tile configurations per mode (BM, BN, stages, waves along N): the 256 x 256
+// tile runs 8 waves, two per SIMD, 128 x 64 each (one wave per SIMD with
+// 128 x 128 each reads less from LDS but measured 4-13% slower on every
+// serving shape: the second wave covers the first one's LDS and copy-issue
+// stalls, the prologue and the epilogue, and overlaps the 4-bit
+// dequantization with the MFMAs); a Q4 stage is smaller, so its 256 x 256
+// tile keeps three stages in flight
 template <int MODE>
 struct Tiles {
-  using T256 = Cfg<256, 256, MODE == M_Q4 ? 3 : 2, MODE>;
+  using T256 = Cfg<256, 256, MODE == M_Q4 ? 3 : 2, MODE, 4>;
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 5, MODE>;
   using T64 = Cfg<64, 64, 8, MODE>;
