@@ -150,8 +150,10 @@ def kernel_rooflines():
     out = {}
 
     # attention: self-attention of the serving batch (16 rows x 512 tokens,
-    # 24 heads) and of the 4-bit model (8 rows x 1024 tokens, 32 heads)
-    for name, (Bn, S, nh) in {"attn_serve": (16, 512, 24), "attn_q4": (8, 1024, 32)}.items():
+    # 24 heads), of the 4-bit model (8 rows x 1024 tokens, 32 heads) and of a
+    # long-form clip on the mid-size model (a CFG pair of 8192 tokens, 16 heads)
+    for name, (Bn, S, nh) in {"attn_serve": (16, 512, 24), "attn_q4": (8, 1024, 32),
+                              "attn_long": (2, 8192, 16)}.items():
         qkv = torch.randn((Bn * S, 3 * nh * 64), dtype=torch.float16, device="cuda", generator=g)
         o = torch.empty((Bn * S, nh * 64), dtype=torch.float16, device="cuda")
         q, k, v = qkv[:, :nh * 64], qkv[:, nh * 64:2 * nh * 64], qkv[:, 2 * nh * 64:]
