@@ -51,6 +51,7 @@ class DiTConfig:
     wmode: str          # "w8a8" | "f16" | "q4"
     seed: int
     ln_eps: float = 1e-5
+    steer_mode: str = "add"  # "add" (alpha, residual-norm units) | "project" (beta)
 
     @property
     def head_dim(self) -> int:

@@ -18,6 +18,7 @@ ALD_ACT_NONE, ALD_ACT_GELU = 0, 1
 ALD_PREQUANT = 1
 ALD_EULER, ALD_RENOISE = 0, 1
 ALD_STEER_ADD, ALD_STEER_PROJECT = 0, 1
+STEER_MODES = {"add": ALD_STEER_ADD, "project": ALD_STEER_PROJECT}
 
 WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4}
 
@@ -39,7 +40,7 @@ class AldError(RuntimeError):
 class dit_config(ctypes.Structure):
     _fields_ = [("n_blocks", c_int), ("hidden", c_int), ("n_heads", c_int), ("head_dim", c_int),
                 ("mlp", c_int), ("channels", c_int), ("text_tokens", c_int), ("text_dim", c_int),
-                ("wmode", c_int), ("steer_block", c_int), ("ln_eps", c_float)]
+                ("wmode", c_int), ("steer_block", c_int), ("ln_eps", c_float), ("steer_mode", c_int)]
 
 
 class dit_linear(ctypes.Structure):

@@ -107,6 +107,7 @@ int check_config(const dit_config* c) {
   CHECK(c->hidden <= 8192 && c->mlp <= 8192 && c->text_dim <= 8192, ALD_E_UNSUPPORTED);
   CHECK(c->hidden % 2 == 0, ALD_E_UNSUPPORTED);
   CHECK(c->steer_block >= -1 && c->steer_block < c->n_blocks, ALD_E_INVALID);
+  CHECK(c->steer_mode == ALD_STEER_ADD || c->steer_mode == ALD_STEER_PROJECT, ALD_E_INVALID);
   CHECK(c->ln_eps >= 0.0f, ALD_E_INVALID);
   return ALD_OK;
 }
@@ -258,7 +259,7 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     run_linear(bw.down, wm, in.A, in.lda, in.xs, M, F, H, b.h, H, 0, b.h, H, st);
     if (l == c->steer_block) {
       if (a->block_norms) launch_row_norms(b.h, H, M, H, a->block_norms, st);
-      launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, st);
+      launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, c->steer_mode == ALD_STEER_PROJECT, st);
     }
   }
 
@@ -467,13 +468,12 @@ int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R, c
               const float* alpha, float resid_norm, const float* dir, int mode, hipStream_t stream) {
   CHECK(M >= 0 && H > 0, ALD_E_INVALID);
   CHECK(mode == ALD_STEER_ADD || mode == ALD_STEER_PROJECT, ALD_E_INVALID);
-  CHECK(mode == ALD_STEER_ADD, ALD_E_UNSUPPORTED);
   if (M == 0) return ALD_OK;
   CHECK(h && alpha && dir && al16(h) && al16(dir), ALD_E_INVALID);
   CHECK(H % 8 == 0 && ldh >= H && ldh % 8 == 0, ALD_E_INVALID);
   if (!row_req) CHECK(rows_per_req > 0 && R > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, row_req ? 1 : R, row_req};
-  launch_steer(h, ldh, M, H, map, alpha, resid_norm, dir, stream);
+  launch_steer(h, ldh, M, H, map, alpha, resid_norm, dir, mode == ALD_STEER_PROJECT, stream);
   return launched();
 }
 

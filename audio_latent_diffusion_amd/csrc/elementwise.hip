@@ -20,8 +20,11 @@ __device__ __forceinline__ int req_of(const RowMap& m, uint32_t row) {
   return m.row_req ? m.row_req[i] : (int)((i / (uint32_t)m.rows_per_req) % (uint32_t)m.R);
 }
 
-// h[m, :] += (alpha[r] * resid_norm) * dir  -- rows with alpha == 0 untouched
-template <int NV>
+// Steering of the rows of h whose request strength a = alpha[r] is nonzero
+// (rows with a == 0 are not touched at all):
+//   add      : h[m, :] += (a * resid_norm) * dir
+//   project  : h[m, :] += (a * (h[m, :] . dir)) * dir   (fp32 dot product)
+template <int NV, bool PROJ>
 __global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, int64_t ldh, int M, int H, RowMap map,
                                                     const float* __restrict__ alpha, float resid_norm,
                                                     const float* __restrict__ dir) {
@@ -38,18 +41,31 @@ __global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, in
       const float4 d1 = *reinterpret_cast<const float4*>(dir + e + 4);
       dv[j][0] = d0.x; dv[j][1] = d0.y; dv[j][2] = d0.z; dv[j][3] = d0.w;
       dv[j][4] = d1.x; dv[j][5] = d1.y; dv[j][6] = d1.z; dv[j][7] = d1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dv[j][i] = 0.0f;
     }
   }
   for (; m < M; m += stride) {
     const float a = alpha[req_of(map, (uint32_t)m)];
     if (a == 0.0f) continue;  // exact no-op: no write at all (uniform over the wave)
-    const float coef = a * resid_norm;
     uint16_t* row = h + (int64_t)m * ldh;
     v4i raw[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = (lane + WAVE * j) * 8;
-      if (e < H) raw[j] = ld16_nt(row + e);
+      raw[j] = e < H ? ld16_nt(row + e) : v4i{0, 0, 0, 0};
+    }
+    float coef = a * resid_norm;
+    if constexpr (PROJ) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint16_t* hv = reinterpret_cast<const uint16_t*>(&raw[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dot = fmaf(h2f(hv[i]), dv[j][i], dot);
+      }
+      coef = a * wave_sum(dot);
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -309,17 +325,24 @@ void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* 
 static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 static inline dim3 grid_lat(int64_t n_tok, int C) { return grid_for(n_tok * (C / 4)); }
 
-void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
-                  const float* dir, hipStream_t st) {
-  if (M <= 0 || H <= 0) return;
+template <bool PROJ>
+static void launch_steer_mode(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha,
+                              float resid_norm, const float* dir, hipStream_t st) {
   dim3 grid((unsigned)std::min<int64_t>((M + 3) / 4, 2048)), block(256);
   const int nv = (H + 511) / 512;
-  if (nv <= 1) hipLaunchKernelGGL(steer_kernel<1>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 2) hipLaunchKernelGGL(steer_kernel<2>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 3) hipLaunchKernelGGL(steer_kernel<3>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 4) hipLaunchKernelGGL(steer_kernel<4>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 8) hipLaunchKernelGGL(steer_kernel<8>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else hipLaunchKernelGGL(steer_kernel<16>, grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  if (nv <= 1) hipLaunchKernelGGL((steer_kernel<1, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 2) hipLaunchKernelGGL((steer_kernel<2, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 3) hipLaunchKernelGGL((steer_kernel<3, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 4) hipLaunchKernelGGL((steer_kernel<4, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else if (nv <= 8) hipLaunchKernelGGL((steer_kernel<8, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+  else hipLaunchKernelGGL((steer_kernel<16, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+}
+
+void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
+                  const float* dir, int project, hipStream_t st) {
+  if (M <= 0 || H <= 0) return;
+  if (project) launch_steer_mode<true>(h, ldh, M, H, map, alpha, resid_norm, dir, st);
+  else launch_steer_mode<false>(h, ldh, M, H, map, alpha, resid_norm, dir, st);
 }
 
 void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,

@@ -68,8 +68,9 @@ void gemm_dma_prepare();
 
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st);
 
+// project = 0: h += (alpha resid_norm) dir; project = 1: h += (alpha (h . dir)) dir
 void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
-                  const float* dir, hipStream_t st);
+                  const float* dir, int project, hipStream_t st);
 void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,
                       hipStream_t st);
 void launch_euler(float* x, const float* v_hat, int64_t n_tok, int C, RowMap map, const float* t_cur,

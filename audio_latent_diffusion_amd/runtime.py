@@ -70,7 +70,7 @@ class DiTModel:
         cfg = self.cfg
         self.c_cfg = L.dit_config(cfg.n_blocks, cfg.hidden, cfg.n_heads, cfg.hidden // cfg.n_heads, cfg.mlp,
                                   cfg.channels, cfg.text_tokens, cfg.text_dim, self.wmode, cfg.steer_block,
-                                  cfg.ln_eps)
+                                  cfg.ln_eps, L.STEER_MODES[cfg.steer_mode])
         arr = (L.dit_block_weights * max(1, cfg.n_blocks))()
         for i, d in enumerate(self.blocks):
             bw = arr[i]

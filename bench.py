@@ -200,6 +200,9 @@ def kernel_rooflines():
     d /= d.norm()
     ms = _timed(lambda: B.steer_add(x, alpha, 1.0, d))
     out["steer_add"] = _entry("hbm", ms, 4.0 * M * H, HBM_PEAK_GBS, "GB/s", shape=f"{M} x {H}")
+    beta = torch.full((1,), 1e-3, device="cuda")  # small: repeated amplification stays finite
+    ms = _timed(lambda: B.steer_add(x, beta, 1.0, d, mode=L.ALD_STEER_PROJECT))
+    out["steer_project"] = _entry("hbm", ms, 4.0 * M * H, HBM_PEAK_GBS, "GB/s", shape=f"{M} x {H}")
     del x, q
     Mf = M // 4
     xf = torch.randn((Mf, F), dtype=torch.float16, device="cuda", generator=g)

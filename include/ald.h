@@ -176,15 +176,18 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * Steering, CFG merge, sampler.                                           *
  * ------------------------------------------------------------------------ */
 
-/* Residual-stream steering add (aria, Section III; Chinese summary,
- * activation steering): for every row m of h [M, ldh] fp16 with request
- * r = row_req ? row_req[m] : (m / rows_per_req) % R,
- *   h[m, :] = fp16(h[m, :] + (alpha[r] * resid_norm) * dir[:])   (fp32 math)
- * alpha [R] fp32 is read on the device at execution time (a captured graph
- * picks up new values without re-capture).  Rows with alpha[r] == 0 are not
- * written at all, so the result is bit-identical to not calling.
- * dir [H] fp32 unit direction.  mode: ALD_STEER_ADD only (ALD_STEER_PROJECT
- * returns ALD_E_UNSUPPORTED).  H % 8 == 0. */
+/* Residual-stream steering (aria, Section III: the direction is added, or
+ * projected onto, at the chosen block's output; Chinese summary, activation
+ * steering, for the additive formula): for every row m of h [M, ldh] fp16
+ * with request r = row_req ? row_req[m] : (m / rows_per_req) % R and
+ * strength a = alpha[r],
+ *   ALD_STEER_ADD    : h[m, :] = fp16(h[m, :] + (a * resid_norm) * dir[:])
+ *   ALD_STEER_PROJECT: h[m, :] = fp16(h[m, :] + (a * (h[m, :] . dir)) * dir[:])
+ * (fp32 math; the projection strength carries no residual-norm unit and
+ * resid_norm is ignored).  alpha [R] fp32 is read on the device at execution
+ * time (a captured graph picks up new values without re-capture).  Rows with
+ * a == 0 are not written at all, so the result is bit-identical to not
+ * calling.  dir [H] fp32 unit direction.  H % 8 == 0. */
 int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R,
               const int32_t* row_req, const float* alpha, float resid_norm,
               const float* dir, int mode, hipStream_t stream);
@@ -231,6 +234,7 @@ typedef struct {
   int wmode;         /* ALD_W8A8 | ALD_F16 | ALD_Q4    */
   int steer_block;   /* block whose output is steered; -1: none */
   float ln_eps;
+  int steer_mode;    /* ALD_STEER_ADD | ALD_STEER_PROJECT */
 } dit_config;
 
 /* One linear layer's weights in the precision of dit_config.wmode:

@@ -279,6 +279,28 @@ def steer_add(h16, row_alpha, resid_norm, direction) -> np.ndarray:
     return h
 
 
+def steer_project(h16, row_beta, direction) -> np.ndarray:
+    """Projection steering (aria, Section III: the direction is either added
+    or projected onto; the steering ablation compares the additive strength
+    alpha with a projection strength beta).  Reading: projection
+    amplification, h <- h + beta * (h . d_hat) * d_hat, which scales the
+    component of h along d_hat by (1 + beta) and leaves the orthogonal part
+    alone; beta carries no residual-norm unit (the dot product already does).
+
+    Rows whose strength is exactly 0 are returned untouched.  Other rows: the
+    dot product and the sum in fp64, rounded once to fp16.
+    """
+    h = np.array(h16, dtype=F16, copy=True)
+    b = np.asarray(row_beta, dtype=F32)
+    rows = np.nonzero(b != 0)[0]
+    if rows.size:
+        d = np.asarray(direction, F32).astype(F64)
+        hr = h[rows].astype(F64)
+        c = b[rows].astype(F64) * (hr @ d)
+        h[rows] = (hr + c[:, None] * d[None, :]).astype(F16)
+    return h
+
+
 def cfg_merge(v_cond16, v_uncond16, w) -> np.ndarray:
     """Classifier-free-guidance merge of the vLLM audio pipeline page,
     Section 2.4, Eq. (1), applied to the velocity: w * cond + (1 - w) * uncond,
@@ -425,7 +447,10 @@ def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv:
         if li in keep_blocks:
             trace.block_out[li] = h.copy()
         if li == cfg.steer_block:
-            h = steer_add(h, row_alpha, resid_norm, direction)
+            if cfg.steer_mode == "project":
+                h = steer_project(h, row_alpha, direction)
+            else:
+                h = steer_add(h, row_alpha, resid_norm, direction)
     u = layer_norm(h, P.lnf_g, P.lnf_b, cfg.ln_eps)
     v = f16_linear(u, P.w_out, P.b_out)
     trace.v = v

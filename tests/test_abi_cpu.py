@@ -70,8 +70,6 @@ def test_attention_and_elementwise_validation():
                         None) == L.ALD_E_INVALID      # stride narrower than n_heads * 64
     assert lib.attn_fwd(None, FAKE, FAKE, 128, 128, 2, 64, 1, 8, 8, None, None, 0, 0, 0.1, FAKE, 128,
                         None) == L.ALD_E_INVALID
-    assert lib.steer_add(FAKE, 64, 4, 64, 4, 1, None, FAKE, 1.0, FAKE, L.ALD_STEER_PROJECT,
-                         None) == L.ALD_E_UNSUPPORTED
     assert lib.steer_add(FAKE, 64, 4, 64, 4, 1, None, FAKE, 1.0, FAKE, 9, None) == L.ALD_E_INVALID
     assert lib.steer_add(FAKE, 64, 4, 64, 0, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_INVALID
     assert lib.cfg_merge(FAKE, 10, 64, 0, None, FAKE, FAKE, None) == L.ALD_E_INVALID
@@ -87,7 +85,7 @@ def test_attention_and_elementwise_validation():
 
 def _cfg(**kw):
     d = dict(n_blocks=2, hidden=256, n_heads=4, head_dim=64, mlp=1024, channels=64, text_tokens=32, text_dim=256,
-             wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5)
+             wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5, steer_mode=L.ALD_STEER_ADD)
     d.update(kw)
     return L.dit_config(**d)
 
@@ -126,6 +124,8 @@ def test_step_validation():
                         None) == L.ALD_E_WORKSPACE
     bad = _cfg(head_dim=32, n_heads=8)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_UNSUPPORTED
+    bad = _cfg(steer_mode=7)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     bad = _cfg(steer_block=2)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     bad = _cfg(wmode=7)

@@ -270,6 +270,26 @@ def test_steer_add():
     assert host(ht).tobytes() == h.tobytes()
 
 
+@pytest.mark.parametrize("H", [256, 1536, 2000])
+def test_steer_project(H):
+    """Projection steering, h += beta (h . d) d, on rows of nonzero beta; rows of
+    beta = 0 untouched bit for bit (ragged H exercises the partial chunk)."""
+    r = rng(9 + H)
+    M, S, R = 4 * 96, 96, 2
+    h = r.standard_normal((M, H)).astype(np.float16)
+    d = r.standard_normal(H)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    beta = np.array([0.0, 0.75], np.float32)
+    ht = dev(h)
+    B.steer_add(ht, dev(beta), 123.0, dev(d), rows_per_req=S, R=R, mode=L.ALD_STEER_PROJECT)
+    got = host(ht)
+    row_req = (np.arange(M) // S) % R
+    ref = O.steer_project(h, beta[row_req], d)
+    f16_close(got, ref, rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    untouched = row_req == 0
+    assert got[untouched].tobytes() == h[untouched].tobytes()
+
+
 def test_cfg_merge_and_sampler():
     r = rng(9)
     R, S, C = 3, 50, 64

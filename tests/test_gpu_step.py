@@ -54,6 +54,28 @@ def test_tiny_step_parity(wmode):
     assert verr < 5e-2
 
 
+def test_tiny_step_projection_steering():
+    """Projection steering at block 1 (beta 0.5): the step against the oracle,
+    and beta = 0 bit-identical to the unsteered pass."""
+    cfg = I.TINY.replace(steer_mode="project")
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, p)
+    run = _runner(model, inp)
+    run.step(0)
+    got = host(run.x)
+    ref, _ = _oracle_steps(O.prepare_model(cfg, p), inp, [0])
+    err = O.normwise_rel_err(got, ref)
+    print(f"tiny projection steering: latent err {err:.2e}")
+    assert err < TOL
+    inp.alpha[:] = 0
+    a = _runner(model, inp)
+    a.step(0)
+    b = _runner(model.with_steer_block(-1), inp)
+    b.step(0)
+    assert host(a.x).tobytes() == host(b.x).tobytes()
+
+
 def test_alpha_zero_bit_identical(tiny):
     cfg, p, model, _ = tiny
     inp = I.make_inputs(cfg)

@@ -156,6 +156,41 @@ def test_steer_closed_form_and_linearity():
     assert np.allclose(delta[0.5], 2 * delta[0.25], atol=2.0 ** -8)
 
 
+def test_steer_project_beta_zero_and_orthogonal_rows_untouched():
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((5, 32)).astype(np.float16)
+    h[0, 1] = np.float16(-0.0)
+    d = np.zeros(32, np.float32)
+    d[3] = 1.0                                   # d_hat = e_3
+    out = O.steer_project(h, np.zeros(5, np.float32), d)
+    assert out.tobytes() == h.tobytes()          # beta = 0: bit-identical
+    h[2, 3] = 0                                  # row 2 orthogonal to d_hat
+    out = O.steer_project(h, np.full(5, 0.75, np.float32), d)
+    assert out[2].tobytes() == h[2].tobytes()    # h . d_hat = 0: nothing moves
+    # along e_3 only coordinate 3 changes, scaled by 1 + beta (one rounding)
+    rest = np.delete(np.arange(32), 3)
+    assert np.array_equal(out[:, rest], h[:, rest])
+    assert np.array_equal(out[:, 3], (h[:, 3].astype(np.float64) * 1.75).astype(np.float16))
+
+
+def test_steer_project_scales_the_component_along_the_direction():
+    rng = np.random.default_rng(7)
+    h = rng.standard_normal((4, 64)).astype(np.float16)
+    d = rng.standard_normal(64)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    d64 = d.astype(np.float64)
+    h64 = h.astype(np.float64)
+    par = h64 @ d64                               # component along d_hat
+    orth = h64 - par[:, None] * d64[None, :]
+    for beta in (-0.5, 0.5, 2.0):
+        out = O.steer_project(h, np.full(4, beta, np.float32), d).astype(np.float64)
+        assert np.allclose(out @ d64, (1 + beta) * par, atol=2e-2)
+        assert np.allclose(out - (out @ d64)[:, None] * d64[None, :], orth, atol=2.0 ** -7)
+    # beta = -1 removes the component (up to the fp16 rounding of the result)
+    out = O.steer_project(h, np.full(4, -1.0, np.float32), d).astype(np.float64)
+    assert np.all(np.abs(out @ d64) < 2e-2)
+
+
 def test_mean_row_norm():
     h = np.array([[3, 4, 0], [0, 0, 1]], np.float16)
     assert O.mean_row_norm(h) == pytest.approx(3.0)   # (5 + 1) / 2
