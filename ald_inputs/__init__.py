@@ -48,7 +48,7 @@ class DiTConfig:
     steer_block: int    # 0-based block index whose output is steered
     steer_alpha: float
     steer_steps: Tuple[int, ...]  # steps (0-based, inclusive set) with alpha != 0
-    wmode: str          # "w8a8" | "f16" | "q4"
+    wmode: str          # "w8a8" | "f16" | "q4" | "w8a16"
     seed: int
     ln_eps: float = 1e-5
     steer_mode: str = "add"  # "add" (alpha, residual-norm units) | "project" (beta)

@@ -191,6 +191,15 @@ def f16_linear(x16, w16, bias=None, residual=None, act=0) -> np.ndarray:
     return _epilogue(y64, bias, residual, act)
 
 
+def q8w_linear(x16, wq, w_scale, bias=None, residual=None, act=0) -> np.ndarray:
+    """8-bit weight-only linear (aria, Section III-A: 8-bit weight storage;
+    the activations stay fp16).  The weight is its dequantized value
+    W[n, k] = q[n, k] * s[n] in fp64; y = fp16(act(x . W^T + bias) + residual)."""
+    w64 = np.asarray(wq, np.int8).astype(F64) * np.asarray(w_scale, F32).astype(F64)[:, None]
+    y64 = np.asarray(x16, F16).astype(F64) @ w64.T
+    return _epilogue(y64, bias, residual, act)
+
+
 def q4_linear(x16, packed, scales16, bias=None, residual=None, act=0, group=32) -> np.ndarray:
     """4-bit weight-only linear: weights dequantized to fp16, then as f16_linear."""
     return f16_linear(x16, dequantize_q4(packed, scales16, group), bias, residual, act)
@@ -351,12 +360,14 @@ class PreparedLinear:
             return w8a8_linear(x16, self.wq, self.ws, self.bias, residual, act).y
         if self.mode == "q4":
             return q4_linear(x16, self.q4, self.q4s, self.bias, residual, act)
+        if self.mode == "w8a16":
+            return q8w_linear(x16, self.wq, self.ws, self.bias, residual, act)
         return f16_linear(x16, self.w16, self.bias, residual, act)
 
 
 def prepare_linear(w16, bias, mode) -> PreparedLinear:
     p = PreparedLinear(mode, np.asarray(w16, F16), np.asarray(bias, F32))
-    if mode == "w8a8":
+    if mode in ("w8a8", "w8a16"):
         p.wq, p.ws = quantize_rows_q8(p.w16)
     elif mode == "q4":
         p.q4, p.q4s = quantize_q4(p.w16)

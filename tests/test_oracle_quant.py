@@ -191,3 +191,56 @@ def test_planted_rounding_mistake_is_caught(monkeypatch):
         test_q8_hand_cases()
     monkeypatch.setattr(O, "quantize_rows_q8", real)
     test_q8_hand_cases()
+
+
+def test_q8w_brute_force_exact():
+    """8-bit weight-only linear against a plain triple loop; operands chosen so
+    every product and sum is exact in fp64 and the fp16 result is exact too,
+    with a distinct power-of-two scale per output channel (a scale applied
+    along the wrong axis, or a transposed weight, changes the result)."""
+    rng = np.random.default_rng(11)
+    M, K, N = 5, 64, 7
+    x = (rng.integers(-8, 9, size=(M, K)) / 4).astype(np.float16)
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s = (2.0 ** -rng.integers(4, 9, size=N)).astype(np.float32)
+    b = (rng.integers(-4, 5, size=N) / 8).astype(np.float32)
+    y = O.q8w_linear(x, q, s, b)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * int(q[n, k]) * Fraction(float(s[n]))
+            acc += Fraction(float(b[n]))
+            assert float(y[m, n]) == float(np.float16(float(acc))), (m, n)
+
+
+def test_q8w_error_bound_vs_unquantized_weight():
+    """With the weight's own per-channel q8 quantization, the result stays
+    within the quantizer's half-step bound of the fp16-weight product."""
+    rng = np.random.default_rng(12)
+    M, K, N = 16, 256, 48
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float16)
+    q, s = O.quantize_rows_q8(w)
+    y = O.q8w_linear(x, q, s).astype(np.float64)
+    exact = x.astype(np.float64) @ w.astype(np.float64).T
+    bound = np.abs(x.astype(np.float64)).sum(axis=1)[:, None] * s.astype(np.float64)[None, :] / 2
+    fp16_round = np.abs(exact) * 2.0 ** -11 + 2.0 ** -24
+    assert np.all(np.abs(y - exact) <= bound * 1.0001 + fp16_round * 1.01)
+    # the weight-only arm is strictly closer than W8A8, which also rounds x
+    w8 = O.w8a8_linear(x, q, s).y.astype(np.float64)
+    assert np.abs(y - exact).mean() < np.abs(w8 - exact).mean()
+
+
+def test_q8w_residual_and_gelu():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((6, 64)).astype(np.float16)
+    q = rng.integers(-127, 128, size=(10, 64)).astype(np.int8)
+    s = (0.001 * (1 + rng.random(10))).astype(np.float32)
+    res = rng.standard_normal((6, 10)).astype(np.float16)
+    lin = x.astype(np.float64) @ (q.astype(np.float64) * s.astype(np.float64)[:, None]).T
+    got = O.q8w_linear(x, q, s, residual=res).astype(np.float64)
+    assert np.allclose(got, lin + res.astype(np.float64), atol=2e-3, rtol=2e-3)
+    from math import erf, sqrt
+    ref = np.vectorize(lambda v: 0.5 * v * (1 + erf(v / sqrt(2))))(lin)
+    assert np.allclose(O.q8w_linear(x, q, s, act=1).astype(np.float64), ref, atol=1e-3, rtol=1e-3)
