@@ -13,19 +13,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libald.so")
 
 ALD_OK, ALD_E_INVALID, ALD_E_UNSUPPORTED, ALD_E_WORKSPACE, ALD_E_LAUNCH = 0, -1, -2, -3, -4
-ALD_W8A8, ALD_F16, ALD_Q4 = 0, 1, 2
+ALD_W8A8, ALD_F16, ALD_Q4, ALD_W8A16 = 0, 1, 2, 3
 ALD_ACT_NONE, ALD_ACT_GELU = 0, 1
 ALD_PREQUANT = 1
 ALD_EULER, ALD_RENOISE = 0, 1
 ALD_STEER_ADD, ALD_STEER_PROJECT = 0, 1
 STEER_MODES = {"add": ALD_STEER_ADD, "project": ALD_STEER_PROJECT}
 
-WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4}
+WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4, "w8a16": ALD_W8A16}
 
 # every extern "C" entry point of include/ald.h
 EXPORTS = (
     "ald_strerror", "ald_version", "quantize_rows_q8", "quantize_q4", "ln_quant", "ln_f16",
-    "w8a8_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "cfg_merge",
+    "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "cfg_merge",
     "sampler_update", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
     "dit_graph_launch", "dit_graph_destroy",
 )
@@ -82,6 +82,7 @@ def _declare(lib):
         "ln_f16": (I, [V, I64, I, I, V, V, F, V, I64, V]),
         "w8a8_linear": (I, [V, I64, I, I, V, V, I, V, V, I64, I, V, I64, V, V, V, c_uint, V]),
         "q4_linear": (I, [V, I64, I, I, V, V, I, V, V, I64, I, V, I64, V]),
+        "q8w_linear": (I, [V, I64, I, I, V, V, I, V, V, I64, I, V, I64, V]),
         "f16_linear": (I, [V, I64, I, I, V, I, V, V, I64, I, V, I64, V]),
         "attn_fwd": (I, [V, V, V, I64, I64, I, I, I, I, I, V, V, I, I, F, V, I64, V]),
         "steer_add": (I, [V, I64, I, I, I, I, V, V, F, V, I, V]),

@@ -92,6 +92,18 @@ def w8a8_linear(x, wq, w_scale, bias=None, residual=None, act=0, y=None, xq=None
     return y
 
 
+def q8w_linear(x, wq, w_scale, bias=None, residual=None, act=0, y=None):
+    """fp16 x times int8 weights [N, K] with fp32 per-channel scales."""
+    _dev(x, torch.float16, "x")
+    M, K = x.shape
+    N = wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.float16, device=x.device) if y is None else y
+    L.check("q8w_linear", L.lib().q8w_linear(_p(x), _ld(x), M, K, _p(wq), _p(w_scale), N, _p(bias), _p(residual),
+                                             _ld(residual) if residual is not None else 0, act, _p(y), _ld(y),
+                                             _stream()))
+    return y
+
+
 def q4_linear(x, wq4, w_scale, bias=None, residual=None, act=0, y=None):
     _dev(x, torch.float16, "x")
     M, K = x.shape

@@ -98,12 +98,16 @@ int check_config(const dit_config* c) {
   CHECK(c->n_blocks >= 0 && c->hidden > 0 && c->n_heads > 0 && c->mlp > 0 && c->channels > 0 &&
             c->text_tokens > 0 && c->text_dim > 0,
         ALD_E_INVALID);
-  CHECK(c->wmode == ALD_W8A8 || c->wmode == ALD_F16 || c->wmode == ALD_Q4, ALD_E_INVALID);
+  CHECK(c->wmode == ALD_W8A8 || c->wmode == ALD_F16 || c->wmode == ALD_Q4 || c->wmode == ALD_W8A16,
+        ALD_E_INVALID);
   CHECK(c->head_dim == 64 && c->hidden == c->n_heads * 64, ALD_E_UNSUPPORTED);
   CHECK(c->hidden % 16 == 0 && c->mlp % 16 == 0 && c->text_dim % 16 == 0 && c->channels % 8 == 0,
         ALD_E_UNSUPPORTED);
   if (c->wmode == ALD_Q4)
     CHECK(c->hidden % 32 == 0 && c->mlp % 32 == 0 && c->text_dim % 32 == 0, ALD_E_UNSUPPORTED);
+  // the 8-bit weight-only GEMM streams 64-element K slices and has no generic fallback
+  if (c->wmode == ALD_W8A16)
+    CHECK(c->hidden % 64 == 0 && c->mlp % 64 == 0 && c->text_dim % 64 == 0, ALD_E_UNSUPPORTED);
   CHECK(c->hidden <= 8192 && c->mlp <= 8192 && c->text_dim <= 8192, ALD_E_UNSUPPORTED);
   CHECK(c->hidden % 2 == 0, ALD_E_UNSUPPORTED);
   CHECK(c->steer_block >= -1 && c->steer_block < c->n_blocks, ALD_E_INVALID);
@@ -138,7 +142,7 @@ int check_weights(const dit_config* c, const dit_weights* w) {
 }
 
 // y[M, N] = epilogue(A . W^T) for one block linear; A is int8 codes (W8A8,
-// with per-row scales xs) or fp16 (F16 / Q4)
+// with per-row scales xs) or fp16 (F16 / Q4 / W8A16)
 void run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, const float* xs, int M, int K, int N,
                 const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy, hipStream_t st) {
   GemmArgs g;
@@ -161,6 +165,9 @@ void run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, cons
   } else if (wmode == ALD_Q4) {
     g.b_scale = static_cast<const uint16_t*>(L.scale);
     launch_gemm(A_F16, B_Q4, g, st);
+  } else if (wmode == ALD_W8A16) {
+    g.epi.w_scale = static_cast<const float*>(L.scale);
+    launch_gemm(A_F16, B_I8, g, st);
   } else {
     launch_gemm(A_F16, B_F16, g, st);
   }
@@ -211,6 +218,9 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   if (a->renoise) CHECK(a->x0 && a->eps && al16(a->x0) && al16(a->eps), ALD_E_INVALID);
   if (a->v_out) CHECK(al16(a->v_out), ALD_E_INVALID);
   CHECK(2 * a->n_tok <= INT32_MAX, ALD_E_UNSUPPORTED);
+  // W8A16: the DMA GEMM addresses activations with 32-bit byte offsets
+  if (c->wmode == ALD_W8A16)
+    CHECK(2 * a->n_tok * 2 * (int64_t)std::max(c->hidden, c->mlp) < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
   CHECK(ws && al16(ws), ALD_E_INVALID);
   StepBuffers b;
   size_t need = carve_step(c, a->n_tok, a->R, static_cast<uint8_t*>(ws), ws_bytes, &b);
@@ -386,6 +396,37 @@ int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, 
   return launched();
 }
 
+int q8w_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, const float* w_scale, int N,
+               const float* bias, const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy,
+               hipStream_t stream) {
+  CHECK(M >= 0 && N >= 0 && K > 0, ALD_E_INVALID);
+  int e = check_epilogue(M, N, residual, ldr, act, y, ldy);
+  if (e) return e;
+  if (M == 0 || N == 0) return ALD_OK;
+  CHECK(x && wq && w_scale && y, ALD_E_INVALID);
+  CHECK(al16(x) && al16(wq) && ldx >= K && ldx % 8 == 0, ALD_E_INVALID);
+  CHECK(K % 64 == 0, ALD_E_UNSUPPORTED);
+  GemmArgs g;
+  g.A = x;
+  g.lda = ldx;
+  g.B = wq;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi.w_scale = w_scale;
+  g.epi.bias = bias;
+  g.epi.residual = residual;
+  g.epi.ldr = ldr;
+  g.epi.y = y;
+  g.epi.ldy = ldy;
+  g.epi.act = act;
+  // only the DMA GEMM implements this operand pair
+  CHECK(gemm_dma_applicable(A_F16, B_I8, g), ALD_E_UNSUPPORTED);
+  prepare();
+  launch_gemm(A_F16, B_I8, g, stream);
+  return launched();
+}
+
 int q4_linear(const uint16_t* x, int64_t ldx, int M, int K, const uint8_t* wq4, const uint16_t* w_scale, int N,
               const float* bias, const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy,
               hipStream_t stream) {
@@ -527,6 +568,7 @@ int dit_text_kv(const dit_config* c, const dit_weights* w, const uint16_t* text,
   const int Dt = c->text_dim, H = c->hidden;
   size_t need = align256((size_t)rows * Dt) + align256((size_t)rows * 4);
   CHECK(need <= ws_bytes, ALD_E_WORKSPACE);
+  if (c->wmode == ALD_W8A16) CHECK((int64_t)rows * Dt * 2 < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
   prepare();
   int8_t* codes = static_cast<int8_t*>(ws);
   float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)rows * Dt));

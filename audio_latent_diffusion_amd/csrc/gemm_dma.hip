@@ -77,19 +77,19 @@ namespace {
 constexpr int BLK = 1024;  // LDS block: one 16-byte copy instruction (64 lanes)
 constexpr int KB = 128;    // X bytes per stage and row (one cache line)
 
-enum { M_I8 = 0, M_F16 = 1, M_Q4 = 2 };                              // operand modes
+enum { M_I8 = 0, M_F16 = 1, M_Q4 = 2, M_Q8W = 3 };                  // operand modes
 enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };  // epilogue kinds
 
 template <int BM_, int BN_, int STAGES_, int MODE_, int WGN_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, MODE = MODE_;
-  static constexpr bool INT = MODE == M_I8, Q4 = MODE == M_Q4;
+  static constexpr bool INT = MODE == M_I8, Q4 = MODE == M_Q4, Q8W = MODE == M_Q8W;
   static constexpr int WGM = 2, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int KS = 4;                      // 32-byte X slices per stage
   static constexpr int BX = BM / 8;                 // X blocks per stage (8 rows x 128 B)
-  static constexpr int BW = Q4 ? BN / 32 : BN / 8;  // W blocks per stage
+  static constexpr int BW = Q4 ? BN / 32 : (Q8W ? BN / 16 : BN / 8);  // W blocks per stage
   // Q4 scale copies (64 rows each), padded so that the copies split evenly
   static constexpr int SC0 = Q4 ? BN / 64 : 0;
   static constexpr int SCL = Q4 ? SC0 + (WAVES - (BX + BW + SC0) % WAVES) % WAVES : 0;
@@ -159,7 +159,9 @@ struct Loader {
     const int b = wave + C::WAVES * i;
     return b < C::BX ? 0 : (b < C::BX + C::BW ? 1 : 2);
   }
-  __device__ __forceinline__ static int step(int k) { return k == 0 ? KB : (C::Q4 ? (k == 1 ? 32 : 4) : KB); }
+  __device__ __forceinline__ static int step(int k) {
+    return k == 0 ? KB : (C::Q4 ? (k == 1 ? 32 : 4) : (C::Q8W ? 64 : KB));
+  }
   __device__ __forceinline__ static int dst(int b) {
     return b < C::BX + C::BW ? b * BLK : C::S_OFF + (b - C::BX - C::BW) * 256;
   }
@@ -176,7 +178,11 @@ struct Loader {
         off[i] = (uint32_t)r * ldx + ((lane & 7) ^ swz(tr)) * 16;
       } else if (b < C::BX + C::BW) {
         const int bw = b - C::BX;
-        if constexpr (!C::Q4) {  // int8 / fp16 W: same layout as X
+        if constexpr (C::Q8W) {  // int8 W of fp16 X: 64 bytes per row and stage, 16 rows per block
+          const int tr = bw * 16 + (lane >> 2);
+          const int r = min(n0 + tr, g.N - 1);
+          off[i] = (uint32_t)r * (uint32_t)g.K + ((lane & 3) ^ (tr & 3)) * 16;
+        } else if constexpr (!C::Q4) {  // int8 / fp16 W: same layout as X
           const int tr = bw * 8 + (lane >> 3);
           const int r = min(n0 + tr, g.N - 1);
           off[i] = (uint32_t)r * (uint32_t)(g.K * EB) + ((lane & 7) ^ swz(tr)) * 16;
@@ -279,6 +285,22 @@ __device__ __forceinline__ v4i dequant8(uint32_t packed, v2h s2) {
   return out;
 }
 
+// 8 int8 weights -> 8 fp16, exact: with the sign bit flipped a byte is
+// q + 128; placed under the fp16 exponent byte 0x64 it reads 1024 + q + 128,
+// and subtracting 1152 gives q.  v_perm_b32 interleaves two bytes of the
+// data with two 0x64 bytes per register.
+__device__ __forceinline__ v4i widen_i8x8(uint2 w) {
+  const uint32_t a = w.x ^ 0x80808080u, b = w.y ^ 0x80808080u;
+  const v2h off = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const uint32_t e = 0x64646464u;
+  const uint32_t h[4] = {__builtin_amdgcn_perm(e, a, 0x04010400u), __builtin_amdgcn_perm(e, a, 0x04030402u),
+                         __builtin_amdgcn_perm(e, b, 0x04010400u), __builtin_amdgcn_perm(e, b, 0x04030402u)};
+  v4i out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(int, __builtin_bit_cast(v2h, h[i]) + off);
+  return out;
+}
+
 template <class C>
 using AccT = typename std::conditional<C::INT, v16i, v16f>::type;
 
@@ -301,7 +323,9 @@ __device__ __forceinline__ void mfma_slice(AccT<C> (&acc)[C::NJ][C::MI], const v
 // Operand fragments of K slice ks from a stage.  X (and int8 / fp16 W): 16
 // swizzled bytes per lane.  Q4 W: slice ks covers values 16 ks .. 16 ks + 15
 // of the stage, i.e. bytes 8 (ks % 2) .. 8 (ks % 2) + 7 of group ks / 2; lane
-// l takes the 4 bytes at 4 (l / 32) of those and its row's scale.
+// l takes the 4 bytes at 4 (l / 32) of those and its row's scale.  Q8W W
+// (64-byte rows, chunk c at slot c ^ (row & 3)): slice ks is chunk ks; lane l
+// takes its 8 bytes at 8 (l / 32) and widens them to fp16.
 template <class C>
 struct Frags {
   int off[C::KS];  // lane's byte offset of slice ks in a 32-row block (8-row blocks of 128 B)
@@ -323,7 +347,12 @@ struct Frags {
     const uint8_t* sx = stage + wm * C::MI * B32;
 #pragma unroll
     for (int i = 0; i < C::MI; ++i) xf[i] = *reinterpret_cast<const v4i*>(sx + i * B32 + off[ks]);
-    if constexpr (!C::Q4) {
+    if constexpr (C::Q8W) {
+      const int lr = threadIdx.x & 31, h = (threadIdx.x >> 5) & 1;
+      const uint8_t* sw = stage + C::W_OFF + (wn * C::WN + lr) * 64 + ((ks ^ (lr & 3)) << 4) + 8 * h;
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) wf[j] = widen_i8x8(*reinterpret_cast<const uint2*>(sw + j * 32 * 64));
+    } else if constexpr (!C::Q4) {
       const uint8_t* sw = stage + C::W_OFF + wn * C::NJ * B32;
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) wf[j] = *reinterpret_cast<const v4i*>(sw + j * B32 + off[ks]);
@@ -515,6 +544,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
         for (int r = 0; r < 8; ++r) {
           float x;
           if constexpr (INT) x = __builtin_fmaf((float)(int32_t)a[r] * xs, ws[r], bs[r]);
+          else if constexpr (C::Q8W) x = __builtin_fmaf(__builtin_bit_cast(float, a[r]), ws[r], bs[r]);
           else x = __builtin_bit_cast(float, a[r]) + bs[r];
           if constexpr (GELU) x = gelu_as(x);
           if constexpr (RES) x += res[r];
@@ -573,7 +603,7 @@ void prep_cfg() {
 // tile keeps three stages in flight
 template <int MODE>
 struct Tiles {
-  using T256 = Cfg<256, 256, MODE == M_Q4 ? 3 : 2, MODE, 4>;
+  using T256 = Cfg<256, 256, (MODE == M_Q4 || MODE == M_Q8W) ? 3 : 2, MODE, 4>;
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 5, MODE>;
   using T64 = Cfg<64, 64, 8, MODE>;
@@ -608,13 +638,15 @@ void gemm_dma_prepare() {
   prep_mode<M_I8>();
   prep_mode<M_F16>();
   prep_mode<M_Q4>();
+  prep_mode<M_Q8W>();
 }
 
 bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
   const bool i8 = akind == A_I8 && bkind == B_I8;
   const bool f16 = akind == A_F16 && bkind == B_F16;
   const bool q4 = akind == A_F16 && bkind == B_Q4;
-  if (!(i8 || f16 || q4)) return false;
+  const bool q8w = akind == A_F16 && bkind == B_I8;
+  if (!(i8 || f16 || q4 || q8w)) return false;
   const int64_t kb = (int64_t)g.K * (i8 ? 1 : 2);
   if (kb % KB != 0) return false;  // whole 128-byte X stages (Q4: whole pairs of groups)
   const int64_t ldb = (int64_t)g.lda * (i8 ? 1 : 2);
@@ -622,7 +654,7 @@ bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
   if ((reinterpret_cast<uintptr_t>(g.A) & 15) || (reinterpret_cast<uintptr_t>(g.B) & 15)) return false;
   if (q4 && (reinterpret_cast<uintptr_t>(g.b_scale) & 3)) return false;
   // copy sources are 32-bit byte offsets from the operand base pointers
-  const int64_t wbytes = (int64_t)g.N * (q4 ? g.K / 2 : kb);
+  const int64_t wbytes = (int64_t)g.N * (q4 ? g.K / 2 : (q8w ? g.K : kb));
   if ((int64_t)g.M * ldb >= ((int64_t)1 << 32) || wbytes >= ((int64_t)1 << 32)) return false;
   return g.M > 0 && g.N > 0;
 }
@@ -630,6 +662,7 @@ bool gemm_dma_applicable(int akind, int bkind, const GemmArgs& g) {
 void launch_gemm_dma(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
   if (akind == A_I8) dispatch<M_I8>(g, st);
   else if (bkind == B_Q4) dispatch<M_Q4>(g, st);
+  else if (bkind == B_I8) dispatch<M_Q8W>(g, st);
   else dispatch<M_F16>(g, st);
 }
 

@@ -1,7 +1,7 @@
 """Device-resident DiT model and step runner over the C ABI.
 
 DiTModel uploads the fp16 weights, packs the block linears on the GPU
-(per-output-channel int8 for W8A8, group-32 int4 for q4) and releases the
+(per-output-channel int8 for W8A8 and W8A16, group-32 int4 for q4) and releases the
 fp16 copies afterwards, so the lower precision replaces the footprint
 instead of adding to it (aria, Section III-A, runtime).  StepRunner owns
 the latent state, the per-step device arrays (t, steering strength,
@@ -53,7 +53,7 @@ class DiTModel:
             for name, w16 in blk.w.items():
                 wt = _t(w16, f16, dev)
                 bias = _t(blk.b[name], f32, dev)
-                if self.wmode == L.ALD_W8A8:
+                if self.wmode in (L.ALD_W8A8, L.ALD_W8A16):
                     q, s = B.quantize_rows_q8(wt)
                     d[name] = (q, s, bias)
                 elif self.wmode == L.ALD_Q4:

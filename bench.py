@@ -162,18 +162,23 @@ def kernel_rooflines():
                            shape=f"batch {Bn} x {S} tokens x {nh} heads, head dim 64")
         del qkv, o
 
-    # fp16-weight GEMMs (serving block mix) and 4-bit-weight GEMMs (4-bit model mix)
-    for name, M, shapes, q4 in (("f16_gemm_serve", 8192, MIX_SHAPES(1536, 6144), False),
-                                ("q4_gemm", 8192, MIX_SHAPES(2048, 8192), True)):
+    # fp16-weight and 8-bit weight-only GEMMs (serving block mix), 4-bit-weight
+    # GEMMs (4-bit model mix); all three run fp16 MFMAs
+    for name, M, shapes, kind in (("f16_gemm_serve", 8192, MIX_SHAPES(1536, 6144), "f16"),
+                                  ("q8w_gemm_serve", 8192, MIX_SHAPES(1536, 6144), "q8w"),
+                                  ("q4_gemm", 8192, MIX_SHAPES(2048, 8192), "q4")):
         launches, flops = [], 0.0
         for K, N in shapes:
             x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
             w = (0.02 * torch.randn((N, K), device="cuda", generator=g)).half()
             b = torch.zeros(N, device="cuda")
             y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-            if q4:
+            if kind == "q4":
                 p, sc = B.quantize_q4(w)
                 launches.append(lambda x=x, p=p, sc=sc, b=b, y=y: B.q4_linear(x, p, sc, b, y=y))
+            elif kind == "q8w":
+                p, sc = B.quantize_rows_q8(w)
+                launches.append(lambda x=x, p=p, sc=sc, b=b, y=y: B.q8w_linear(x, p, sc, b, y=y))
             else:
                 launches.append(lambda x=x, w=w, b=b, y=y: B.f16_linear(x, w, b, y=y))
             flops += 2.0 * M * N * K

@@ -56,7 +56,7 @@ enum {
 
 /* Weight precision of the block linears (aria, Section III-A: the precision
  * ladder fp16 / 8-bit / W8A8 / 4-bit). */
-enum { ALD_W8A8 = 0, ALD_F16 = 1, ALD_Q4 = 2 };
+enum { ALD_W8A8 = 0, ALD_F16 = 1, ALD_Q4 = 2, ALD_W8A16 = 3 };
 
 /* Epilogue activation. */
 enum { ALD_ACT_NONE = 0, ALD_ACT_GELU = 1 };
@@ -134,6 +134,21 @@ int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K,
                 const float* bias, const uint16_t* residual, int64_t ldr,
                 int act, uint16_t* y, int64_t ldy, int8_t* xq, float* x_scale,
                 int32_t* acc, unsigned flags, hipStream_t stream);
+
+/* 8-bit weight-only linear (aria, Section III-A: 8-bit weights, a rung of the
+ * precision ladder distinct from W8A8): fp16 activations, int8 weights with
+ * one fp32 scale per output channel (layout of quantize_rows_q8 applied to
+ * the weights):
+ *   y[m, n] = fp16( s[n] * sum_k x[m, k] q[n, k] + bias[n] (+GELU) (+res) )
+ * The codes are widened to fp16 exactly inside the GEMM main loop, fp16 x
+ * fp16 -> fp32 on MFMA, and the channel scale is applied in the epilogue
+ * (equal in real arithmetic to x . (q s)).  wq [N, K] int8, w_scale [N] fp32.
+ * K % 64 == 0, ldx % 8 == 0, x and wq 16-byte aligned (ALD_E_UNSUPPORTED /
+ * ALD_E_INVALID otherwise). */
+int q8w_linear(const uint16_t* x, int64_t ldx, int M, int K,
+               const int8_t* wq, const float* w_scale, int N,
+               const float* bias, const uint16_t* residual, int64_t ldr,
+               int act, uint16_t* y, int64_t ldy, hipStream_t stream);
 
 /* 4-bit weight-only linear: W = fp16(q * s) dequantized inside the GEMM main
  * loop, fp16 x fp16 -> fp32 on MFMA.  wq4 [N, K/2], w_scale [N, K/32] fp16
@@ -231,14 +246,14 @@ typedef struct {
   int channels;      /* latent channels C              */
   int text_tokens;   /* T                              */
   int text_dim;      /* D_t                            */
-  int wmode;         /* ALD_W8A8 | ALD_F16 | ALD_Q4    */
+  int wmode;         /* ALD_W8A8 | ALD_F16 | ALD_Q4 | ALD_W8A16 */
   int steer_block;   /* block whose output is steered; -1: none */
   float ln_eps;
   int steer_mode;    /* ALD_STEER_ADD | ALD_STEER_PROJECT */
 } dit_config;
 
 /* One linear layer's weights in the precision of dit_config.wmode:
- *   ALD_W8A8: w = int8 [N, K], scale = fp32 [N]
+ *   ALD_W8A8 and ALD_W8A16: w = int8 [N, K], scale = fp32 [N]
  *   ALD_F16 : w = fp16 [N, K], scale = NULL
  *   ALD_Q4  : w = uint8 [N, K/2], scale = fp16 [N, K/32]
  * bias fp32 [N]. */

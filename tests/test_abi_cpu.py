@@ -57,6 +57,11 @@ def test_gemm_validation():
     assert lib.w8a8_linear(None, 64, 0, 64, None, None, 8, None, None, 0, 0, None, 8, None, None, None, 0,
                            None) == L.ALD_OK
     assert lib.q4_linear(FAKE, 64, 4, 48, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_UNSUPPORTED
+    # 8-bit weight-only: K must be whole 64-element slices; a missing scale is invalid
+    assert lib.q8w_linear(FAKE, 96, 4, 96, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_UNSUPPORTED
+    assert lib.q8w_linear(FAKE, 64, 4, 64, FAKE, None, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_INVALID
+    assert lib.q8w_linear(FAKE, 60, 4, 64, FAKE, FAKE, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_INVALID
+    assert lib.q8w_linear(None, 64, 0, 64, None, None, 8, None, None, 0, 0, None, 8, None) == L.ALD_OK
     assert lib.f16_linear(FAKE, 64, 4, 64, None, 8, None, None, 0, 0, FAKE, 8, None) == L.ALD_E_INVALID
     assert lib.quantize_q4(FAKE, 4, 48, FAKE, FAKE, None) == L.ALD_E_UNSUPPORTED
     assert lib.quantize_rows_q8(FAKE, 64, 4, 60, FAKE, 64, FAKE, None) == L.ALD_E_INVALID
@@ -130,6 +135,9 @@ def test_step_validation():
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     bad = _cfg(wmode=7)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    # W8A16 needs the widths in whole 64-element slices
+    bad = _cfg(wmode=L.ALD_W8A16, text_dim=96)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_UNSUPPORTED
     a2 = L.dit_step_args(x=FAKE, text_kv=FAKE, R=1, seq=60, n_tok=64, max_seq=64, t_cur=FAKE, t_next=FAKE,
                          guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE)
     assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a2), FAKE, need, None) == L.ALD_E_INVALID

@@ -183,6 +183,53 @@ def test_q4_full_shapes_sampled(M, K, N):
     f16_close(host(y)[rows], O.q4_linear(host(x)[rows], p, s, b, act=1))
 
 
+# ------------------------------------------------------------- 8-bit weight-only GEMM
+
+# one shape per tile size of the launch (64x64, 128x64, 128x128 and the
+# 8-wave 256x256), ragged in M and N, K an odd number of 64-element slices
+@pytest.mark.parametrize("M,K,N", [(1, 64, 1), (77, 192, 130), (200, 640, 203), (1100, 320, 1400),
+                                   (1500, 576, 1900), (3000, 640, 3900)])
+def test_q8w_linear(M, K, N):
+    r = rng(M * 5 + K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    q, s = O.quantize_rows_q8(w)
+    y = B.q8w_linear(dev(x), dev(q), dev(s), dev(b), residual=dev(res))
+    f16_close(host(y), O.q8w_linear(x, q, s, b, residual=res))
+
+
+def test_q8w_gelu_inplace_residual_and_strided_input():
+    r = rng(21)
+    M, K, N = 160, 384, 272
+    xw = r.standard_normal((M, K + 64)).astype(np.float16)
+    w = (0.05 * r.standard_normal((N, K))).astype(np.float16)
+    q, s = O.quantize_rows_q8(w)
+    xd = dev(xw)[:, :K]  # row stride K + 64
+    y = B.q8w_linear(xd, dev(q), dev(s), act=L.ALD_ACT_GELU)
+    f16_close(host(y), O.q8w_linear(xw[:, :K], q, s, None, act=1))
+    h = r.standard_normal((M, N)).astype(np.float16)
+    ht = dev(h)
+    B.q8w_linear(xd, dev(q), dev(s), residual=ht, y=ht)
+    f16_close(host(ht), O.q8w_linear(xw[:, :K], q, s, None, residual=h))
+
+
+@pytest.mark.parametrize("M,K,N", [(8192, 1536, 4608), (8192, 6144, 1536)])
+def test_q8w_serve_shapes_sampled(M, K, N):
+    """8-bit weight-only GEMMs at the serving CFG batch (8192 rows, hidden
+    1536, MLP 6144) in the step's launch configuration, sampled rows."""
+    r = rng(M + K + N + 1)
+    g = torch.Generator(device="cuda").manual_seed(K + N + 1)
+    x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    q, s = O.quantize_rows_q8(w)
+    y = B.q8w_linear(x, dev(q), dev(s), dev(b), act=L.ALD_ACT_GELU)
+    rows = np.concatenate([np.sort(rng(2).choice(M, 40, replace=False)), [0, M - 1]])
+    f16_close(host(y)[rows], O.q8w_linear(host(x)[rows], q, s, b, act=1))
+
+
 # ------------------------------------------------------------- attention
 
 def _attn_ref(q, k, v, nh, cu_q, cu_k):

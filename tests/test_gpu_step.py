@@ -38,7 +38,7 @@ def _oracle_steps(om, inp, steps, resid=RESID):
     return x, tr
 
 
-@pytest.mark.parametrize("wmode", ["w8a8", "f16", "q4"])
+@pytest.mark.parametrize("wmode", ["w8a8", "f16", "q4", "w8a16"])
 def test_tiny_step_parity(wmode):
     cfg = I.TINY.replace(wmode=wmode)
     p = I.make_params(cfg)

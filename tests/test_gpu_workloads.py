@@ -44,9 +44,9 @@ def _parity(cfg, steps, inp=None):
     return err
 
 
-@pytest.mark.parametrize("wmode", ["w8a8", "f16"])
+@pytest.mark.parametrize("wmode", ["w8a8", "f16", "w8a16"])
 def test_serve_widths_two_blocks(wmode):
-    """Serving widths, both weight arms on the same inputs; steering active."""
+    """Serving widths, each weight arm on the same inputs; steering active."""
     cfg = I.SERVE.replace(n_blocks=2, wmode=wmode, steer_block=1, steer_alpha=0.5, steer_steps=(0,))
     assert _parity(cfg, [0]) < TOL
 
