@@ -52,6 +52,12 @@ class DiTConfig:
     seed: int
     ln_eps: float = 1e-5
     steer_mode: str = "add"  # "add" (alpha, residual-norm units) | "project" (beta)
+    steer_site: str = "residual"  # "residual" (block output) | "latent" (model input) | "text"
+
+    @property
+    def steer_dim(self) -> int:
+        """Width of the steered tensor: H, C or D_t."""
+        return {"residual": self.hidden, "latent": self.channels, "text": self.text_dim}[self.steer_site]
 
     @property
     def head_dim(self) -> int:
@@ -164,7 +170,7 @@ class StepInputs:
     eps:    fp32 [R*S, C] re-noising draw for warm start
     seqlens: int [R] latent length per request
     guidance: fp32 [R]
-    direction: fp32 [H] unit steering direction
+    direction: fp32 [H, C or D_t by steering site] unit steering direction
     t_grid: fp32 [N+1]  t_i = 1 - i/N
     alpha:  fp32 [N, R] steering strength per step and request
     start_step: int [R] first step run by each request (0 = cold start)
@@ -196,7 +202,7 @@ def make_inputs(cfg: DiTConfig, seqlens: Optional[np.ndarray] = None) -> StepInp
     x = st[_S_LATENT].standard_normal((tot, C), dtype=np.float32)
     text = np.zeros((2 * R, T, Dt), dtype=np.float16)
     text[:R] = st[_S_TEXT].standard_normal((R, T, Dt), dtype=np.float32).astype(np.float16)
-    g = st[_S_DIR].standard_normal(H)
+    g = st[_S_DIR].standard_normal(cfg.steer_dim)
     direction = (g / np.sqrt(np.sum(g * g))).astype(np.float32)
     alpha = np.zeros((N, R), dtype=np.float32)
     for s in cfg.steer_steps:

@@ -310,6 +310,50 @@ def steer_project(h16, row_beta, direction) -> np.ndarray:
     return h
 
 
+def steer_latent(x32, row_alpha, resid_norm, direction, mode="add") -> np.ndarray:
+    """Steering at the compact audio latent (aria, Section III: the latent is
+    one of three injection sites, beside the residual stream and the text
+    conditioning).  Reading: the shift applies to the denoiser's input at the
+    steered step, not to the sampler state, as a hook on the model input would.
+
+    x32: fp32 [N, C] latent state; returns the fp16 model input [N, C].  Rows
+    whose strength is exactly 0 are fp16(x) (the unsteered input); others
+    x + a * resid_norm * d (add) or x + a * (x . d) * d (project) in fp64,
+    rounded once to fp16.
+    """
+    x = np.asarray(x32, F32)
+    out = x.astype(F16)
+    a = np.asarray(row_alpha, dtype=F32)
+    rows = np.nonzero(a != 0)[0]
+    if rows.size:
+        d = np.asarray(direction, F32).astype(F64)
+        xr = x[rows].astype(F64)
+        if mode == "project":
+            c = a[rows].astype(F64) * (xr @ d)
+        elif mode == "add":
+            c = a[rows].astype(F64) * float(resid_norm)
+        else:
+            raise ValueError(mode)
+        out[rows] = (xr + c[:, None] * d[None, :]).astype(F16)
+    return out
+
+
+def steer_text(text16, R, T, alpha_req, resid_norm, direction, mode="add") -> np.ndarray:
+    """Steering at the text conditioning (aria, Section III, third injection
+    site).  text16: fp16 [2R*T, D_t], the cond rows of request r at
+    [r*T, (r+1)*T), then the null-prompt rows.  Reading: only the cond rows
+    carry text conditioning, so only they are steered (strength alpha_req[r]);
+    the null prompt stays as it is.  Same arithmetic as the residual site."""
+    t = np.asarray(text16, F16).reshape(2 * R * T, -1)
+    row_alpha = np.zeros(2 * R * T, F32)
+    row_alpha[:R * T] = np.repeat(np.asarray(alpha_req, F32), T)
+    if mode == "project":
+        return steer_project(t, row_alpha, direction)
+    if mode == "add":
+        return steer_add(t, row_alpha, resid_norm, direction)
+    raise ValueError(mode)
+
+
 def cfg_merge(v_cond16, v_uncond16, w) -> np.ndarray:
     """Classifier-free-guidance merge of the vLLM audio pipeline page,
     Section 2.4, Eq. (1), applied to the velocity: w * cond + (1 - w) * uncond,
@@ -408,10 +452,14 @@ class StepTrace:
 
 def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv: List[np.ndarray],
                 t_cur: np.ndarray, row_alpha_req: np.ndarray, resid_norm: float,
-                direction: np.ndarray, keep_blocks: Sequence[int] = ()) -> (np.ndarray, StepTrace):
+                direction: np.ndarray, keep_blocks: Sequence[int] = (),
+                text16: Optional[np.ndarray] = None) -> (np.ndarray, StepTrace):
     """Model velocity v (fp16, [cond tokens | uncond tokens] x C) for the
     packed latent x (fp32 [N, C]) of R requests with per-request t and
-    steering strength.
+    steering strength.  The steering site is cfg.steer_site: "residual" (the
+    chosen block's output), "latent" (the model input) or "text" (the cond
+    text conditioning, whose keys/values are then recomputed from the steered
+    text; text16 is required for it).
 
     Block topology (reading; the pages say only that each block writes an
     additive update into a residual stream and that the denoiser
@@ -431,11 +479,19 @@ def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv:
     # rows: [cond tokens (request-packed) | uncond tokens]; both rows of a
     # CFG pair see the same latent (the companion is kept in sync with the
     # main request, vLLM audio pipeline page, Section 2.4)
-    x2 = np.concatenate([x, x], axis=0)
+    site = getattr(cfg, "steer_site", "residual")
+    steering = cfg.steer_block >= 0
+    if steering and site == "latent":
+        x_in = steer_latent(x, np.asarray(row_alpha_req, F32)[req_of_tok], resid_norm, direction, cfg.steer_mode)
+    else:
+        x_in = np.asarray(x, F32).astype(F16)
+    if steering and site == "text":
+        kv = text_kv(model, steer_text(text16, R, T, row_alpha_req, resid_norm, direction, cfg.steer_mode))
+    x2 = np.concatenate([x_in, x_in], axis=0)
     req_of_row = np.concatenate([req_of_tok, req_of_tok])
     t_row = np.asarray(t_cur, F32)[req_of_row]
     temb = timestep_embedding(t_row, H)
-    h64 = np.asarray(x2, F32).astype(F16).astype(F64) @ P.w_in.astype(F64).T
+    h64 = x2.astype(F64) @ P.w_in.astype(F64).T
     h = (h64 + P.b_in.astype(F64)[None, :] + temb).astype(F16)
     cu_q = np.concatenate([cu, Ntot + cu[1:]])       # 2R sequences
     cu_t = np.arange(2 * R + 1, dtype=np.int64) * T  # text rows per CFG row
@@ -457,7 +513,7 @@ def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv:
         h = lin["down"](g, residual=h)
         if li in keep_blocks:
             trace.block_out[li] = h.copy()
-        if li == cfg.steer_block:
+        if steering and site == "residual" and li == cfg.steer_block:
             if cfg.steer_mode == "project":
                 h = steer_project(h, row_alpha, direction)
             else:
@@ -470,13 +526,15 @@ def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv:
 
 def dit_step(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv: List[np.ndarray],
              t_cur, t_next, guidance, row_alpha_req, resid_norm, direction,
-             active: Optional[np.ndarray] = None, keep_blocks: Sequence[int] = ()):
+             active: Optional[np.ndarray] = None, keep_blocks: Sequence[int] = (),
+             text16: Optional[np.ndarray] = None):
     """One denoising step for all requests: model pass on the CFG pair, merge,
     Euler update.  Requests whose `active` flag is false keep their latent."""
     R = len(seqlens)
     seqlens = np.asarray(seqlens, dtype=np.int64)
     Ntot = int(seqlens.sum())
-    v, trace = dit_forward(model, x, seqlens, kv, t_cur, row_alpha_req, resid_norm, direction, keep_blocks)
+    v, trace = dit_forward(model, x, seqlens, kv, t_cur, row_alpha_req, resid_norm, direction, keep_blocks,
+                           text16)
     req = np.repeat(np.arange(R), seqlens)
     w = np.asarray(guidance, F32)[req][:, None]
     v_hat = cfg_merge(v[:Ntot], v[Ntot:], w)
@@ -526,7 +584,7 @@ def run_sampler(model: PreparedModel, inp, kv=None, resid_norm: float = 0.0,
         t_cur = np.full(R, tg[i], F32)
         t_next = np.full(R, tg[i + 1], F32)
         x, tr = dit_step(model, x, inp.seqlens, kv, t_cur, t_next, inp.guidance, alpha[i],
-                         resid_norm, inp.direction, active, keep_blocks)
+                         resid_norm, inp.direction, active, keep_blocks, inp.text)
         traces.append(tr)
     return x, traces
 

@@ -191,6 +191,52 @@ def test_steer_project_scales_the_component_along_the_direction():
     assert np.all(np.abs(out @ d64) < 2e-2)
 
 
+def test_steer_latent_zero_rows_and_closed_forms():
+    """Latent site: rows with strength 0 are the unsteered fp16 input; on a zero
+    latent the add gives fp16(a * n * d) exactly; along a basis direction only
+    that channel moves; projection of an orthogonal row is a no-op."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    d = np.zeros(64, np.float32)
+    d[5] = 1.0
+    a = np.array([0, 0.5, 0, -0.25, 1.0, 0], np.float32)
+    out = O.steer_latent(x, a, 4.0, d)
+    assert out.dtype == np.float16
+    zero = a == 0
+    assert out[zero].tobytes() == x[zero].astype(np.float16).tobytes()
+    rest = np.delete(np.arange(64), 5)
+    assert np.array_equal(out[:, rest], x[:, rest].astype(np.float16))
+    assert np.array_equal(out[:, 5], (x[:, 5].astype(np.float64) + 4.0 * a).astype(np.float16))
+    z = O.steer_latent(np.zeros((2, 64), np.float32), np.array([0.5, -2.0], np.float32), 3.0, d)
+    assert z[0, 5] == np.float16(1.5) and z[1, 5] == np.float16(-6.0) and not z[:, rest].any()
+    # projection: x + b (x . d) d scales channel 5 by (1 + b), one rounding of the fp32 state
+    p = O.steer_latent(x, a, 4.0, d, mode="project")
+    assert np.array_equal(p[:, 5], (x[:, 5].astype(np.float64) * (1 + a.astype(np.float64))).astype(np.float16))
+    x[1, 5] = 0
+    assert O.steer_latent(x, a, 4.0, d, mode="project")[1].tobytes() == x[1].astype(np.float16).tobytes()
+
+
+def test_steer_text_only_cond_rows_of_each_request():
+    """Text site: request r's cond rows [r*T, (r+1)*T) get strength alpha[r];
+    the null-prompt rows and every row of a request with alpha 0 stay bitwise."""
+    rng = np.random.default_rng(9)
+    R, T, D = 3, 4, 32
+    t = rng.standard_normal((2 * R * T, D)).astype(np.float16)
+    d = rng.standard_normal(D)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    a = np.array([0.5, 0.0, -1.0], np.float32)
+    out = O.steer_text(t, R, T, a, 2.0, d)
+    assert out[R * T:].tobytes() == t[R * T:].tobytes()
+    assert out[T:2 * T].tobytes() == t[T:2 * T].tobytes()
+    for r in (0, 2):
+        rows = slice(r * T, (r + 1) * T)
+        ref = (t[rows].astype(np.float64) + float(a[r]) * 2.0 * d.astype(np.float64)).astype(np.float16)
+        assert np.array_equal(out[rows], ref)
+    pr = O.steer_text(t, R, T, a, 2.0, d, mode="project")
+    assert pr[R * T:].tobytes() == t[R * T:].tobytes()
+    assert np.array_equal(pr[:T], O.steer_project(t[:T], np.full(T, 0.5, np.float32), d))
+
+
 def test_mean_row_norm():
     h = np.array([[3, 4, 0], [0, 0, 1]], np.float16)
     assert O.mean_row_norm(h) == pytest.approx(3.0)   # (5 + 1) / 2

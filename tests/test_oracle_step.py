@@ -50,6 +50,51 @@ def test_alpha_zero_equals_unsteered(tiny):
     assert not np.array_equal(x1, x3)
 
 
+@pytest.mark.parametrize("site", ["latent", "text"])
+@pytest.mark.parametrize("mode", ["add", "project"])
+def test_other_sites_alpha_zero_identity_and_effect(tiny, site, mode):
+    """Latent and text sites: strength 0 is bit-identical to no steering; a
+    nonzero strength changes the step; the sampler state itself is not
+    steered (the update is x + dt * v_hat from the unsteered x)."""
+    m, inp, kv = tiny
+    cfg = CFG.replace(steer_site=site, steer_mode=mode)
+    ms = O.PreparedModel(cfg, m.params, m.lin)
+    rng = np.random.default_rng(12)
+    d = rng.standard_normal(cfg.steer_dim)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    R = len(inp.seqlens)
+    args = (np.full(R, 1.0, np.float32), np.full(R, 0.875, np.float32), np.full(R, 3.0, np.float32))
+    off, _ = O.dit_step(O.PreparedModel(CFG.replace(steer_block=-1), m.params, m.lin), inp.x, inp.seqlens, kv,
+                        *args, np.zeros(R, np.float32), 5.0, np.eye(CFG.hidden, dtype=np.float32)[0])
+    x0, _ = O.dit_step(ms, inp.x, inp.seqlens, kv, *args, np.zeros(R, np.float32), 5.0, d, text16=inp.text)
+    assert x0.tobytes() == off.tobytes()
+    x1, tr = O.dit_step(ms, inp.x, inp.seqlens, kv, *args, np.full(R, 0.5, np.float32), 5.0, d, text16=inp.text)
+    assert O.normwise_rel_err(x1, off) > 1e-4
+    assert np.array_equal(x1, O.euler_update(inp.x, tr.v_hat, np.float32(1.0), np.float32(0.875)))
+
+
+def test_text_site_recomputes_kv_from_the_steered_text(tiny):
+    """With text steering, the step equals an unsteered step fed the keys and
+    values of the steered text (so the steering acts only through them)."""
+    m, inp, kv = tiny
+    cfg = CFG.replace(steer_site="text")
+    rng = np.random.default_rng(13)
+    d = rng.standard_normal(CFG.text_dim)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    R = len(inp.seqlens)
+    args = (np.full(R, 1.0, np.float32), np.full(R, 0.875, np.float32), np.full(R, 3.0, np.float32))
+    a = np.full(R, 0.7, np.float32)
+    xs, _ = O.dit_step(O.PreparedModel(cfg, m.params, m.lin), inp.x, inp.seqlens, kv, *args, a, 6.0, d,
+                       text16=inp.text)
+    kv_s = O.text_kv(m, O.steer_text(inp.text.reshape(-1, CFG.text_dim), R, CFG.text_tokens, a, 6.0, d))
+    xr, _ = O.dit_step(O.PreparedModel(CFG.replace(steer_block=-1), m.params, m.lin), inp.x, inp.seqlens, kv_s,
+                       *args, np.zeros(R, np.float32), 6.0, d)
+    assert xs.tobytes() == xr.tobytes()
+    # the null-prompt keys and values are untouched
+    for li in range(CFG.n_blocks):
+        assert np.array_equal(kv_s[li][R * CFG.text_tokens:], kv[li][R * CFG.text_tokens:])
+
+
 def test_guidance_one_is_cond_branch(tiny):
     m, inp, kv = tiny
     x, tr = _step(m, inp.x, inp.seqlens, kv, w=1.0)
