@@ -19,13 +19,15 @@ ALD_PREQUANT = 1
 ALD_EULER, ALD_RENOISE = 0, 1
 ALD_STEER_ADD, ALD_STEER_PROJECT = 0, 1
 STEER_MODES = {"add": ALD_STEER_ADD, "project": ALD_STEER_PROJECT}
+ALD_SITE_RESIDUAL, ALD_SITE_LATENT, ALD_SITE_TEXT = 0, 1, 2
+STEER_SITES = {"residual": ALD_SITE_RESIDUAL, "latent": ALD_SITE_LATENT, "text": ALD_SITE_TEXT}
 
 WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4, "w8a16": ALD_W8A16}
 
 # every extern "C" entry point of include/ald.h
 EXPORTS = (
     "ald_strerror", "ald_version", "quantize_rows_q8", "quantize_q4", "ln_quant", "ln_f16",
-    "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "cfg_merge",
+    "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "steer_latent", "cfg_merge",
     "sampler_update", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
     "dit_graph_launch", "dit_graph_destroy",
 )
@@ -40,7 +42,8 @@ class AldError(RuntimeError):
 class dit_config(ctypes.Structure):
     _fields_ = [("n_blocks", c_int), ("hidden", c_int), ("n_heads", c_int), ("head_dim", c_int),
                 ("mlp", c_int), ("channels", c_int), ("text_tokens", c_int), ("text_dim", c_int),
-                ("wmode", c_int), ("steer_block", c_int), ("ln_eps", c_float), ("steer_mode", c_int)]
+                ("wmode", c_int), ("steer_block", c_int), ("ln_eps", c_float), ("steer_mode", c_int),
+                ("steer_site", c_int)]
 
 
 class dit_linear(ctypes.Structure):
@@ -65,7 +68,7 @@ class dit_step_args(ctypes.Structure):
                 ("t_cur", c_void_p), ("t_next", c_void_p), ("guidance", c_void_p), ("alpha", c_void_p),
                 ("resid_norm", c_float), ("direction", c_void_p), ("active", c_void_p),
                 ("renoise", c_void_p), ("x0", c_void_p), ("eps", c_void_p), ("v_out", c_void_p),
-                ("block_norms", c_void_p)]
+                ("block_norms", c_void_p), ("text", c_void_p)]
 
 
 _lib = None
@@ -86,6 +89,7 @@ def _declare(lib):
         "f16_linear": (I, [V, I64, I, I, V, I, V, V, I64, I, V, I64, V]),
         "attn_fwd": (I, [V, V, V, I64, I64, I, I, I, I, I, V, V, I, I, F, V, I64, V]),
         "steer_add": (I, [V, I64, I, I, I, I, V, V, F, V, I, V]),
+        "steer_latent": (I, [V, V, I64, I, I, I, V, V, F, V, I, V]),
         "cfg_merge": (I, [V, I64, I, I, V, V, V, V]),
         "sampler_update": (I, [I, V, V, V, V, I64, I, I, V, V, V, V, V]),
         "dit_workspace_size": (c_size_t, [POINTER(dit_config), I64, I]),

@@ -150,6 +150,17 @@ def steer_add(h, alpha, resid_norm, direction, rows_per_req=1, R=1, row_req=None
     return h
 
 
+def steer_latent(x, alpha, resid_norm, direction, rows_per_req=1, R=1, row_req=None, mode=L.ALD_STEER_ADD,
+                 out=None):
+    """Steered copy of the fp32 latent x [n_tok, C] (the model's input at the latent site)."""
+    _dev(x, torch.float32, "x")
+    n_tok, C = x.shape
+    out = torch.empty_like(x) if out is None else out
+    L.check("steer_latent", L.lib().steer_latent(_p(x), _p(out), n_tok, C, rows_per_req, R, _p(row_req), _p(alpha),
+                                                 float(resid_norm), _p(direction), mode, _stream()))
+    return out
+
+
 def cfg_merge(v, w, rows_per_req=1, row_req=None, v_hat=None):
     _dev(v, torch.float16, "v")
     n2, C = v.shape

@@ -70,7 +70,14 @@ struct StepBuffers {
   float* xs;
   uint16_t* v;
   int32_t* cu2;
+  float* x_lat;      // latent site: steered model input [n_tok, C]
+  uint16_t* text_s;  // text site: steered text [2R*T, D_t]
+  int8_t* tcodes;    // text site, W8A8: its int8 codes and row scales
+  float* tscale;
+  uint16_t* kv;      // text site: one block's K/V of the steered text [2R*T, 2H]
 };
+
+bool steers(const dit_config* c, int site) { return c->steer_block >= 0 && c->steer_site == site; }
 
 // same carve used by dit_workspace_size (with base = nullptr) and dit_step
 size_t carve_step(const dit_config* c, int64_t n_tok, int R, uint8_t* base, size_t cap, StepBuffers* b) {
@@ -80,7 +87,7 @@ size_t carve_step(const dit_config* c, int64_t n_tok, int R, uint8_t* base, size
   const int64_t wide = std::max<int64_t>(3 * H, F);
   const int64_t codes = std::max<int64_t>(M * std::max<int64_t>(H, F), rows_t * c->text_dim);
   Carve cv{base, 0, cap};
-  StepBuffers t;
+  StepBuffers t{};
   t.h = cv.take<uint16_t>(M * H);
   t.big = cv.take<uint16_t>(M * wide);
   t.ao = cv.take<uint16_t>(M * H);
@@ -89,6 +96,15 @@ size_t carve_step(const dit_config* c, int64_t n_tok, int R, uint8_t* base, size
   t.xs = cv.take<float>(std::max<int64_t>(M, rows_t));
   t.v = cv.take<uint16_t>(M * C);
   t.cu2 = cv.take<int32_t>(2 * (int64_t)R + 1);
+  if (steers(c, ALD_SITE_LATENT)) t.x_lat = cv.take<float>(n_tok * C);
+  if (steers(c, ALD_SITE_TEXT)) {
+    t.text_s = cv.take<uint16_t>(rows_t * c->text_dim);
+    if (c->wmode == ALD_W8A8) {
+      t.tcodes = cv.take<int8_t>(rows_t * c->text_dim);
+      t.tscale = cv.take<float>(rows_t);
+    }
+    t.kv = cv.take<uint16_t>(rows_t * 2 * H);
+  }
   if (b) *b = t;
   return cv.off;
 }
@@ -112,6 +128,9 @@ int check_config(const dit_config* c) {
   CHECK(c->hidden % 2 == 0, ALD_E_UNSUPPORTED);
   CHECK(c->steer_block >= -1 && c->steer_block < c->n_blocks, ALD_E_INVALID);
   CHECK(c->steer_mode == ALD_STEER_ADD || c->steer_mode == ALD_STEER_PROJECT, ALD_E_INVALID);
+  CHECK(c->steer_site == ALD_SITE_RESIDUAL || c->steer_site == ALD_SITE_LATENT || c->steer_site == ALD_SITE_TEXT,
+        ALD_E_INVALID);
+  if (steers(c, ALD_SITE_LATENT)) CHECK(c->channels <= 512, ALD_E_UNSUPPORTED);
   CHECK(c->ln_eps >= 0.0f, ALD_E_INVALID);
   return ALD_OK;
 }
@@ -215,12 +234,16 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     CHECK(a->seq > 0 && (int64_t)a->seq * a->R == a->n_tok, ALD_E_INVALID);
   }
   if (c->steer_block >= 0) CHECK(a->alpha && a->direction && al16(a->direction), ALD_E_INVALID);
+  if (steers(c, ALD_SITE_TEXT)) CHECK(a->text && al16(a->text), ALD_E_INVALID);
   if (a->renoise) CHECK(a->x0 && a->eps && al16(a->x0) && al16(a->eps), ALD_E_INVALID);
   if (a->v_out) CHECK(al16(a->v_out), ALD_E_INVALID);
   CHECK(2 * a->n_tok <= INT32_MAX, ALD_E_UNSUPPORTED);
   // W8A16: the DMA GEMM addresses activations with 32-bit byte offsets
-  if (c->wmode == ALD_W8A16)
+  if (c->wmode == ALD_W8A16) {
     CHECK(2 * a->n_tok * 2 * (int64_t)std::max(c->hidden, c->mlp) < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
+    if (steers(c, ALD_SITE_TEXT))
+      CHECK(2 * (int64_t)a->R * c->text_tokens * c->text_dim * 2 < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
+  }
   CHECK(ws && al16(ws), ALD_E_INVALID);
   StepBuffers b;
   size_t need = carve_step(c, a->n_tok, a->R, static_cast<uint8_t*>(ws), ws_bytes, &b);
@@ -241,13 +264,39 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   }
   if (a->renoise) launch_renoise(a->x, a->x0, a->eps, n_tok, C, map, a->t_cur, a->renoise, st);
 
+  const bool project = c->steer_mode == ALD_STEER_PROJECT;
+  // latent site: the model reads a steered copy of the latent, the state stays
+  const float* x_in = a->x;
+  if (steers(c, ALD_SITE_LATENT)) {
+    launch_steer_latent(a->x, b.x_lat, n_tok, C, map, a->alpha, a->resid_norm, a->direction, project, st);
+    x_in = b.x_lat;
+  }
   // input projection of the fp32 latent (both CFG rows read the same latent) + time embedding
-  launch_inproj(a->x, n_tok, M, C, w->w_in, H, w->b_in, a->t_cur, map, b.h, st);
+  launch_inproj(x_in, n_tok, M, C, w->w_in, H, w->b_in, a->t_cur, map, b.h, st);
+
+  // text site: steer the cond text rows (request r owns rows [r T, (r+1) T)),
+  // copy the null-prompt rows, and take its activation operand once
+  const bool text_site = steers(c, ALD_SITE_TEXT);
+  const int rows_t = 2 * R * T;
+  ActIn tin{nullptr, 0, nullptr};
+  if (text_site) {
+    const int Dt = c->text_dim;
+    launch_steer_copy(a->text, Dt, b.text_s, Dt, rows_t, R * T, Dt, RowMap{0, T, R, nullptr}, a->alpha,
+                      a->resid_norm, a->direction, project, st);
+    if (wm == ALD_W8A8) {
+      launch_row_quant(b.text_s, Dt, rows_t, Dt, b.tcodes, Dt, b.tscale, st);
+      tin = {b.tcodes, Dt, b.tscale};
+    } else {
+      tin = {b.text_s, Dt, nullptr};
+    }
+  }
 
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   for (int l = 0; l < c->n_blocks; ++l) {
     const dit_block_weights& bw = w->blocks[l];
-    const uint16_t* kv = a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
+    const uint16_t* kv = text_site ? b.kv : a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
+    if (text_site)  // the same linear dit_text_kv applies, on the steered text
+      run_linear(bw.kv, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, 2 * H, nullptr, 0, 0, b.kv, 2 * H, st);
     // self-attention
     ActIn in = layernorm_in(wm, b.h, M, H, bw.ln1_g, bw.ln1_b, c->ln_eps, b, st);
     run_linear(bw.qkv, wm, in.A, in.lda, in.xs, M, H, 3 * H, nullptr, 0, 0, b.big, 3 * H, st);
@@ -267,9 +316,9 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     run_linear(bw.up, wm, in.A, in.lda, in.xs, M, H, F, nullptr, 0, ALD_ACT_GELU, b.big, F, st);
     in = quantize_in(wm, b.big, F, M, F, b, st);
     run_linear(bw.down, wm, in.A, in.lda, in.xs, M, F, H, b.h, H, 0, b.h, H, st);
-    if (l == c->steer_block) {
+    if (steers(c, ALD_SITE_RESIDUAL) && l == c->steer_block) {
       if (a->block_norms) launch_row_norms(b.h, H, M, H, a->block_norms, st);
-      launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, c->steer_mode == ALD_STEER_PROJECT, st);
+      launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, project, st);
     }
   }
 
@@ -512,9 +561,25 @@ int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R, c
   if (M == 0) return ALD_OK;
   CHECK(h && alpha && dir && al16(h) && al16(dir), ALD_E_INVALID);
   CHECK(H % 8 == 0 && ldh >= H && ldh % 8 == 0, ALD_E_INVALID);
+  CHECK(H <= 8192, ALD_E_UNSUPPORTED);
   if (!row_req) CHECK(rows_per_req > 0 && R > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, row_req ? 1 : R, row_req};
   launch_steer(h, ldh, M, H, map, alpha, resid_norm, dir, mode == ALD_STEER_PROJECT, stream);
+  return launched();
+}
+
+int steer_latent(const float* x, float* x_out, int64_t n_tok, int C, int rows_per_req, int R,
+                 const int32_t* row_req, const float* alpha, float resid_norm, const float* dir, int mode,
+                 hipStream_t stream) {
+  CHECK(n_tok >= 0 && C > 0, ALD_E_INVALID);
+  CHECK(mode == ALD_STEER_ADD || mode == ALD_STEER_PROJECT, ALD_E_INVALID);
+  if (n_tok == 0) return ALD_OK;
+  CHECK(x && x_out && alpha && dir && x != x_out, ALD_E_INVALID);
+  CHECK(al16(x) && al16(x_out) && al16(dir) && C % 4 == 0, ALD_E_INVALID);
+  CHECK(C <= 512 && n_tok < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
+  if (!row_req) CHECK(rows_per_req > 0 && R > 0, ALD_E_INVALID);
+  RowMap map{0, row_req ? 1 : rows_per_req, row_req ? 1 : R, row_req};
+  launch_steer_latent(x, x_out, n_tok, C, map, alpha, resid_norm, dir, mode == ALD_STEER_PROJECT, stream);
   return launched();
 }
 

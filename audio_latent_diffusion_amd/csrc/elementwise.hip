@@ -20,12 +20,28 @@ __device__ __forceinline__ int req_of(const RowMap& m, uint32_t row) {
   return m.row_req ? m.row_req[i] : (int)((i / (uint32_t)m.rows_per_req) % (uint32_t)m.R);
 }
 
-// Steering of the rows of h whose request strength a = alpha[r] is nonzero
-// (rows with a == 0 are not touched at all):
-//   add      : h[m, :] += (a * resid_norm) * dir
-//   project  : h[m, :] += (a * (h[m, :] . dir)) * dir   (fp32 dot product)
-template <int NV, bool PROJ>
-__global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, int64_t ldh, int M, int H, RowMap map,
+__device__ __forceinline__ void load4h_nt(const uint16_t* p, float f[4]) {
+  const v2i r = ld8_nt(p);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f[2 * i] = h2f((uint16_t)((uint32_t)r[i] & 0xFFFFu));
+    f[2 * i + 1] = h2f((uint16_t)((uint32_t)r[i] >> 16));
+  }
+}
+__device__ __forceinline__ v4f ld4f_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ void st4f_nt(float* p, v4f v) { __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p)); }
+
+// Steering of the rows m < M_steer whose request strength a = alpha[r] is
+// nonzero (fp16 rows of H values, fp32 arithmetic, one rounding):
+//   add      : dst[m, :] = src[m, :] + (a * resid_norm) * dir
+//   project  : dst[m, :] = src[m, :] + (a * (src[m, :] . dir)) * dir
+// In place (OOP false, src == dst) rows with a == 0 are not touched at all;
+// out of place they and the rows m >= M_steer are copied unchanged.
+template <int NV, bool PROJ, bool OOP>
+__global__ __launch_bounds__(256) void steer_kernel(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd,
+                                                    int M, int M_steer, int H, RowMap map,
                                                     const float* __restrict__ alpha, float resid_norm,
                                                     const float* __restrict__ dir) {
   const int lane = threadIdx.x & 63;
@@ -47,14 +63,24 @@ __global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, in
     }
   }
   for (; m < M; m += stride) {
-    const float a = alpha[req_of(map, (uint32_t)m)];
-    if (a == 0.0f) continue;  // exact no-op: no write at all (uniform over the wave)
-    uint16_t* row = h + (int64_t)m * ldh;
+    const float a = m < M_steer ? alpha[req_of(map, (uint32_t)m)] : 0.0f;
+    const uint16_t* srow = src + (int64_t)m * lds;
+    uint16_t* drow = dst + (int64_t)m * ldd;
+    if (a == 0.0f) {  // exact no-op (uniform over the wave)
+      if constexpr (OOP) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int e = (lane + WAVE * j) * 8;
+          if (e < H) st16_nt(drow + e, ld16_nt(srow + e));
+        }
+      }
+      continue;
+    }
     v4i raw[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = (lane + WAVE * j) * 8;
-      raw[j] = e < H ? ld16_nt(row + e) : v4i{0, 0, 0, 0};
+      raw[j] = e < H ? ld16_nt(srow + e) : v4i{0, 0, 0, 0};
     }
     float coef = a * resid_norm;
     if constexpr (PROJ) {
@@ -74,24 +100,65 @@ __global__ __launch_bounds__(256) void steer_kernel(uint16_t* __restrict__ h, in
         uint16_t* hv = reinterpret_cast<uint16_t*>(&raw[j]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = f2h(h2f(hv[i]) + coef * dv[j][i]);
-        st16_nt(row + e, raw[j]);
+        st16_nt(drow + e, raw[j]);
       }
     }
   }
 }
 
-__device__ __forceinline__ void load4h_nt(const uint16_t* p, float f[4]) {
-  const v2i r = ld8_nt(p);
+// Steering of the fp32 latent fed to the model (the latent site): one wave
+// per token, a lane holds 4 consecutive channels per 256-channel slice;
+//   add     : xs[t, :] = x[t, :] + (a * resid_norm) * dir
+//   project : xs[t, :] = x[t, :] + (a * (x[t, :] . dir)) * dir
+// as one fp32 FMA per value; tokens with a == 0 are copied unchanged.
+template <int NV, bool PROJ>
+__global__ __launch_bounds__(256) void steer_latent_kernel(const float* __restrict__ x, float* __restrict__ xs,
+                                                           uint32_t n_tok, int C, RowMap map,
+                                                           const float* __restrict__ alpha, float resid_norm,
+                                                           const float* __restrict__ dir) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t stride = gridDim.x * 4u;
+  uint32_t t = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (t >= n_tok) return;
+  v4f dv[NV];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    f[2 * i] = h2f((uint16_t)((uint32_t)r[i] & 0xFFFFu));
-    f[2 * i + 1] = h2f((uint16_t)((uint32_t)r[i] >> 16));
+  for (int j = 0; j < NV; ++j) {
+    const int e = (lane + WAVE * j) * 4;
+    dv[j] = e < C ? *reinterpret_cast<const v4f*>(dir + e) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (; t < n_tok; t += stride) {
+    const float a = alpha[req_of(map, t)];
+    const float* row = x + (int64_t)t * C;
+    float* orow = xs + (int64_t)t * C;
+    v4f v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 4;
+      v[j] = e < C ? ld4f_nt(row + e) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if (a != 0.0f) {  // uniform over the wave
+      float coef = a * resid_norm;
+      if constexpr (PROJ) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dot = fmaf(v[j][i], dv[j][i], dot);
+        coef = a * wave_sum(dot);
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[j][i] = fmaf(coef, dv[j][i], v[j][i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 4;
+      if (e < C) st4f_nt(orow + e, v[j]);
+    }
   }
 }
-__device__ __forceinline__ v4f ld4f_nt(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
-}
-__device__ __forceinline__ void st4f_nt(float* p, v4f v) { __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p)); }
+
 
 // this thread's vector: token and column (false past the end)
 __device__ __forceinline__ bool lat_vec(uint32_t n_tok, int C, uint32_t& tok, int& c) {
@@ -325,24 +392,55 @@ void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* 
 static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 static inline dim3 grid_lat(int64_t n_tok, int C) { return grid_for(n_tok * (C / 4)); }
 
-template <bool PROJ>
-static void launch_steer_mode(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha,
-                              float resid_norm, const float* dir, hipStream_t st) {
+template <bool PROJ, bool OOP>
+static void launch_steer_mode(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int M, int M_steer,
+                              int H, RowMap map, const float* alpha, float resid_norm, const float* dir,
+                              hipStream_t st) {
   dim3 grid((unsigned)std::min<int64_t>((M + 3) / 4, 2048)), block(256);
   const int nv = (H + 511) / 512;
-  if (nv <= 1) hipLaunchKernelGGL((steer_kernel<1, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 2) hipLaunchKernelGGL((steer_kernel<2, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 3) hipLaunchKernelGGL((steer_kernel<3, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 4) hipLaunchKernelGGL((steer_kernel<4, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else if (nv <= 8) hipLaunchKernelGGL((steer_kernel<8, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
-  else hipLaunchKernelGGL((steer_kernel<16, PROJ>), grid, block, 0, st, h, ldh, M, H, map, alpha, resid_norm, dir);
+#define ALD_STEER(NV)                                                                                          \
+  hipLaunchKernelGGL((steer_kernel<NV, PROJ, OOP>), grid, block, 0, st, src, lds, dst, ldd, M, M_steer, H, map, \
+                     alpha, resid_norm, dir)
+  if (nv <= 1) ALD_STEER(1);
+  else if (nv <= 2) ALD_STEER(2);
+  else if (nv <= 3) ALD_STEER(3);
+  else if (nv <= 4) ALD_STEER(4);
+  else if (nv <= 8) ALD_STEER(8);
+  else ALD_STEER(16);
+#undef ALD_STEER
 }
 
 void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
                   const float* dir, int project, hipStream_t st) {
   if (M <= 0 || H <= 0) return;
-  if (project) launch_steer_mode<true>(h, ldh, M, H, map, alpha, resid_norm, dir, st);
-  else launch_steer_mode<false>(h, ldh, M, H, map, alpha, resid_norm, dir, st);
+  if (project) launch_steer_mode<true, false>(h, ldh, h, ldh, M, M, H, map, alpha, resid_norm, dir, st);
+  else launch_steer_mode<false, false>(h, ldh, h, ldh, M, M, H, map, alpha, resid_norm, dir, st);
+}
+
+void launch_steer_copy(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int M, int M_steer, int H,
+                       RowMap map, const float* alpha, float resid_norm, const float* dir, int project,
+                       hipStream_t st) {
+  if (M <= 0 || H <= 0) return;
+  if (project) launch_steer_mode<true, true>(src, lds, dst, ldd, M, M_steer, H, map, alpha, resid_norm, dir, st);
+  else launch_steer_mode<false, true>(src, lds, dst, ldd, M, M_steer, H, map, alpha, resid_norm, dir, st);
+}
+
+void launch_steer_latent(const float* x, float* xs, int64_t n_tok, int C, RowMap map, const float* alpha,
+                         float resid_norm, const float* dir, int project, hipStream_t st) {
+  if (n_tok <= 0 || C <= 0) return;
+  dim3 grid((unsigned)std::min<int64_t>((n_tok + 3) / 4, 2048)), block(256);
+  const bool two = C > 256;
+#define ALD_STEER_LAT(NV, P)                                                                                   \
+  hipLaunchKernelGGL((steer_latent_kernel<NV, P>), grid, block, 0, st, x, xs, (uint32_t)n_tok, C, map, alpha,   \
+                     resid_norm, dir)
+  if (project) {
+    if (two) ALD_STEER_LAT(2, true);
+    else ALD_STEER_LAT(1, true);
+  } else {
+    if (two) ALD_STEER_LAT(2, false);
+    else ALD_STEER_LAT(1, false);
+  }
+#undef ALD_STEER_LAT
 }
 
 void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,

@@ -69,6 +69,13 @@ void gemm_dma_prepare();
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st);
 
 // project = 0: h += (alpha resid_norm) dir; project = 1: h += (alpha (h . dir)) dir
+// out of place: rows m < M_steer steered into dst, the other rows copied
+void launch_steer_copy(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int M, int M_steer, int H,
+                       RowMap map, const float* alpha, float resid_norm, const float* dir, int project,
+                       hipStream_t st);
+// fp32 latent [n_tok, C] (C % 4 == 0, C <= 512) -> steered copy xs
+void launch_steer_latent(const float* x, float* xs, int64_t n_tok, int C, RowMap map, const float* alpha,
+                         float resid_norm, const float* dir, int project, hipStream_t st);
 void launch_steer(uint16_t* h, int64_t ldh, int M, int H, RowMap map, const float* alpha, float resid_norm,
                   const float* dir, int project, hipStream_t st);
 void launch_cfg_merge(const uint16_t* v, int64_t n_tok, int C, RowMap map, const float* w, float* v_hat,

@@ -70,7 +70,7 @@ class DiTModel:
         cfg = self.cfg
         self.c_cfg = L.dit_config(cfg.n_blocks, cfg.hidden, cfg.n_heads, cfg.hidden // cfg.n_heads, cfg.mlp,
                                   cfg.channels, cfg.text_tokens, cfg.text_dim, self.wmode, cfg.steer_block,
-                                  cfg.ln_eps, L.STEER_MODES[cfg.steer_mode])
+                                  cfg.ln_eps, L.STEER_MODES[cfg.steer_mode], L.STEER_SITES[cfg.steer_site])
         arr = (L.dit_block_weights * max(1, cfg.n_blocks))()
         for i, d in enumerate(self.blocks):
             bw = arr[i]
@@ -86,9 +86,13 @@ class DiTModel:
 
     def with_steer_block(self, steer_block: int) -> "DiTModel":
         """Same weights, another steered block (-1: none)."""
+        return self.with_steering(steer_block=steer_block)
+
+    def with_steering(self, **kw) -> "DiTModel":
+        """Same weights, other steering settings (steer_block, steer_mode, steer_site)."""
         other = object.__new__(DiTModel)
         other.__dict__.update(self.__dict__)
-        other.cfg = self.cfg.replace(steer_block=steer_block)
+        other.cfg = self.cfg.replace(**kw)
         other._build_structs()
         return other
 
@@ -189,6 +193,7 @@ class StepRunner:
         a.eps = None if self.renoise is None else self.eps.data_ptr()
         a.v_out = None if self.v_out is None else self.v_out.data_ptr()
         a.block_norms = None if self.block_norms is None else self.block_norms.data_ptr()
+        a.text = self.text.data_ptr()
         return a
 
     def collect_block_norms(self, enable: bool = True):

@@ -228,7 +228,13 @@ def kernel_rooflines():
     tn = torch.full((1,), 0.875, device="cuda")
     ms = _timed(lambda: B.sampler_update(L.ALD_EULER, xs, tc, tn, v_hat=vh, rows_per_req=n_tok))
     out["sampler_euler"] = _entry("hbm", ms, 12.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
-    del xs, vh
+    # latent-site steering: a steered fp32 copy of the latent (4 B read + 4 B written per value)
+    dl = torch.randn(C, device="cuda", generator=g)
+    dl /= dl.norm()
+    xl = torch.empty_like(xs)
+    ms = _timed(lambda: B.steer_latent(xs, alpha, 1.0, dl, rows_per_req=n_tok, out=xl))
+    out["steer_latent"] = _entry("hbm", ms, 8.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
+    del xs, vh, xl
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out

@@ -70,6 +70,10 @@ enum { ALD_EULER = 0, ALD_RENOISE = 1 };
 /* steer_add modes (aria, Section III: add the direction, or project onto it). */
 enum { ALD_STEER_ADD = 0, ALD_STEER_PROJECT = 1 };
 
+/* Steering sites of the step (aria, Section III: the residual stream at a
+ * block's output, the compact audio latent, the text conditioning). */
+enum { ALD_SITE_RESIDUAL = 0, ALD_SITE_LATENT = 1, ALD_SITE_TEXT = 2 };
+
 const char* ald_strerror(int code);
 int ald_version(void);
 
@@ -202,10 +206,21 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * resid_norm is ignored).  alpha [R] fp32 is read on the device at execution
  * time (a captured graph picks up new values without re-capture).  Rows with
  * a == 0 are not written at all, so the result is bit-identical to not
- * calling.  dir [H] fp32 unit direction.  H % 8 == 0. */
+ * calling.  dir [H] fp32 unit direction.  H % 8 == 0, H <= 8192. */
 int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R,
               const int32_t* row_req, const float* alpha, float resid_norm,
               const float* dir, int mode, hipStream_t stream);
+
+/* Latent-site steering (aria, Section III: the compact audio latent is an
+ * injection site): x_out = x + (a * resid_norm) * dir (ALD_STEER_ADD) or
+ * x + (a * (x . dir)) * dir (ALD_STEER_PROJECT) per token, one fp32 FMA per
+ * value, with a = alpha[r] and r = row_req ? row_req[i] : (i / rows_per_req) % R.
+ * Tokens with a == 0 are copied unchanged.  x, x_out fp32 [n_tok, C]
+ * (distinct), dir [C] fp32; C % 4 == 0, C <= 512; 16-byte aligned.  The step
+ * feeds x_out to the model and keeps x as the sampler state. */
+int steer_latent(const float* x, float* x_out, int64_t n_tok, int C, int rows_per_req, int R,
+                 const int32_t* row_req, const float* alpha, float resid_norm,
+                 const float* dir, int mode, hipStream_t stream);
 
 /* CFG merge (vLLM audio pipeline page, Section 2.4, Eq. (1)) on the model
  * velocity: v [2 * n_tok, C] fp16 holds the cond rows [0, n_tok) then the
@@ -247,9 +262,11 @@ typedef struct {
   int text_tokens;   /* T                              */
   int text_dim;      /* D_t                            */
   int wmode;         /* ALD_W8A8 | ALD_F16 | ALD_Q4 | ALD_W8A16 */
-  int steer_block;   /* block whose output is steered; -1: none */
+  int steer_block;   /* block whose output is steered (residual site);
+                        -1: no steering at any site */
   float ln_eps;
   int steer_mode;    /* ALD_STEER_ADD | ALD_STEER_PROJECT */
+  int steer_site;    /* ALD_SITE_RESIDUAL | ALD_SITE_LATENT | ALD_SITE_TEXT */
 } dit_config;
 
 /* One linear layer's weights in the precision of dit_config.wmode:
@@ -302,7 +319,8 @@ typedef struct {
   const float* guidance;      /* CFG weight w per request                       */
   const float* alpha;         /* steering strength per request for this step    */
   float resid_norm;           /* ||h_bar|| of the steered block (host)          */
-  const float* direction;     /* fp32 [H] unit steering direction               */
+  const float* direction;     /* fp32 unit steering direction: [H] residual site,
+                                 [C] latent site, [D_t] text site               */
   const uint8_t* active;      /* uint8 [R]: requests whose latent is updated, or NULL (all) */
   const uint8_t* renoise;     /* uint8 [R]: requests re-noised at t_cur before the pass, or NULL */
   const float* x0;            /* fp32 [n_tok, C] cached clean latent (renoise)  */
@@ -310,6 +328,8 @@ typedef struct {
   uint16_t* v_out;            /* optional fp16 [2 n_tok, C]: model velocity     */
   float* block_norms;         /* optional fp32 [2 n_tok]: per-row L2 norm of the
                                  steered block's output before steering         */
+  const uint16_t* text;       /* fp16 [2R * T, D_t] text conditioning as given to
+                                 dit_text_kv; read by the text site only         */
 } dit_step_args;
 
 /* Workspace bytes needed by dit_step / dit_text_kv for up to max_tokens
@@ -324,9 +344,17 @@ int dit_text_kv(const dit_config* cfg, const dit_weights* w,
                 size_t ws_bytes, hipStream_t stream);
 
 /* One denoising step: input projection + time embedding, n_blocks DiT
- * blocks (steering add after block steer_block), final LayerNorm + output
- * projection, CFG merge, Euler update (with optional warm-start re-noise
- * first).  Enqueues only; capturable. */
+ * blocks, final LayerNorm + output projection, CFG merge, Euler update (with
+ * optional warm-start re-noise first).  Steering (when steer_block >= 0), at
+ * steer_site with operation steer_mode and strength alpha[r]:
+ *   ALD_SITE_RESIDUAL: every row of request r after block steer_block;
+ *   ALD_SITE_LATENT  : the latent fed to the input projection (steer_latent;
+ *                      the sampler state x itself is not shifted); C <= 512;
+ *   ALD_SITE_TEXT    : the cond text rows of request r (the null-prompt rows
+ *                      are left alone), after which every block's text K/V is
+ *                      recomputed from the steered text inside the step
+ *                      (args->text required; args->text_kv is then unused).
+ * Enqueues only; capturable. */
 int dit_step(const dit_config* cfg, const dit_weights* w,
              const dit_step_args* args, void* ws, size_t ws_bytes,
              hipStream_t stream);

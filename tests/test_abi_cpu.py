@@ -77,6 +77,12 @@ def test_attention_and_elementwise_validation():
                         None) == L.ALD_E_INVALID
     assert lib.steer_add(FAKE, 64, 4, 64, 4, 1, None, FAKE, 1.0, FAKE, 9, None) == L.ALD_E_INVALID
     assert lib.steer_add(FAKE, 64, 4, 64, 0, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_INVALID
+    assert lib.steer_add(FAKE, 16384, 4, 16384, 1, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_UNSUPPORTED
+    assert lib.steer_latent(FAKE, FAKE, 8, 64, 8, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_INVALID  # in place
+    assert lib.steer_latent(FAKE, FAKE + 4096, 8, 1024, 8, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_UNSUPPORTED
+    assert lib.steer_latent(FAKE, FAKE + 4096, 8, 62, 8, 1, None, FAKE, 1.0, FAKE, 0, None) == L.ALD_E_INVALID
+    assert lib.steer_latent(FAKE, FAKE + 4096, 8, 64, 8, 1, None, FAKE, 1.0, FAKE, 2, None) == L.ALD_E_INVALID
+    assert lib.steer_latent(None, None, 0, 64, 8, 1, None, None, 1.0, None, 0, None) == L.ALD_OK
     assert lib.cfg_merge(FAKE, 10, 64, 0, None, FAKE, FAKE, None) == L.ALD_E_INVALID
     assert lib.sampler_update(5, FAKE, FAKE, None, None, 10, 64, 10, None, FAKE, FAKE, None, None) == L.ALD_E_INVALID
     assert lib.sampler_update(L.ALD_RENOISE, FAKE, None, None, FAKE, 10, 64, 10, None, FAKE, None, None,
@@ -90,7 +96,8 @@ def test_attention_and_elementwise_validation():
 
 def _cfg(**kw):
     d = dict(n_blocks=2, hidden=256, n_heads=4, head_dim=64, mlp=1024, channels=64, text_tokens=32, text_dim=256,
-             wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5, steer_mode=L.ALD_STEER_ADD)
+             wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5, steer_mode=L.ALD_STEER_ADD,
+             steer_site=L.ALD_SITE_RESIDUAL)
     d.update(kw)
     return L.dit_config(**d)
 
@@ -131,6 +138,17 @@ def test_step_validation():
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_UNSUPPORTED
     bad = _cfg(steer_mode=7)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    bad = _cfg(steer_site=3)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    # the text site reads the raw text, which these args do not give
+    txt = _cfg(steer_site=L.ALD_SITE_TEXT)
+    need_t = lib.dit_workspace_size(ctypes.byref(txt), 64, 1)
+    assert need_t > need  # steered text, its codes and one block's K/V
+    assert lib.dit_step(ctypes.byref(txt), ctypes.byref(w), ctypes.byref(a), FAKE, need_t, None) == L.ALD_E_INVALID
+    lat = _cfg(steer_site=L.ALD_SITE_LATENT)
+    assert lib.dit_workspace_size(ctypes.byref(lat), 64, 1) == need + 64 * 64 * 4
+    assert lib.dit_step(ctypes.byref(lat), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_WORKSPACE
+    assert lib.dit_workspace_size(ctypes.byref(_cfg(steer_site=L.ALD_SITE_LATENT, steer_block=-1)), 64, 1) == need
     bad = _cfg(steer_block=2)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     bad = _cfg(wmode=7)

@@ -337,6 +337,37 @@ def test_steer_project(H):
     assert got[untouched].tobytes() == h[untouched].tobytes()
 
 
+@pytest.mark.parametrize("C,mode", [(64, L.ALD_STEER_ADD), (64, L.ALD_STEER_PROJECT), (200, L.ALD_STEER_ADD),
+                                    (512, L.ALD_STEER_PROJECT)])
+def test_steer_latent(C, mode):
+    """Latent-site steering: a steered fp32 copy of the latent; tokens of a
+    zero-strength request are copied bit for bit, the others agree with the
+    oracle after the fp16 rounding the model input gets (one fp32 FMA per
+    value before it, so at most one fp16 step apart)."""
+    r = rng(10 + C)
+    lens = np.array([37, 0, 300, 129])
+    n, R = int(lens.sum()), len(lens)
+    x = r.standard_normal((n, C)).astype(np.float32)
+    d = r.standard_normal(C)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    alpha = np.array([0.5, 0.25, 0.0, -1.5], np.float32)
+    row_req = np.repeat(np.arange(R), lens).astype(np.int32)
+    got = host(B.steer_latent(dev(x), dev(alpha), 7.5, dev(d), row_req=dev(row_req), mode=mode))
+    mname = "project" if mode == L.ALD_STEER_PROJECT else "add"
+    ref = O.steer_latent(x, alpha[row_req], 7.5, d, mode=mname)
+    zero = alpha[row_req] == 0
+    assert got[zero].tobytes() == x[zero].tobytes()
+    g16 = got.astype(np.float16).astype(np.float64)
+    r16 = ref.astype(np.float64)
+    ulp = np.spacing(np.abs(ref)).astype(np.float64)
+    assert np.all(np.abs(g16 - r16) <= ulp * 1.0001 + 2.0 ** -24)
+    # dense mapping (rows_per_req) gives the same result as the explicit map
+    dense = host(B.steer_latent(dev(x[:300]), dev(alpha[:3]), 7.5, dev(d), rows_per_req=100, R=3, mode=mode))
+    assert dense.tobytes() == host(B.steer_latent(dev(x[:300]), dev(alpha[:3]), 7.5, dev(d),
+                                                  row_req=dev((np.arange(300) // 100).astype(np.int32)),
+                                                  mode=mode)).tobytes()
+
+
 def test_cfg_merge_and_sampler():
     r = rng(9)
     R, S, C = 3, 50, 64

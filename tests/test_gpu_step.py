@@ -76,6 +76,81 @@ def test_tiny_step_projection_steering():
     assert host(a.x).tobytes() == host(b.x).tobytes()
 
 
+@pytest.mark.parametrize("site,mode,wmode", [("latent", "add", "w8a8"), ("latent", "project", "w8a8"),
+                                             ("text", "add", "w8a8"), ("text", "project", "w8a8"),
+                                             ("text", "add", "f16"), ("latent", "add", "w8a16")])
+def test_tiny_step_other_sites(site, mode, wmode):
+    """Steering at the latent (model input) and text-conditioning sites.
+
+    One steered step against the oracle (latent and velocity), and the
+    steering's own effect on the velocity (steered minus unsteered, on each
+    side) against the oracle's, so a path that dropped the steering would
+    fail even where the effect is below the step bar; strength 0 is
+    bit-identical to the unsteered pass."""
+    cfg = I.TINY.replace(steer_site=site, steer_mode=mode, wmode=wmode)
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    # a projection only scales the text's small component along d: a larger
+    # strength makes its effect measurable
+    inp.alpha[0] = 8.0 if (site, mode) == ("text", "project") else 2.0
+    om = O.prepare_model(cfg, p)
+    om_off = O.prepare_model(cfg.replace(steer_block=-1), p)
+    # the site's own norm unit: mean token norm of the latent or of the cond text
+    resid = O.mean_row_norm(inp.x.astype(np.float16)) if site == "latent" else \
+        O.mean_row_norm(inp.text[:cfg.requests].reshape(-1, cfg.text_dim))
+    model = runtime.DiTModel(cfg, p)
+    run = _runner(model, inp, resid=resid, keep_velocity=True)
+    run.step(0)
+    off = _runner(model.with_steer_block(-1), inp, resid=resid, keep_velocity=True)
+    off.step(0)
+    ref, tr = _oracle_steps(om, inp, [0], resid=resid)
+    _, tr_off = _oracle_steps(om_off, inp, [0], resid=resid)
+    err = O.normwise_rel_err(host(run.x), ref)
+    vg, vo = host(run.v_out).astype(np.float64), tr[0].v.astype(np.float64)
+    verr = O.normwise_rel_err(vg, vo)
+    d_gpu = vg - host(off.v_out).astype(np.float64)
+    d_ref = vo - tr_off[0].v.astype(np.float64)
+    derr = O.normwise_rel_err(d_gpu, d_ref)
+    print(f"tiny {site} {mode} {wmode}: latent err {err:.2e}, velocity err {verr:.2e}, "
+          f"steering effect {O.normwise_rel_err(tr_off[0].v, vo):.2e}, effect err {derr:.2e}")
+    assert err < TOL
+    assert verr < 5e-2
+    assert derr < 0.25
+    inp.alpha[:] = 0
+    a = _runner(model, inp, resid=resid)
+    a.step(0)
+    b = _runner(model.with_steer_block(-1), inp)
+    b.step(0)
+    assert host(a.x).tobytes() == host(b.x).tobytes()
+
+
+def test_text_site_graph_equals_eager(tiny):
+    """The text site recomputes the text K/V inside every step: an 8-step
+    graph replay equals eager execution bit for bit, before and after new
+    strengths are written into device memory."""
+    cfg, p, model, om = tiny
+    cfg8 = cfg.replace(steer_site="text", steer_steps=(2, 3, 4, 5))
+    inp = I.make_inputs(cfg8)
+    mt = model.with_steering(steer_site="text")
+    eager = _runner(mt, inp)
+    for i in range(8):
+        eager.step(i)
+    g = _runner(mt, inp)
+    g.capture()
+    g.replay()
+    assert host(g.x).tobytes() == host(eager.x).tobytes()
+    g.x.copy_(torch.from_numpy(inp.x).cuda())
+    new_alpha = np.zeros_like(inp.alpha)
+    new_alpha[5:8] = -0.3
+    g.alpha.copy_(torch.from_numpy(new_alpha).cuda())
+    g.replay()
+    inp.alpha = new_alpha
+    e2 = _runner(mt, inp)
+    for i in range(8):
+        e2.step(i)
+    assert host(g.x).tobytes() == host(e2.x).tobytes()
+
+
 def test_alpha_zero_bit_identical(tiny):
     cfg, p, model, _ = tiny
     inp = I.make_inputs(cfg)
