@@ -53,6 +53,10 @@ class DiTConfig:
     ln_eps: float = 1e-5
     steer_mode: str = "add"  # "add" (alpha, residual-norm units) | "project" (beta)
     steer_site: str = "residual"  # "residual" (block output) | "latent" (model input) | "text"
+    sampler: str = "flow"   # "flow" (velocity, Euler on t) | "ddim" (epsilon, DDIM on alpha_bar)
+    train_steps: int = 1000  # DDIM: training timesteps T of the noise schedule
+    beta_1: float = 1e-4     # DDIM: betas linear from beta_1 to beta_T
+    beta_T: float = 0.02
 
     @property
     def steer_dim(self) -> int:
@@ -80,8 +84,11 @@ MID = DiTConfig("mid", 16, 1024, 16, 4096, 256, 64, 128, 768, 1, 3.0, 8, 12, 0.5
 SERVE = DiTConfig("serve", 24, 1536, 24, 6144, 512, 64, 128, 768, 8, 3.0, 8, 12, 0.0, (), "w8a8", 2)
 Q4 = DiTConfig("q4", 24, 2048, 32, 8192, 1024, 64, 256, 1024, 4, 3.0, 8, 12, 0.0, (), "q4", 3)
 MIXED = DiTConfig("mixed", 16, 1024, 16, 4096, 576, 64, 128, 768, 32, 3.0, 16, 12, 0.5, (), "w8a8", 4)
+# the DDIM backbone of the warm-start serving pages: 200 steps on a linear-beta schedule
+TINY_DDIM = TINY.replace(name="tiny_ddim", n_steps=200, sampler="ddim", seed=5)
+MID_DDIM = MID.replace(name="mid_ddim", n_steps=200, sampler="ddim", steer_steps=tuple(range(40, 80)), seed=6)
 
-CONFIGS: Dict[str, DiTConfig] = {c.name: c for c in (TINY, MID, SERVE, Q4, MIXED)}
+CONFIGS: Dict[str, DiTConfig] = {c.name: c for c in (TINY, MID, SERVE, Q4, MIXED, TINY_DDIM, MID_DDIM)}
 
 LINEARS = ("qkv", "o", "q", "kv", "ox", "up", "down")
 
@@ -185,6 +192,7 @@ class StepInputs:
     start_step: np.ndarray
     x0: Optional[np.ndarray] = None
     eps: Optional[np.ndarray] = None
+    timesteps: Optional[np.ndarray] = None  # DDIM: int [N] descending training timesteps
 
 
 def t_grid(n_steps: int) -> np.ndarray:
@@ -208,10 +216,44 @@ def make_inputs(cfg: DiTConfig, seqlens: Optional[np.ndarray] = None) -> StepInp
     for s in cfg.steer_steps:
         if 0 <= s < N:
             alpha[s, :] = cfg.steer_alpha
+    tg, ts = t_grid(N), None
+    if cfg.sampler == "ddim":
+        ts = ddim_timesteps(N, cfg.train_steps)
+        tg = np.concatenate([ts / cfg.train_steps, [0.0]]).astype(np.float32)
     return StepInputs(x=x, text=text, seqlens=seqlens,
                       guidance=np.full(R, cfg.guidance, dtype=np.float32),
-                      direction=direction, t_grid=t_grid(N), alpha=alpha,
-                      start_step=np.zeros(R, dtype=np.int64))
+                      direction=direction, t_grid=tg, alpha=alpha,
+                      start_step=np.zeros(R, dtype=np.int64), timesteps=ts)
+
+
+def ddim_timesteps(n_steps: int, train_steps: int) -> np.ndarray:
+    """DDIM grid of N evenly spaced training timesteps, descending:
+    (N - 1 - i) * (T / N) for i = 0..N-1 (T a multiple of N); the time
+    embedding of grid point i takes t = timesteps[i] / T."""
+    assert train_steps % n_steps == 0
+    return ((n_steps - 1 - np.arange(n_steps)) * (train_steps // n_steps)).astype(np.int64)
+
+
+SKIP_ARMS = tuple(range(0, 70, 5))  # warm-start skip percentages 0 %, 5 %, ..., 65 %
+
+
+def make_ddim_warm_inputs(cfg: DiTConfig, arms_pct: np.ndarray,
+                          seqlens: Optional[np.ndarray] = None) -> StepInputs:
+    """DDIM requests warm-started at percentage-granular skip arms: request r
+    skips k_r = arms_pct[r] * N / 100 steps (N a multiple of 20, so every arm
+    is a whole step), is re-noised at grid point k_r from a seeded stand-in
+    for a cached clean latent and runs steps k_r..N-1; arm 0 is a cold start."""
+    arms_pct = np.asarray(arms_pct, np.int64)
+    assert cfg.sampler == "ddim" and cfg.n_steps % 20 == 0
+    assert np.all(np.isin(arms_pct, SKIP_ARMS))
+    R = len(arms_pct)
+    base = make_inputs(cfg.replace(requests=R), seqlens=seqlens)
+    st = _streams(cfg.seed)
+    tot = int(np.asarray(base.seqlens).sum())
+    base.start_step = arms_pct * cfg.n_steps // 100
+    base.x0 = st[_S_EXTRA].standard_normal((tot, cfg.channels), dtype=np.float32)
+    base.eps = st[_S_NOISE].standard_normal((tot, cfg.channels), dtype=np.float32)
+    return base
 
 
 def make_mixed_inputs(cfg: DiTConfig, requests: Optional[int] = None,

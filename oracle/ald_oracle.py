@@ -380,6 +380,45 @@ def renoise(x0, eps, t) -> np.ndarray:
     return ((F32(1.0) - t) * np.asarray(x0, F32) + t * np.asarray(eps, F32)).astype(F32)
 
 
+def ddpm_alpha_bar(T: int, beta_1: float, beta_T: float) -> np.ndarray:
+    """Cumulative signal fraction of a diffusion noise schedule with betas
+    linear from beta_1 to beta_T over T training steps (the schedule of the
+    DDPM paper; the pages name the DDIM sampler but not its schedule):
+    alpha_bar[t] = prod_{s <= t} (1 - beta_s), t = 0..T-1, fp64."""
+    beta = np.linspace(beta_1, beta_T, T, dtype=F64)
+    return np.cumprod(1.0 - beta)
+
+
+def ddim_update(x, eps_hat, abar_cur, abar_next) -> np.ndarray:
+    """Deterministic DDIM step (eta = 0) on an epsilon prediction: first the
+    clean-latent estimate x0 = (x - sqrt(1 - a) eps) / sqrt(a), then the
+    latent at the next grid point sqrt(a') x0 + sqrt(1 - a') eps.  fp64, the
+    new state rounded once to fp32.  a' = 1 (the end of the grid) returns x0."""
+    x = np.asarray(x, F32).astype(F64)
+    e = np.asarray(eps_hat, F32).astype(F64)
+    a = np.asarray(abar_cur, F32).astype(F64)
+    an = np.asarray(abar_next, F32).astype(F64)
+    x0 = (x - np.sqrt(1.0 - a) * e) / np.sqrt(a)
+    return (np.sqrt(an) * x0 + np.sqrt(1.0 - an) * e).astype(F32)
+
+
+def renoise_vp(x0, eps, abar) -> np.ndarray:
+    """Warm start under the DDIM sampler (SoundWeaver, Section 2: a sample of
+    the forward process q(x_t* | x0_hat)): sqrt(a) x0 + sqrt(1 - a) eps at the
+    skip point's alpha_bar a, fp64 rounded to fp32."""
+    a = np.asarray(abar, F32).astype(F64)
+    return (np.sqrt(a) * np.asarray(x0, F32).astype(F64)
+            + np.sqrt(1.0 - a) * np.asarray(eps, F32).astype(F64)).astype(F32)
+
+
+def ddim_alpha_bars(cfg, timesteps) -> np.ndarray:
+    """alpha_bar at each grid point of a DDIM run over the given descending
+    training timesteps, with 1 after the last (so the last step returns the
+    clean estimate), rounded to the fp32 the sampler state uses; [N + 1]."""
+    ab = ddpm_alpha_bar(cfg.train_steps, cfg.beta_1, cfg.beta_T)
+    return np.concatenate([ab[np.asarray(timesteps, np.int64)], [1.0]]).astype(F32)
+
+
 def skip_start_step(p: float, n_steps: int) -> int:
     """Steps skipped for a skip fraction p: k = floor(p * N + 1/2)."""
     return int(math.floor(p * n_steps + 0.5))
@@ -527,9 +566,14 @@ def dit_forward(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv:
 def dit_step(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv: List[np.ndarray],
              t_cur, t_next, guidance, row_alpha_req, resid_norm, direction,
              active: Optional[np.ndarray] = None, keep_blocks: Sequence[int] = (),
-             text16: Optional[np.ndarray] = None):
+             text16: Optional[np.ndarray] = None, abar_cur=None, abar_next=None):
     """One denoising step for all requests: model pass on the CFG pair, merge,
-    Euler update.  Requests whose `active` flag is false keep their latent."""
+    sampler update.  Requests whose `active` flag is false keep their latent.
+    cfg.sampler "flow": the model output is a velocity and the update the
+    flow-matching Euler step from t_cur to t_next; "ddim": the model output is
+    an epsilon prediction (reading) and the update the DDIM step from
+    abar_cur to abar_next (per request), t_cur feeding only the time
+    embedding."""
     R = len(seqlens)
     seqlens = np.asarray(seqlens, dtype=np.int64)
     Ntot = int(seqlens.sum())
@@ -538,9 +582,13 @@ def dit_step(model: PreparedModel, x: np.ndarray, seqlens: Sequence[int], kv: Li
     req = np.repeat(np.arange(R), seqlens)
     w = np.asarray(guidance, F32)[req][:, None]
     v_hat = cfg_merge(v[:Ntot], v[Ntot:], w)
-    tc = np.asarray(t_cur, F32)[req][:, None]
-    tn = np.asarray(t_next, F32)[req][:, None]
-    x_new = euler_update(x, v_hat, tc, tn)
+    if getattr(model.cfg, "sampler", "flow") == "ddim":
+        x_new = ddim_update(x, v_hat, np.asarray(abar_cur, F32)[req][:, None],
+                            np.asarray(abar_next, F32)[req][:, None])
+    else:
+        tc = np.asarray(t_cur, F32)[req][:, None]
+        tn = np.asarray(t_next, F32)[req][:, None]
+        x_new = euler_update(x, v_hat, tc, tn)
     if active is not None:
         keep = ~np.asarray(active, bool)[req]
         x_new[keep] = np.asarray(x, F32)[keep]
@@ -566,6 +614,8 @@ def run_sampler(model: PreparedModel, inp, kv=None, resid_norm: float = 0.0,
     """
     tg = np.asarray(inp.t_grid, F32)
     N = len(tg) - 1
+    ddim = getattr(model.cfg, "sampler", "flow") == "ddim"
+    ab = ddim_alpha_bars(model.cfg, inp.timesteps) if ddim else None
     if kv is None:
         kv = text_kv(model, inp.text)
     x = np.array(inp.x, dtype=F32, copy=True)
@@ -579,12 +629,15 @@ def run_sampler(model: PreparedModel, inp, kv=None, resid_norm: float = 0.0,
             rn = (start == i) & (start > 0)
             if rn.any():
                 rows = rn[req]
-                x[rows] = renoise(inp.x0[rows], inp.eps[rows], tg[i])
+                x[rows] = (renoise_vp(inp.x0[rows], inp.eps[rows], ab[i]) if ddim
+                           else renoise(inp.x0[rows], inp.eps[rows], tg[i]))
         active = start <= i
         t_cur = np.full(R, tg[i], F32)
         t_next = np.full(R, tg[i + 1], F32)
         x, tr = dit_step(model, x, inp.seqlens, kv, t_cur, t_next, inp.guidance, alpha[i],
-                         resid_norm, inp.direction, active, keep_blocks, inp.text)
+                         resid_norm, inp.direction, active, keep_blocks, inp.text,
+                         None if ab is None else np.full(R, ab[i], F32),
+                         None if ab is None else np.full(R, ab[i + 1], F32))
         traces.append(tr)
     return x, traces
 

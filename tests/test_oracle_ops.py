@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import ald_inputs as I
 from oracle import ald_oracle as O
 
 
@@ -286,6 +287,72 @@ def test_renoise_endpoints_and_path():
     for i in range(k, N):
         x = O.euler_update(x, eps - x0, tg[i], tg[i + 1])
     assert np.allclose(x, x0, atol=1e-5)
+
+
+# ---------------------------------------------------------------- DDIM sampler
+
+def test_ddpm_alpha_bar_closed_forms():
+    T, b1, bT = 1000, 1e-4, 0.02
+    ab = O.ddpm_alpha_bar(T, b1, bT)
+    assert ab.shape == (T,)
+    assert ab[0] == pytest.approx(1 - b1, rel=1e-15)
+    db = (bT - b1) / (T - 1)
+    assert ab[1] == pytest.approx((1 - b1) * (1 - b1 - db), rel=1e-15)
+    assert ab[T - 1] / ab[T - 2] == pytest.approx(1 - bT, rel=1e-12)   # last beta is beta_T
+    assert np.all(np.diff(ab) < 0) and 0 < ab[-1] < 1e-4              # almost pure noise at T
+
+
+def test_ddim_timesteps_grid():
+    ts = I.ddim_timesteps(200, 1000)
+    assert ts[0] == 995 and ts[-1] == 0 and len(ts) == 200 and np.all(np.diff(ts) == -5)
+    ab = O.ddim_alpha_bars(I.TINY_DDIM, ts)
+    assert ab.shape == (201,) and ab[-1] == 1.0 and np.all(np.diff(ab) > 0)
+
+
+def test_ddim_update_closed_forms():
+    """With the true noise as the prediction, a DDIM step moves the forward
+    sample sqrt(a) x0 + sqrt(1-a) eps to the forward sample at a'; a' = a is
+    the identity; a' = 1 returns the clean estimate."""
+    rng = np.random.default_rng(21)
+    x0 = rng.standard_normal((8, 64))
+    eps = rng.standard_normal((8, 64))
+    a, an = np.float32(0.3), np.float32(0.55)
+    x = (np.sqrt(np.float64(a)) * x0 + np.sqrt(1 - np.float64(a)) * eps).astype(np.float32)
+    e32 = eps.astype(np.float32)
+    got = O.ddim_update(x, e32, a, an).astype(np.float64)
+    want = np.sqrt(np.float64(an)) * x0 + np.sqrt(1 - np.float64(an)) * eps
+    assert np.allclose(got, want, atol=2e-6)
+    assert np.allclose(O.ddim_update(x, e32, a, a), x, rtol=0, atol=1e-6)
+    x0_hat = (x.astype(np.float64) - np.sqrt(1 - np.float64(a)) * e32) / np.sqrt(np.float64(a))
+    assert np.array_equal(O.ddim_update(x, e32, a, np.float32(1.0)), x0_hat.astype(np.float32))
+
+
+def test_ddim_exact_noise_trajectory_recovers_x0():
+    """200 DDIM steps on the linear-beta grid with the prediction fixed to the
+    noise that made the start: the run ends at the clean latent."""
+    rng = np.random.default_rng(22)
+    x0 = rng.standard_normal((4, 64)).astype(np.float32)
+    eps = rng.standard_normal((4, 64)).astype(np.float32)
+    ab = O.ddim_alpha_bars(I.TINY_DDIM, I.ddim_timesteps(200, 1000))
+    x = O.renoise_vp(x0, eps, ab[0])
+    for i in range(200):
+        x = O.ddim_update(x, eps, ab[i], ab[i + 1])
+    assert np.allclose(x, x0, atol=1e-4)
+
+
+def test_renoise_vp_endpoints_and_variance():
+    rng = np.random.default_rng(23)
+    x0 = rng.standard_normal((2000, 64)).astype(np.float32)
+    eps = rng.standard_normal((2000, 64)).astype(np.float32)
+    assert np.array_equal(O.renoise_vp(x0, eps, np.float32(1.0)), x0)
+    assert np.array_equal(O.renoise_vp(x0, eps, np.float32(0.0)), eps)
+    assert np.var(O.renoise_vp(x0, eps, np.float32(0.37))) == pytest.approx(1.0, abs=0.02)
+
+
+def test_skip_arms_are_whole_steps():
+    cfg = I.TINY_DDIM
+    inp = I.make_ddim_warm_inputs(cfg, np.array([0, 5, 35, 65]))
+    assert inp.start_step.tolist() == [0, 10, 70, 130]
 
 
 def test_skip_start_step():

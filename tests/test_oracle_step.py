@@ -182,3 +182,24 @@ def test_resid_norm_calibration_trace(tiny):
                        keep_blocks=[1])
     n = O.mean_row_norm(tr.block_out[1])
     assert np.isfinite(n) and n > 0
+
+
+def test_ddim_step_and_skip_arm_warm_start():
+    """DDIM sampler: a step is the DDIM update of the guided prediction at the
+    grid's alpha_bar; a warm request whose arm skips 10 % waits until step 20
+    and is then re-noised to the forward sample at that grid point."""
+    cfg = I.TINY_DDIM.replace(n_blocks=1)
+    p = I.make_params(cfg)
+    m = O.prepare_model(cfg, p)
+    inp = I.make_ddim_warm_inputs(cfg, np.array([0, 10]), seqlens=np.array([40, 24]))
+    ab = O.ddim_alpha_bars(cfg, inp.timesteps)
+    x, tr = O.run_sampler(m, inp, resid_norm=5.0, steps=[19, 20])
+    n0 = 40
+    # request 1 skipped step 19 (inactive), then at step 20 started from the re-noised latent
+    xr = O.renoise_vp(inp.x0[n0:], inp.eps[n0:], ab[20])
+    assert np.array_equal(x[n0:], O.ddim_update(xr, tr[1].v_hat[n0:], ab[20], ab[21]))
+    # request 0 ran both steps from its own latent
+    x19 = O.ddim_update(inp.x[:n0], tr[0].v_hat[:n0], ab[19], ab[20])
+    assert np.array_equal(x[:n0], O.ddim_update(x19, tr[1].v_hat[:n0], ab[20], ab[21]))
+    # the model input time of grid point i is timesteps[i] / T
+    assert inp.t_grid[20] == np.float32(inp.timesteps[20] / cfg.train_steps)
