@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_float, c_int, c_int64, c_size_t, c_uint, c_void_p
+from ctypes import POINTER, c_double, c_float, c_int, c_int64, c_size_t, c_uint, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libald.so")
@@ -16,7 +16,9 @@ ALD_OK, ALD_E_INVALID, ALD_E_UNSUPPORTED, ALD_E_WORKSPACE, ALD_E_LAUNCH = 0, -1,
 ALD_W8A8, ALD_F16, ALD_Q4, ALD_W8A16 = 0, 1, 2, 3
 ALD_ACT_NONE, ALD_ACT_GELU = 0, 1
 ALD_PREQUANT = 1
-ALD_EULER, ALD_RENOISE = 0, 1
+ALD_EULER, ALD_RENOISE, ALD_DDIM, ALD_RENOISE_VP = 0, 1, 2, 3
+ALD_SAMPLER_FLOW, ALD_SAMPLER_DDIM = 0, 1
+SAMPLERS = {"flow": ALD_SAMPLER_FLOW, "ddim": ALD_SAMPLER_DDIM}
 ALD_STEER_ADD, ALD_STEER_PROJECT = 0, 1
 STEER_MODES = {"add": ALD_STEER_ADD, "project": ALD_STEER_PROJECT}
 ALD_SITE_RESIDUAL, ALD_SITE_LATENT, ALD_SITE_TEXT = 0, 1, 2
@@ -28,7 +30,7 @@ WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4, "w8a16": ALD_W8A16}
 EXPORTS = (
     "ald_strerror", "ald_version", "quantize_rows_q8", "quantize_q4", "ln_quant", "ln_f16",
     "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "steer_latent", "cfg_merge",
-    "sampler_update", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
+    "sampler_update", "ddim_alpha_bar", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
     "dit_graph_launch", "dit_graph_destroy",
 )
 
@@ -43,7 +45,7 @@ class dit_config(ctypes.Structure):
     _fields_ = [("n_blocks", c_int), ("hidden", c_int), ("n_heads", c_int), ("head_dim", c_int),
                 ("mlp", c_int), ("channels", c_int), ("text_tokens", c_int), ("text_dim", c_int),
                 ("wmode", c_int), ("steer_block", c_int), ("ln_eps", c_float), ("steer_mode", c_int),
-                ("steer_site", c_int)]
+                ("steer_site", c_int), ("sampler", c_int)]
 
 
 class dit_linear(ctypes.Structure):
@@ -68,7 +70,8 @@ class dit_step_args(ctypes.Structure):
                 ("t_cur", c_void_p), ("t_next", c_void_p), ("guidance", c_void_p), ("alpha", c_void_p),
                 ("resid_norm", c_float), ("direction", c_void_p), ("active", c_void_p),
                 ("renoise", c_void_p), ("x0", c_void_p), ("eps", c_void_p), ("v_out", c_void_p),
-                ("block_norms", c_void_p), ("text", c_void_p)]
+                ("block_norms", c_void_p), ("text", c_void_p), ("abar_cur", c_void_p),
+                ("abar_next", c_void_p)]
 
 
 _lib = None
@@ -92,6 +95,7 @@ def _declare(lib):
         "steer_latent": (I, [V, V, I64, I, I, I, V, V, F, V, I, V]),
         "cfg_merge": (I, [V, I64, I, I, V, V, V, V]),
         "sampler_update": (I, [I, V, V, V, V, I64, I, I, V, V, V, V, V]),
+        "ddim_alpha_bar": (I, [I, c_double, c_double, V, I, V]),
         "dit_workspace_size": (c_size_t, [POINTER(dit_config), I64, I]),
         "dit_text_kv": (I, [POINTER(dit_config), POINTER(dit_weights), V, I, V, V, c_size_t, V]),
         "dit_step": (I, [POINTER(dit_config), POINTER(dit_weights), POINTER(dit_step_args), V, c_size_t, V]),

@@ -6,8 +6,10 @@ current stream.  Every computation happens inside libald.so.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
+import numpy as np
 import torch
 
 from . import _lib as L
@@ -169,6 +171,16 @@ def cfg_merge(v, w, rows_per_req=1, row_req=None, v_hat=None):
     L.check("cfg_merge", L.lib().cfg_merge(_p(v), n_tok, C, rows_per_req, _p(row_req), _p(w), _p(v_hat),
                                            _stream()))
     return v_hat
+
+
+def ddim_alpha_bar(T, beta_1, beta_T, timesteps):
+    """alpha_bar of the linear-beta schedule at the grid timesteps, then 1 (host, fp32 [n + 1])."""
+    ts = np.ascontiguousarray(np.asarray(timesteps, np.int32))
+    out = np.empty(len(ts) + 1, np.float32)
+    L.check("ddim_alpha_bar", L.lib().ddim_alpha_bar(int(T), float(beta_1), float(beta_T),
+                                                     ts.ctypes.data_as(ctypes.c_void_p), len(ts),
+                                                     out.ctypes.data_as(ctypes.c_void_p)))
+    return out
 
 
 def sampler_update(op, x, t_cur, t_next=None, v_hat=None, x0=None, eps=None, rows_per_req=1, row_req=None,

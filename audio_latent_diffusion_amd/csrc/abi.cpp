@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/ald.h"
 #include "kernels.h"
@@ -131,6 +132,7 @@ int check_config(const dit_config* c) {
   CHECK(c->steer_site == ALD_SITE_RESIDUAL || c->steer_site == ALD_SITE_LATENT || c->steer_site == ALD_SITE_TEXT,
         ALD_E_INVALID);
   if (steers(c, ALD_SITE_LATENT)) CHECK(c->channels <= 512, ALD_E_UNSUPPORTED);
+  CHECK(c->sampler == ALD_SAMPLER_FLOW || c->sampler == ALD_SAMPLER_DDIM, ALD_E_INVALID);
   CHECK(c->ln_eps >= 0.0f, ALD_E_INVALID);
   return ALD_OK;
 }
@@ -227,6 +229,8 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   CHECK(a->R > 0 && a->n_tok > 0, ALD_E_INVALID);
   CHECK(a->x && al16(a->x) && a->text_kv && al16(a->text_kv), ALD_E_INVALID);
   CHECK(a->t_cur && a->t_next && a->guidance, ALD_E_INVALID);
+  const bool ddim = c->sampler == ALD_SAMPLER_DDIM;
+  if (ddim) CHECK(a->abar_cur && a->abar_next, ALD_E_INVALID);
   const bool varlen = a->cu_seqlens != nullptr;
   if (varlen) {
     CHECK(a->row_req && a->max_seq > 0, ALD_E_INVALID);
@@ -262,7 +266,10 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     launch_cu_pairs(a->cu_seqlens, R, n_tok, b.cu2, st);
     cu2 = b.cu2;
   }
-  if (a->renoise) launch_renoise(a->x, a->x0, a->eps, n_tok, C, map, a->t_cur, a->renoise, st);
+  if (a->renoise) {
+    if (ddim) launch_renoise_vp(a->x, a->x0, a->eps, n_tok, C, map, a->abar_cur, a->renoise, st);
+    else launch_renoise(a->x, a->x0, a->eps, n_tok, C, map, a->t_cur, a->renoise, st);
+  }
 
   const bool project = c->steer_mode == ALD_STEER_PROJECT;
   // latent site: the model reads a steered copy of the latent, the state stays
@@ -338,7 +345,8 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     g.epi.ldy = C;
     launch_gemm(A_F16, B_F16, g, st);
   }
-  launch_cfg_euler(v, a->x, n_tok, C, map, a->guidance, a->t_cur, a->t_next, a->active, st);
+  if (ddim) launch_cfg_ddim(v, a->x, n_tok, C, map, a->guidance, a->abar_cur, a->abar_next, a->active, st);
+  else launch_cfg_euler(v, a->x, n_tok, C, map, a->guidance, a->t_cur, a->t_next, a->active, st);
   return launched();
 }
 
@@ -599,21 +607,40 @@ int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req, const i
 int sampler_update(int op, float* x, const float* v_hat, const float* x0, const float* eps, int64_t n_tok, int C,
                    int rows_per_req, const int32_t* row_req, const float* t_cur, const float* t_next,
                    const uint8_t* active, hipStream_t stream) {
-  CHECK(op == ALD_EULER || op == ALD_RENOISE, ALD_E_INVALID);
+  CHECK(op == ALD_EULER || op == ALD_RENOISE || op == ALD_DDIM || op == ALD_RENOISE_VP, ALD_E_INVALID);
   CHECK(n_tok >= 0 && C > 0, ALD_E_INVALID);
   if (n_tok == 0) return ALD_OK;
   CHECK(x && t_cur && al16(x) && C % 4 == 0, ALD_E_INVALID);
   CHECK(n_tok * (C / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
   if (!row_req) CHECK(rows_per_req > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, INT32_MAX, row_req};
-  if (op == ALD_EULER) {
+  if (op == ALD_EULER || op == ALD_DDIM) {
     CHECK(v_hat && t_next && al16(v_hat), ALD_E_INVALID);
-    launch_euler(x, v_hat, n_tok, C, map, t_cur, t_next, active, stream);
+    if (op == ALD_EULER) launch_euler(x, v_hat, n_tok, C, map, t_cur, t_next, active, stream);
+    else launch_ddim(x, v_hat, n_tok, C, map, t_cur, t_next, active, stream);
   } else {
     CHECK(x0 && eps && al16(x0) && al16(eps), ALD_E_INVALID);
-    launch_renoise(x, x0, eps, n_tok, C, map, t_cur, active, stream);
+    if (op == ALD_RENOISE) launch_renoise(x, x0, eps, n_tok, C, map, t_cur, active, stream);
+    else launch_renoise_vp(x, x0, eps, n_tok, C, map, t_cur, active, stream);
   }
   return launched();
+}
+
+int ddim_alpha_bar(int T, double beta_1, double beta_T, const int32_t* timesteps, int n, float* abar_out) {
+  CHECK(T >= 2 && n >= 0 && abar_out && (n == 0 || timesteps), ALD_E_INVALID);
+  CHECK(beta_1 > 0.0 && beta_T > 0.0 && beta_1 < 1.0 && beta_T < 1.0, ALD_E_INVALID);
+  for (int i = 0; i < n; ++i) CHECK(timesteps[i] >= 0 && timesteps[i] < T, ALD_E_INVALID);
+  // the running product, one factor per training step, read at each grid timestep
+  std::vector<double> ab(T);
+  double prod = 1.0;
+  for (int t = 0; t < T; ++t) {
+    const double beta = beta_1 + (beta_T - beta_1) * t / (T - 1);
+    prod *= 1.0 - beta;
+    ab[t] = prod;
+  }
+  for (int i = 0; i < n; ++i) abar_out[i] = (float)ab[timesteps[i]];
+  abar_out[n] = 1.0f;
+  return ALD_OK;
 }
 
 size_t dit_workspace_size(const dit_config* cfg, int64_t max_tokens, int R) {

@@ -1,5 +1,6 @@
-// Bandwidth-bound elementwise kernels: steering add, CFG merge, sampler
-// updates (Euler, warm-start re-noise), their fusion used inside the step,
+// Bandwidth-bound elementwise kernels: steering (residual, text and latent
+// sites), CFG merge, sampler updates (flow-matching Euler and DDIM, with their
+// warm-start re-noise), their fusions used inside the step,
 // per-row L2 norms (steering calibration) and the CFG-pair sequence offsets.
 //
 // Latent kernels: one thread per vector of 4 consecutive latent values,
@@ -249,6 +250,80 @@ __global__ __launch_bounds__(256) void cfg_euler_kernel(const uint16_t* __restri
   st4f_nt(x + o, xv);
 }
 
+// DDIM (eta = 0) on an epsilon prediction, in the method's two steps:
+// x0 = (x - sqrt(1 - a) e) / sqrt(a), x' = sqrt(a') x0 + sqrt(1 - a') e
+struct DdimCoef {
+  float sb, inv_sa, san, sbn;
+};
+__device__ __forceinline__ DdimCoef ddim_coef(float a, float an) {
+  return {sqrtf(1.0f - a), 1.0f / sqrtf(a), sqrtf(an), sqrtf(1.0f - an)};
+}
+__device__ __forceinline__ float ddim_apply(const DdimCoef& k, float x, float e) {
+  const float x0 = (x - k.sb * e) * k.inv_sa;
+  return k.san * x0 + k.sbn * e;
+}
+
+__global__ __launch_bounds__(256) void ddim_kernel(float* __restrict__ x, const float* __restrict__ e_hat,
+                                                   uint32_t n_tok, int C, RowMap map, const float* __restrict__ ab,
+                                                   const float* __restrict__ ab_next,
+                                                   const uint8_t* __restrict__ active) {
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  v4f xv = ld4f_nt(x + o);
+  const v4f ev = ld4f_nt(e_hat + o);
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const DdimCoef k = ddim_coef(ab[r], ab_next[r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xv[i] = ddim_apply(k, xv[i], ev[i]);
+  st4f_nt(x + o, xv);
+}
+
+// warm start under DDIM: x = sqrt(a) x0 + sqrt(1 - a) eps at the skip point
+__global__ __launch_bounds__(256) void renoise_vp_kernel(float* __restrict__ x, const float* __restrict__ x0,
+                                                         const float* __restrict__ eps, uint32_t n_tok, int C,
+                                                         RowMap map, const float* __restrict__ ab,
+                                                         const uint8_t* __restrict__ active) {
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  const v4f av = ld4f_nt(x0 + o);
+  const v4f ev = ld4f_nt(eps + o);
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const float sa = sqrtf(ab[r]), sb = sqrtf(1.0f - ab[r]);
+  v4f out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = sa * av[i] + sb * ev[i];
+  st4f_nt(x + o, out);
+}
+
+// fused CFG merge + DDIM for the step: the guided prediction never touches memory
+__global__ __launch_bounds__(256) void cfg_ddim_kernel(const uint16_t* __restrict__ v, float* __restrict__ x,
+                                                       uint32_t n_tok, int C, RowMap map, const float* __restrict__ w,
+                                                       const float* __restrict__ ab, const float* __restrict__ ab_next,
+                                                       const uint8_t* __restrict__ active) {
+  uint32_t tok;
+  int c;
+  if (!lat_vec(n_tok, C, tok, c)) return;
+  const int64_t o = (int64_t)tok * C + c;
+  float fc[4], fu[4];
+  load4h_nt(v + o, fc);
+  load4h_nt(v + (int64_t)n_tok * C + o, fu);
+  v4f xv = ld4f_nt(x + o);
+  const int r = req_of(map, tok);
+  if (active && !active[r]) return;
+  const float wr = w[r];
+  const float wu = 1.0f - wr;
+  const DdimCoef k = ddim_coef(ab[r], ab_next[r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xv[i] = ddim_apply(k, xv[i], wr * fc[i] + wu * fu[i]);
+  st4f_nt(x + o, xv);
+}
+
 // per-row L2 norm (fp32), one wave per row
 __global__ __launch_bounds__(256) void row_norms_kernel(const uint16_t* __restrict__ h, int64_t ldh, int M, int H,
                                                         float* __restrict__ out) {
@@ -468,6 +543,27 @@ void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap 
   if (n_tok <= 0) return;
   hipLaunchKernelGGL(cfg_euler_kernel, grid_lat(n_tok, C), dim3(256), 0, st, v, x, (uint32_t)n_tok, C, map, w,
                      t_cur, t_next, active);
+}
+
+void launch_ddim(float* x, const float* e_hat, int64_t n_tok, int C, RowMap map, const float* ab,
+                 const float* ab_next, const uint8_t* active, hipStream_t st) {
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(ddim_kernel, grid_lat(n_tok, C), dim3(256), 0, st, x, e_hat, (uint32_t)n_tok, C, map, ab,
+                     ab_next, active);
+}
+
+void launch_renoise_vp(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
+                       const float* ab, const uint8_t* active, hipStream_t st) {
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(renoise_vp_kernel, grid_lat(n_tok, C), dim3(256), 0, st, x, x0, eps, (uint32_t)n_tok, C, map,
+                     ab, active);
+}
+
+void launch_cfg_ddim(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
+                     const float* ab, const float* ab_next, const uint8_t* active, hipStream_t st) {
+  if (n_tok <= 0) return;
+  hipLaunchKernelGGL(cfg_ddim_kernel, grid_lat(n_tok, C), dim3(256), 0, st, v, x, (uint32_t)n_tok, C, map, w, ab,
+                     ab_next, active);
 }
 
 void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st) {

@@ -84,6 +84,14 @@ void launch_euler(float* x, const float* v_hat, int64_t n_tok, int C, RowMap map
                   const float* t_next, const uint8_t* active, hipStream_t st);
 void launch_renoise(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
                     const float* t_cur, const uint8_t* active, hipStream_t st);
+// DDIM on alpha_bar (ab: current grid point, ab_next: the next one), warm-start
+// re-noise sqrt(ab) x0 + sqrt(1 - ab) eps, and the step's fused CFG + DDIM
+void launch_ddim(float* x, const float* e_hat, int64_t n_tok, int C, RowMap map, const float* ab,
+                 const float* ab_next, const uint8_t* active, hipStream_t st);
+void launch_renoise_vp(float* x, const float* x0, const float* eps, int64_t n_tok, int C, RowMap map,
+                       const float* ab, const uint8_t* active, hipStream_t st);
+void launch_cfg_ddim(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
+                     const float* ab, const float* ab_next, const uint8_t* active, hipStream_t st);
 void launch_cfg_euler(const uint16_t* v, float* x, int64_t n_tok, int C, RowMap map, const float* w,
                       const float* t_cur, const float* t_next, const uint8_t* active, hipStream_t st);
 void launch_row_norms(const uint16_t* h, int64_t ldh, int M, int H, float* out, hipStream_t st);

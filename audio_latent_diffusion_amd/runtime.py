@@ -70,7 +70,8 @@ class DiTModel:
         cfg = self.cfg
         self.c_cfg = L.dit_config(cfg.n_blocks, cfg.hidden, cfg.n_heads, cfg.hidden // cfg.n_heads, cfg.mlp,
                                   cfg.channels, cfg.text_tokens, cfg.text_dim, self.wmode, cfg.steer_block,
-                                  cfg.ln_eps, L.STEER_MODES[cfg.steer_mode], L.STEER_SITES[cfg.steer_site])
+                                  cfg.ln_eps, L.STEER_MODES[cfg.steer_mode], L.STEER_SITES[cfg.steer_site],
+                                  L.SAMPLERS[cfg.sampler])
         arr = (L.dit_block_weights * max(1, cfg.n_blocks))()
         for i, d in enumerate(self.blocks):
             bw = arr[i]
@@ -86,10 +87,10 @@ class DiTModel:
 
     def with_steer_block(self, steer_block: int) -> "DiTModel":
         """Same weights, another steered block (-1: none)."""
-        return self.with_steering(steer_block=steer_block)
+        return self.with_config(steer_block=steer_block)
 
-    def with_steering(self, **kw) -> "DiTModel":
-        """Same weights, other steering settings (steer_block, steer_mode, steer_site)."""
+    def with_config(self, **kw) -> "DiTModel":
+        """Same weights, other step settings (steering, sampler, grid size)."""
         other = object.__new__(DiTModel)
         other.__dict__.update(self.__dict__)
         other.cfg = self.cfg.replace(**kw)
@@ -119,13 +120,17 @@ class StepRunner:
 
     Dense requests (all of length `seq`) or packed varlen requests
     (`seqlens`).  Per-step arrays are [n_steps, R] so step i reads row i; the
-    host may rewrite them between graph replays without re-capture.
+    host may rewrite them between graph replays without re-capture.  With the
+    DDIM sampler, `timesteps` (int [N], descending) gives the grid: t_grid
+    then feeds only the time embedding and alpha_bar comes from the model's
+    noise schedule.
     """
 
     def __init__(self, model: DiTModel, x0_latent: np.ndarray, text16: np.ndarray, seqlens: Sequence[int],
                  t_grid: np.ndarray, guidance: np.ndarray, alpha: np.ndarray, direction: np.ndarray,
                  resid_norm: float, start_step: Optional[np.ndarray] = None, x0: Optional[np.ndarray] = None,
-                 eps: Optional[np.ndarray] = None, keep_velocity: bool = False):
+                 eps: Optional[np.ndarray] = None, keep_velocity: bool = False,
+                 timesteps: Optional[np.ndarray] = None):
         cfg = model.cfg
         dev = model.device
         self.model = model
@@ -144,6 +149,13 @@ class StepRunner:
         tg = np.asarray(t_grid, np.float32)
         self.t_cur = _t(np.repeat(tg[:-1, None], R, axis=1), f32, dev).contiguous()
         self.t_next = _t(np.repeat(tg[1:, None], R, axis=1), f32, dev).contiguous()
+        self.abar_cur = self.abar_next = None
+        if cfg.sampler == "ddim":
+            if timesteps is None:
+                raise ValueError("the DDIM sampler needs the grid timesteps")
+            ab = B.ddim_alpha_bar(cfg.train_steps, cfg.beta_1, cfg.beta_T, timesteps)
+            self.abar_cur = _t(np.repeat(ab[:-1, None], R, axis=1), f32, dev).contiguous()
+            self.abar_next = _t(np.repeat(ab[1:, None], R, axis=1), f32, dev).contiguous()
         self.guidance = _t(np.asarray(guidance, np.float32).reshape(R), f32, dev)
         self.alpha = _t(np.asarray(alpha, np.float32).reshape(N, R), f32, dev).contiguous()
         self.direction = _t(direction, f32, dev)
@@ -194,6 +206,8 @@ class StepRunner:
         a.v_out = None if self.v_out is None else self.v_out.data_ptr()
         a.block_norms = None if self.block_norms is None else self.block_norms.data_ptr()
         a.text = self.text.data_ptr()
+        a.abar_cur = None if self.abar_cur is None else self.abar_cur[i].data_ptr()
+        a.abar_next = None if self.abar_next is None else self.abar_next[i].data_ptr()
         return a
 
     def collect_block_norms(self, enable: bool = True):

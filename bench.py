@@ -228,6 +228,11 @@ def kernel_rooflines():
     tn = torch.full((1,), 0.875, device="cuda")
     ms = _timed(lambda: B.sampler_update(L.ALD_EULER, xs, tc, tn, v_hat=vh, rows_per_req=n_tok))
     out["sampler_euler"] = _entry("hbm", ms, 12.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
+    ab = torch.full((1,), 0.3, device="cuda")
+    abn = torch.full((1,), 0.35, device="cuda")
+    vh.normal_(generator=g)
+    ms = _timed(lambda: B.sampler_update(L.ALD_DDIM, xs, ab, abn, v_hat=vh, rows_per_req=n_tok))
+    out["sampler_ddim"] = _entry("hbm", ms, 12.0 * n_tok * C, HBM_PEAK_GBS, "GB/s", shape=f"{n_tok} x {C}")
     # latent-site steering: a steered fp32 copy of the latent (4 B read + 4 B written per value)
     dl = torch.randn(C, device="cuda", generator=g)
     dl /= dl.norm()
@@ -327,6 +332,52 @@ def counter_legs(legs, reps):
     torch.cuda.synchronize()
 
 
+def loop_rate(model, inp, resid, replays):
+    """steps/s of whole replays of the run's full sampler loop as one graph."""
+    import torch
+    from audio_latent_diffusion_amd import runtime
+    run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
+                             inp.direction, resid, timesteps=inp.timesteps)
+    n = run.n_steps
+    x_init = run.x.clone()
+    graph = run.capture_graph(range(n))
+    run.x.copy_(x_init)
+    run.launch_graph(graph)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        run.x.copy_(x_init)
+        run.launch_graph(graph)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ok = bool(torch.isfinite(run.x).all().item())
+    run.destroy_graph()
+    return {"steps_per_s": round(replays * n / wall, 2), "ms_per_loop": round(wall * 1e3 / replays, 2),
+            "finite": ok}
+
+
+def variant_loops(model, resid):
+    """The mid-size model's loop under other settings: the DDIM sampler over
+    the 200-step grid (the warm-start pages' backbone setting, steering in
+    steps 40-79), and steering at the latent and text sites (8 Euler steps;
+    the text site re-projects the steered text's K/V in every step)."""
+    import ald_inputs as I
+    out = {}
+    cfg = I.MID_DDIM
+    r = loop_rate(model.with_config(sampler="ddim", n_steps=cfg.n_steps), I.make_inputs(cfg), resid, 2)
+    out["ddim_200"] = dict(workload="DDIM sampler, 200 steps as one hipGraph, steering alpha 0.5 at block 12 "
+                                    "in steps 40-79", **r)
+    for site in ("latent", "text"):
+        cfg = I.MID.replace(steer_site=site)
+        inp = I.make_inputs(cfg)
+        unit = float(np.mean(np.linalg.norm(inp.x, axis=1))) if site == "latent" else \
+            float(np.mean(np.linalg.norm(inp.text[:cfg.requests].reshape(-1, cfg.text_dim).astype(np.float64), axis=1)))
+        r = loop_rate(model.with_config(steer_site=site), inp, unit, 20)
+        out[f"steer_{site}_site"] = dict(workload=f"8 Euler steps as one hipGraph, steering alpha 0.5 at the "
+                                                  f"{site} site in steps 2-5", **r)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +453,7 @@ def main():
     steps_per_s = args.steps / wall
     ok = bool(torch.isfinite(run.x).all().item())
 
+    variants = variant_loops(model, resid)
     ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
     achieved = ops_launch / (ms_launch / 1e3) / 1e12
     traffic = measured_traffic()
@@ -435,6 +487,7 @@ def main():
                      "avg_launch_us": round(ms_launch * 1e3, 2),
                      "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
         "w8a8_gemm_serve": serve,
+        "loop_variants": variants,
         "kernels": kernels,
     }
     if not args.no_cpu:

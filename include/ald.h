@@ -65,7 +65,11 @@ enum { ALD_ACT_NONE = 0, ALD_ACT_GELU = 1 };
 #define ALD_PREQUANT 1u   /* xq / x_scale are inputs (already quantized); x unused */
 
 /* sampler_update ops. */
-enum { ALD_EULER = 0, ALD_RENOISE = 1 };
+enum { ALD_EULER = 0, ALD_RENOISE = 1, ALD_DDIM = 2, ALD_RENOISE_VP = 3 };
+
+/* Samplers of the step: flow matching (velocity, Euler on t) or DDIM
+ * (epsilon prediction, deterministic DDIM on alpha_bar). */
+enum { ALD_SAMPLER_FLOW = 0, ALD_SAMPLER_DDIM = 1 };
 
 /* steer_add modes (aria, Section III: add the direction, or project onto it). */
 enum { ALD_STEER_ADD = 0, ALD_STEER_PROJECT = 1 };
@@ -240,7 +244,16 @@ int cfg_merge(const uint16_t* v, int64_t n_tok, int C, int rows_per_req,
  *   ALD_RENOISE: x  = (1 - t_cur[r]) * x0 + t_cur[r] * eps (warm start,
  *                SoundWeaver Section 2: forward-noise a cached clean latent
  *                to the skip time; eps is supplied by the caller).
- * Unused pointers (v_hat for RENOISE; x0, eps, t_next for EULER) may be NULL.
+ * For the DDIM ops (SoundWeaver, Section 3 setup: the backbones run the DDIM
+ * sampler) t_cur / t_next hold alpha_bar at the current and the next grid
+ * point instead of times, and v_hat is the guided epsilon prediction:
+ *   ALD_DDIM      : x0 = (x - sqrt(1 - a) v_hat) / sqrt(a),
+ *                   x  = sqrt(a') x0 + sqrt(1 - a') v_hat  (a = t_cur[r],
+ *                   a' = t_next[r]; eta = 0; fp32; a' = 1 gives x0)
+ *   ALD_RENOISE_VP: x = sqrt(a) x0 + sqrt(1 - a) eps      (warm start at the
+ *                   skip point's alpha_bar a = t_cur[r])
+ * Unused pointers (v_hat for the re-noise ops; x0, eps, t_next for the
+ * updates) may be NULL.
  * C % 4 == 0; n_tok * C / 4 below 2^31 (else ALD_E_UNSUPPORTED). */
 int sampler_update(int op, float* x, const float* v_hat, const float* x0,
                    const float* eps, int64_t n_tok, int C, int rows_per_req,
@@ -267,6 +280,7 @@ typedef struct {
   float ln_eps;
   int steer_mode;    /* ALD_STEER_ADD | ALD_STEER_PROJECT */
   int steer_site;    /* ALD_SITE_RESIDUAL | ALD_SITE_LATENT | ALD_SITE_TEXT */
+  int sampler;       /* ALD_SAMPLER_FLOW | ALD_SAMPLER_DDIM */
 } dit_config;
 
 /* One linear layer's weights in the precision of dit_config.wmode:
@@ -330,7 +344,17 @@ typedef struct {
                                  steered block's output before steering         */
   const uint16_t* text;       /* fp16 [2R * T, D_t] text conditioning as given to
                                  dit_text_kv; read by the text site only         */
+  const float* abar_cur;      /* DDIM: alpha_bar [R] at this step's grid point  */
+  const float* abar_next;     /*       and at the next one (1 after the last)   */
 } dit_step_args;
+
+/* HOST helper for the DDIM sampler: alpha_bar of the noise schedule whose
+ * betas run linearly from beta_1 to beta_T over T training steps,
+ * alpha_bar[t] = prod_{s <= t} (1 - beta_s) (double precision), gathered at
+ * the n grid timesteps (each in [0, T)) into abar_out[0..n-1], and
+ * abar_out[n] = 1 (after the last step the clean estimate is returned).
+ * abar_out holds n + 1 floats.  Host pointers; no device work. */
+int ddim_alpha_bar(int T, double beta_1, double beta_T, const int32_t* timesteps, int n, float* abar_out);
 
 /* Workspace bytes needed by dit_step / dit_text_kv for up to max_tokens
  * latent tokens (n_tok) and R requests. */
@@ -344,8 +368,13 @@ int dit_text_kv(const dit_config* cfg, const dit_weights* w,
                 size_t ws_bytes, hipStream_t stream);
 
 /* One denoising step: input projection + time embedding, n_blocks DiT
- * blocks, final LayerNorm + output projection, CFG merge, Euler update (with
- * optional warm-start re-noise first).  Steering (when steer_block >= 0), at
+ * blocks, final LayerNorm + output projection, CFG merge, sampler update
+ * (with optional warm-start re-noise first).  ALD_SAMPLER_FLOW: the model
+ * output is a velocity, Euler from t_cur to t_next, re-noise
+ * (1 - t) x0 + t eps.  ALD_SAMPLER_DDIM: the model output is an epsilon
+ * prediction, DDIM from abar_cur to abar_next, re-noise
+ * sqrt(a) x0 + sqrt(1 - a) eps at abar_cur; t_cur feeds only the time
+ * embedding (the grid timestep / T).  Steering (when steer_block >= 0), at
  * steer_site with operation steer_mode and strength alpha[r]:
  *   ALD_SITE_RESIDUAL: every row of request r after block steer_block;
  *   ALD_SITE_LATENT  : the latent fed to the input projection (steer_latent;

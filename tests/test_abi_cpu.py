@@ -1,10 +1,12 @@
 """The C ABI on the CPU: the library loads, exports every declared entry
 point, and its host-side validation rejects bad arguments before any launch
-(no GPU needed: every call here fails validation, so nothing touches HIP)."""
+(no GPU needed: every device entry point called here fails validation, so
+nothing touches HIP; the host-only schedule helper runs for real)."""
 import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from audio_latent_diffusion_amd import _lib as L
@@ -97,7 +99,7 @@ def test_attention_and_elementwise_validation():
 def _cfg(**kw):
     d = dict(n_blocks=2, hidden=256, n_heads=4, head_dim=64, mlp=1024, channels=64, text_tokens=32, text_dim=256,
              wmode=L.ALD_W8A8, steer_block=1, ln_eps=1e-5, steer_mode=L.ALD_STEER_ADD,
-             steer_site=L.ALD_SITE_RESIDUAL)
+             steer_site=L.ALD_SITE_RESIDUAL, sampler=L.ALD_SAMPLER_FLOW)
     d.update(kw)
     return L.dit_config(**d)
 
@@ -140,6 +142,11 @@ def test_step_validation():
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     bad = _cfg(steer_site=3)
     assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    bad = _cfg(sampler=2)
+    assert lib.dit_step(ctypes.byref(bad), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    # the DDIM sampler reads alpha_bar, which these args do not give
+    dd = _cfg(sampler=L.ALD_SAMPLER_DDIM)
+    assert lib.dit_step(ctypes.byref(dd), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
     # the text site reads the raw text, which these args do not give
     txt = _cfg(steer_site=L.ALD_SITE_TEXT)
     need_t = lib.dit_workspace_size(ctypes.byref(txt), 64, 1)
@@ -179,3 +186,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         L.lib()
+
+
+def test_ddim_alpha_bar_host_helper_matches_oracle():
+    """The library's schedule helper (host C++) and the oracle's schedule are
+    independent codes of the same linear-beta product; they agree to fp32."""
+    from audio_latent_diffusion_amd import binding as B
+    from oracle import ald_oracle as O
+    import ald_inputs as I
+    cfg = I.TINY_DDIM
+    ts = I.ddim_timesteps(200, 1000)
+    got = B.ddim_alpha_bar(cfg.train_steps, cfg.beta_1, cfg.beta_T, ts)
+    ref = O.ddim_alpha_bars(cfg, ts)
+    assert got.shape == ref.shape and got[-1] == 1.0
+    assert np.allclose(got, ref, rtol=2.0 ** -23, atol=0)
+    lib = L.lib()
+    out = np.empty(3, np.float32)
+    bad_ts = np.array([0, 1000], np.int32)
+    assert lib.ddim_alpha_bar(1000, 1e-4, 0.02, bad_ts.ctypes.data_as(ctypes.c_void_p), 2,
+                              out.ctypes.data_as(ctypes.c_void_p)) == L.ALD_E_INVALID
+    assert lib.ddim_alpha_bar(1, 1e-4, 0.02, None, 0, out.ctypes.data_as(ctypes.c_void_p)) == L.ALD_E_INVALID
+    assert lib.ddim_alpha_bar(1000, 1e-4, 0.02, None, 0, out.ctypes.data_as(ctypes.c_void_p)) == L.ALD_OK
+    assert out[0] == 1.0
+    # sampler ops: an unknown op and a DDIM update without its prediction are rejected
+    assert lib.sampler_update(4, FAKE, FAKE, None, None, 10, 64, 10, None, FAKE, FAKE, None, None) == L.ALD_E_INVALID
+    assert lib.sampler_update(L.ALD_DDIM, FAKE, None, None, None, 10, 64, 10, None, FAKE, FAKE, None,
+                              None) == L.ALD_E_INVALID
+    assert lib.sampler_update(L.ALD_RENOISE_VP, FAKE, None, FAKE, None, 10, 64, 10, None, FAKE, None, None,
+                              None) == L.ALD_E_INVALID

@@ -368,6 +368,37 @@ def test_steer_latent(C, mode):
                                                   mode=mode)).tobytes()
 
 
+@pytest.mark.parametrize("a,an", [(0.3, 0.55), (4.04e-5, 5.2e-5), (0.9999, 1.0)])
+def test_ddim_sampler_ops(a, an):
+    """DDIM update and its warm-start re-noise against the oracle (fp64), per
+    request alpha_bar; an inactive request keeps its latent bit for bit.  The
+    fp32 update divides by sqrt(a): the bar scales with 1 / sqrt(a)."""
+    r = rng(31)
+    R, S, C = 3, 70, 64
+    n = R * S
+    x = r.standard_normal((n, C)).astype(np.float32)
+    e = r.standard_normal((n, C)).astype(np.float32)
+    x0 = r.standard_normal((n, C)).astype(np.float32)
+    ab = np.array([a, a, 0.5], np.float32)
+    abn = np.array([an, an, 0.7], np.float32)
+    active = np.array([1, 1, 0], np.uint8)
+    req = np.arange(n) // S
+    xd = dev(x)
+    B.sampler_update(L.ALD_DDIM, xd, dev(ab), dev(abn), v_hat=dev(e), rows_per_req=S, active=dev(active))
+    got = host(xd)
+    on = req < 2
+    ref = O.ddim_update(x[on], e[on], ab[req[on]][:, None], abn[req[on]][:, None])
+    err = np.max(np.abs(got[on].astype(np.float64) - ref)) / np.max(np.abs(ref))
+    assert err < 2e-6 / np.sqrt(a), err
+    assert got[~on].tobytes() == x[~on].tobytes()
+    xd = dev(x)
+    B.sampler_update(L.ALD_RENOISE_VP, xd, dev(ab), x0=dev(x0), eps=dev(e), rows_per_req=S, active=dev(active))
+    got = host(xd)
+    ref = O.renoise_vp(x0[on], e[on], ab[req[on]][:, None])
+    assert np.max(np.abs(got[on].astype(np.float64) - ref)) < 1e-6
+    assert got[~on].tobytes() == x[~on].tobytes()
+
+
 def test_cfg_merge_and_sampler():
     r = rng(9)
     R, S, C = 3, 50, 64

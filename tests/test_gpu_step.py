@@ -22,7 +22,8 @@ RESID = 5.0
 
 def _runner(model, inp, resid=RESID, **kw):
     return runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
-                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps, **kw)
+                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps,
+                              timesteps=inp.timesteps, **kw)
 
 
 @pytest.fixture(scope="module")
@@ -131,7 +132,7 @@ def test_text_site_graph_equals_eager(tiny):
     cfg, p, model, om = tiny
     cfg8 = cfg.replace(steer_site="text", steer_steps=(2, 3, 4, 5))
     inp = I.make_inputs(cfg8)
-    mt = model.with_steering(steer_site="text")
+    mt = model.with_config(steer_site="text")
     eager = _runner(mt, inp)
     for i in range(8):
         eager.step(i)
@@ -149,6 +150,46 @@ def test_text_site_graph_equals_eager(tiny):
     for i in range(8):
         e2.step(i)
     assert host(g.x).tobytes() == host(e2.x).tobytes()
+
+
+@pytest.mark.parametrize("steps", [[0, 1], [198, 199]])
+def test_tiny_ddim_steps(steps):
+    """DDIM sampler (epsilon prediction on the 200-step linear-beta grid):
+    the first steps (alpha_bar near 4e-5) and the last two (the last returns
+    the clean estimate) against the oracle."""
+    cfg = I.TINY_DDIM
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    run = _runner(runtime.DiTModel(cfg, p), inp, keep_velocity=True)
+    for i in steps:
+        run.step(i)
+    ref, tr = _oracle_steps(O.prepare_model(cfg, p), inp, steps)
+    err = O.normwise_rel_err(host(run.x), ref)
+    verr = O.normwise_rel_err(host(run.v_out), tr[-1].v)
+    print(f"tiny ddim steps {steps}: latent err {err:.2e}, prediction err {verr:.2e}")
+    assert err < TOL
+    assert verr < 5e-2
+
+
+def test_ddim_skip_arms_full_run_graph():
+    """Two requests, a cold start and a 10 % skip arm (re-noised at step 20),
+    through all 200 DDIM steps: one captured graph equals eager execution bit
+    for bit, and the final latent matches the oracle's whole run."""
+    cfg = I.TINY_DDIM.replace(n_blocks=1, steer_block=0)
+    p = I.make_params(cfg)
+    inp = I.make_ddim_warm_inputs(cfg, np.array([0, 10]), seqlens=np.array([40, 24]))
+    model = runtime.DiTModel(cfg, p)
+    eager = _runner(model, inp)
+    for i in range(cfg.n_steps):
+        eager.step(i)
+    g = _runner(model, inp)
+    g.capture()
+    g.replay()
+    assert host(g.x).tobytes() == host(eager.x).tobytes()
+    ref, _ = O.run_sampler(O.prepare_model(cfg, p), inp, resid_norm=RESID)
+    err = O.normwise_rel_err(host(g.x), ref)
+    print(f"tiny ddim 200 steps, arms 0 % / 10 %: latent err {err:.2e}")
+    assert err < TOL
 
 
 def test_alpha_zero_bit_identical(tiny):

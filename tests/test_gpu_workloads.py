@@ -28,7 +28,8 @@ RESID = 20.0
 
 def _runner(model, inp, resid=RESID, **kw):
     return runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
-                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps, **kw)
+                              inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps,
+                              timesteps=inp.timesteps, **kw)
 
 
 def _parity(cfg, steps, inp=None):

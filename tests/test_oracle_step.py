@@ -188,7 +188,7 @@ def test_ddim_step_and_skip_arm_warm_start():
     """DDIM sampler: a step is the DDIM update of the guided prediction at the
     grid's alpha_bar; a warm request whose arm skips 10 % waits until step 20
     and is then re-noised to the forward sample at that grid point."""
-    cfg = I.TINY_DDIM.replace(n_blocks=1)
+    cfg = I.TINY_DDIM.replace(n_blocks=1, steer_block=0)
     p = I.make_params(cfg)
     m = O.prepare_model(cfg, p)
     inp = I.make_ddim_warm_inputs(cfg, np.array([0, 10]), seqlens=np.array([40, 24]))
