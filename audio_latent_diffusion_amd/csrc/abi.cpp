@@ -242,6 +242,8 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   if (a->renoise) CHECK(a->x0 && a->eps && al16(a->x0) && al16(a->eps), ALD_E_INVALID);
   if (a->v_out) CHECK(al16(a->v_out), ALD_E_INVALID);
   CHECK(2 * a->n_tok <= INT32_MAX, ALD_E_UNSUPPORTED);
+  // the latent kernels index vectors of 4 values with 32-bit arithmetic
+  CHECK(a->n_tok * (c->channels / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
   // W8A16: the DMA GEMM addresses activations with 32-bit byte offsets
   if (c->wmode == ALD_W8A16) {
     CHECK(2 * a->n_tok * 2 * (int64_t)std::max(c->hidden, c->mlp) < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
@@ -584,7 +586,7 @@ int steer_latent(const float* x, float* x_out, int64_t n_tok, int C, int rows_pe
   if (n_tok == 0) return ALD_OK;
   CHECK(x && x_out && alpha && dir && x != x_out, ALD_E_INVALID);
   CHECK(al16(x) && al16(x_out) && al16(dir) && C % 4 == 0, ALD_E_INVALID);
-  CHECK(C <= 512 && n_tok < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
+  CHECK(C <= 512 && n_tok * (C / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
   if (!row_req) CHECK(rows_per_req > 0 && R > 0, ALD_E_INVALID);
   RowMap map{0, row_req ? 1 : rows_per_req, row_req ? 1 : R, row_req};
   launch_steer_latent(x, x_out, n_tok, C, map, alpha, resid_norm, dir, mode == ALD_STEER_PROJECT, stream);

@@ -107,8 +107,43 @@ __global__ __launch_bounds__(256) void steer_kernel(const uint16_t* src, int64_t
   }
 }
 
-// Steering of the fp32 latent fed to the model (the latent site): one wave
-// per token, a lane holds 4 consecutive channels per 256-channel slice;
+// Steering of the fp32 latent fed to the model (the latent site), when C / 4
+// divides 64: one thread per vector of 4 channels, the G = C / 4 lanes of a
+// token consecutive and aligned inside a wave, the projection's dot product
+// summed over them with lane exchanges (every lane takes part, also past the
+// end); formulas as below.
+template <bool PROJ>
+__global__ __launch_bounds__(256) void steer_latent_vec_kernel(const float* __restrict__ x, float* __restrict__ xs,
+                                                               uint32_t n_tok, int C, RowMap map,
+                                                               const float* __restrict__ alpha, float resid_norm,
+                                                               const float* __restrict__ dir) {
+  const int G = C >> 2;
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t tok = i / (uint32_t)G;
+  const int c = (int)(i % (uint32_t)G) * 4;
+  const bool valid = tok < n_tok;
+  const int64_t o = (int64_t)tok * C + c;
+  v4f v = valid ? ld4f_nt(x + o) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const v4f d = *reinterpret_cast<const v4f*>(dir + c);
+  const float a = valid ? alpha[req_of(map, tok)] : 0.0f;
+  float coef = a * resid_norm;
+  if constexpr (PROJ) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dot = fmaf(v[k], d[k], dot);
+    for (int m = 1; m < G; m <<= 1) dot += __shfl_xor(dot, m);
+    coef = a * dot;
+  }
+  if (!valid) return;
+  if (a != 0.0f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = fmaf(coef, d[k], v[k]);
+  }
+  st4f_nt(xs + o, v);
+}
+
+// The general form (C up to 512): one wave per token, a lane holds 4
+// consecutive channels per 256-channel slice;
 //   add     : xs[t, :] = x[t, :] + (a * resid_norm) * dir
 //   project : xs[t, :] = x[t, :] + (a * (x[t, :] . dir)) * dir
 // as one fp32 FMA per value; tokens with a == 0 are copied unchanged.
@@ -503,6 +538,15 @@ void launch_steer_copy(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t 
 void launch_steer_latent(const float* x, float* xs, int64_t n_tok, int C, RowMap map, const float* alpha,
                          float resid_norm, const float* dir, int project, hipStream_t st) {
   if (n_tok <= 0 || C <= 0) return;
+  if (C % 4 == 0 && 64 % (C / 4) == 0) {
+    if (project)
+      hipLaunchKernelGGL((steer_latent_vec_kernel<true>), grid_lat(n_tok, C), dim3(256), 0, st, x, xs,
+                         (uint32_t)n_tok, C, map, alpha, resid_norm, dir);
+    else
+      hipLaunchKernelGGL((steer_latent_vec_kernel<false>), grid_lat(n_tok, C), dim3(256), 0, st, x, xs,
+                         (uint32_t)n_tok, C, map, alpha, resid_norm, dir);
+    return;
+  }
   dim3 grid((unsigned)std::min<int64_t>((n_tok + 3) / 4, 2048)), block(256);
   const bool two = C > 256;
 #define ALD_STEER_LAT(NV, P)                                                                                   \

@@ -220,7 +220,8 @@ int steer_add(uint16_t* h, int64_t ldh, int M, int H, int rows_per_req, int R,
  * x + (a * (x . dir)) * dir (ALD_STEER_PROJECT) per token, one fp32 FMA per
  * value, with a = alpha[r] and r = row_req ? row_req[i] : (i / rows_per_req) % R.
  * Tokens with a == 0 are copied unchanged.  x, x_out fp32 [n_tok, C]
- * (distinct), dir [C] fp32; C % 4 == 0, C <= 512; 16-byte aligned.  The step
+ * (distinct), dir [C] fp32; C % 4 == 0, C <= 512, n_tok * C / 4 below 2^31;
+ * 16-byte aligned.  The step
  * feeds x_out to the model and keeps x as the sampler state. */
 int steer_latent(const float* x, float* x_out, int64_t n_tok, int C, int rows_per_req, int R,
                  const int32_t* row_req, const float* alpha, float resid_norm,

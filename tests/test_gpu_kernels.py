@@ -337,8 +337,10 @@ def test_steer_project(H):
     assert got[untouched].tobytes() == h[untouched].tobytes()
 
 
-@pytest.mark.parametrize("C,mode", [(64, L.ALD_STEER_ADD), (64, L.ALD_STEER_PROJECT), (200, L.ALD_STEER_ADD),
-                                    (512, L.ALD_STEER_PROJECT)])
+# C / 4 dividing 64 takes the one-vector-per-thread kernel (C = 8, 64, 256),
+# the others the wave-per-token kernel (C = 200, 512)
+@pytest.mark.parametrize("C,mode", [(64, L.ALD_STEER_ADD), (64, L.ALD_STEER_PROJECT), (8, L.ALD_STEER_PROJECT),
+                                    (256, L.ALD_STEER_PROJECT), (200, L.ALD_STEER_ADD), (512, L.ALD_STEER_PROJECT)])
 def test_steer_latent(C, mode):
     """Latent-site steering: a steered fp32 copy of the latent; tokens of a
     zero-strength request are copied bit for bit, the others agree with the
