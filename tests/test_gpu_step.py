@@ -236,22 +236,35 @@ def test_graph_replay_equals_eager_and_no_recapture(tiny):
     assert O.normwise_rel_err(host(g.x), ref) < TOL
 
 
-def test_varlen_warm_start_parity(tiny):
-    cfg, p, model, om = tiny
-    cfg3 = cfg.replace(requests=3, n_steps=4)
+SITE_SAMPLER = [("residual", "flow"), ("latent", "flow"), ("text", "flow"), ("text", "ddim"), ("latent", "ddim")]
+
+
+@pytest.mark.parametrize("site,sampler", [("residual", "flow"), ("text", "ddim"), ("latent", "ddim")])
+def test_varlen_warm_start_parity(tiny, site, sampler):
+    """Packed requests of different lengths, two of them warm-started at
+    later steps, steering at the given site, under either sampler."""
+    cfg, p, model, _ = tiny
+    cfg3 = cfg.replace(requests=3, n_steps=4, steer_site=site, sampler=sampler)
     inp = I.make_mixed_inputs(cfg3, seqlens=np.array([16, 33, 64]), warm=np.array([False, True, True]))
     inp.start_step = np.array([0, 1, 2])
-    run = _runner(model, inp)
+    run = _runner(model.with_config(steer_site=site, sampler=sampler, n_steps=4), inp)
     for i in range(4):
         run.step(i)
-    ref, _ = _oracle_steps(om, inp, None)
-    assert O.normwise_rel_err(host(run.x), ref) < TOL
+    ref, _ = _oracle_steps(O.prepare_model(cfg3, p), inp, None)
+    err = O.normwise_rel_err(host(run.x), ref)
+    print(f"varlen warm start, {site} site, {sampler}: latent err {err:.2e}")
+    assert err < TOL
 
 
-def test_packed_equals_single_requests(tiny):
+@pytest.mark.parametrize("site,sampler", SITE_SAMPLER)
+def test_packed_equals_single_requests(tiny, site, sampler):
+    """Three packed requests give, bit for bit, what each gives alone (steered
+    at the given site, under either sampler)."""
     cfg, p, model, _ = tiny
+    model = model.with_config(steer_site=site, sampler=sampler, n_steps=2)
+    cfg = model.cfg
     lens = np.array([40, 64, 17])
-    cfg3 = cfg.replace(requests=3, n_steps=2)
+    cfg3 = cfg.replace(requests=3)
     inp = I.make_mixed_inputs(cfg3, seqlens=lens, warm=np.zeros(3, bool))
     inp.alpha[:] = 0.5
     packed = _runner(model, inp)
