@@ -92,6 +92,31 @@ def gemm_mix_timing(cfg, iters=50):
     return ms_mix / len(shapes), ops / len(shapes), byts / len(shapes)
 
 
+def graph_floor_us(n=200, replays=5):
+    """Time per launch, inside a captured graph like the step's, of a kernel
+    that does no work (zero-strength steering of one row: one workgroup reads
+    the strength and exits): the floor every launch of the step pays."""
+    import torch
+    from audio_latent_diffusion_amd import binding as B
+    h = torch.zeros((1, 64), dtype=torch.float16, device="cuda")
+    a = torch.zeros(1, device="cuda")
+    d = torch.zeros(64, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        B.steer_add(h, a, 1.0, d)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for _ in range(n):
+            B.steer_add(h, a, 1.0, d)
+    gr.replay()
+    torch.cuda.synchronize()
+    ms = _events_time(gr.replay, replays, torch.cuda.current_stream())
+    del gr
+    return ms * 1e3 / n
+
+
 def serve_gemm(iters=20):
     """W8A8 GEMM at the serving-batch shapes (8192 tokens, hidden 1536)."""
     import torch
@@ -455,6 +480,7 @@ def main():
 
     variants = variant_loops(model, resid)
     ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
+    floor_us = graph_floor_us()
     achieved = ops_launch / (ms_launch / 1e3) / 1e12
     traffic = measured_traffic()
     serve = serve_gemm()
@@ -485,6 +511,7 @@ def main():
                      "frac": round(achieved / INT8_PEAK_TOPS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "avg_launch_us": round(ms_launch * 1e3, 2),
+                     "graph_noop_launch_us": round(floor_us, 2),
                      "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
         "w8a8_gemm_serve": serve,
         "loop_variants": variants,
