@@ -135,9 +135,16 @@ def serve_gemm(iters=20):
         for _ in range(3):
             fn()
         ms = _events_time(fn, iters, torch.cuda.current_stream())
+        # with the per-token quantization of an fp16 input in front (two launches)
+        x = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+        fq = lambda: B.w8a8_linear(x, wq, ws, xq=xq, x_scale=xs, y=y)  # noqa: E731
+        for _ in range(3):
+            fq()
+        ms_q = _events_time(fq, iters, torch.cuda.current_stream())
         ops = 2.0 * M * N * K
         out[name] = {"M": M, "K": K, "N": N, "ms": round(ms, 4), "tops": round(ops / ms / 1e9, 1),
-                     "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4)}
+                     "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4),
+                     "quant_plus_gemm_ms": round(ms_q, 4)}
         total_ops += ops
         total_ms += ms
     tops = total_ops / total_ms / 1e9
@@ -510,6 +517,12 @@ def main():
     serve = serve_gemm()
     kernels = kernel_rooflines()
 
+    # the step's algorithmic work: int8 GEMM ops of the block linears (the text
+    # K/V projection is hoisted out of the step) and attention flops
+    M, H, F, S, T, nh = cfg.tokens, cfg.hidden, cfg.mlp, cfg.seq, cfg.text_tokens, cfg.n_heads
+    int8_ops = cfg.n_blocks * sum(2.0 * M * N * K for K, N in MIX_SHAPES(H, F))
+    attn_flops = cfg.n_blocks * cfg.cfg_rows * nh * 4.0 * 64 * (S * S + S * T)
+    step_s = 1.0 / steps_per_s
     line = {
         "metric": "DiT denoise steps/s (CFG batch) + W8A8 GEMM % of int8 MFMA peak on 1 GPU",
         "value": round(steps_per_s, 2),
@@ -537,6 +550,9 @@ def main():
                      "avg_launch_us": round(ms_launch * 1e3, 2),
                      "graph_noop_launch_us": round(floor_us, 2),
                      "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
+        "step_rates": {"int8_gemm_tops": round(int8_ops / step_s / 1e12, 1),
+                       "attention_tflops": round(attn_flops / step_s / 1e12, 2),
+                       "int8_gemm_ops_per_step": int8_ops, "attention_flops_per_step": attn_flops},
         "w8a8_gemm_serve": serve,
         "loop_variants": variants,
         "kernels": kernels,
