@@ -5,17 +5,20 @@
  * as described by "A Quantized Native Runtime for On-Device Semantic Audio
  * Generation" (aria): a DiT denoiser over the audio latent that cross-attends
  * to the text (Section II, reference model), run with 8-bit weights and
- * 8-bit arithmetic (W8A8), 4-bit weights or half precision (Section III-A,
- * runtime), with an activation-steering add at one block's output whose
- * strength lives in device memory so that a captured step loop never needs
- * re-capture (Section III, steering; the Chinese summary of the same paper
- * gives the formula h <- h + alpha * ||h_bar|| * d_hat).  Classifier-free
+ * 8-bit arithmetic (W8A8), 8-bit weights alone, 4-bit weights or half
+ * precision (Section III-A, runtime), with activation steering (the direction
+ * added or projected onto, at a block's output, at the latent or at the text
+ * conditioning) whose strength lives in device memory so that a captured step
+ * loop never needs re-capture (Section III, steering; the Chinese summary of
+ * the same paper gives the formula h <- h + alpha * ||h_bar|| * d_hat).
+ * Classifier-free
  * guidance runs the cond row and its null-prompt companion in one batch and
  * merges them with w * cond + (1 - w) * uncond ("An Efficient vLLM-Based
  * Inference Pipeline for Unified Audio Understanding and Generation",
  * Section 2.4, Eq. (1)).  The sampler may warm-start from a cached clean
  * latent forward-noised to an intermediate step ("SoundWeaver: Semantic
- * Warm-Starting for Text-to-Audio Diffusion Serving", Section 2).
+ * Warm-Starting for Text-to-Audio Diffusion Serving", Section 2), under the
+ * flow-matching Euler sampler or the DDIM sampler that page's backbones run.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless a parameter says "host".
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ALD_VERSION 100
+#define ALD_VERSION 200  /* 200: steering sites, W8A16, the DDIM sampler (new config and step fields) */
 
 enum {
   ALD_OK = 0,
@@ -55,7 +58,8 @@ enum {
 };
 
 /* Weight precision of the block linears (aria, Section III-A: the precision
- * ladder fp16 / 8-bit / W8A8 / 4-bit). */
+ * ladder fp16 / 8-bit / W8A8 / 4-bit; ALD_W8A16 is the 8-bit weight-only
+ * rung). */
 enum { ALD_W8A8 = 0, ALD_F16 = 1, ALD_Q4 = 2, ALD_W8A16 = 3 };
 
 /* Epilogue activation. */
