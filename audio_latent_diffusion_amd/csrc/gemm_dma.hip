@@ -600,13 +600,17 @@ void prep_cfg() {
 // serving shape: the second wave covers the first one's LDS and copy-issue
 // stalls, the prologue and the epilogue, and overlaps the 4-bit
 // dequantization with the MFMAs); a Q4 stage is smaller, so its 256 x 256
-// tile keeps three stages in flight
+// tile keeps three stages in flight.  The smaller tiles serve short launches
+// (M of a few hundred rows), where the launch is latency-bound: four stages
+// measured 3-13 % faster than five (128 x 64) and eight (64 x 64) stages on
+// those shapes in every operand mode, K = 4096 included; three or fewer
+// stages, and more, were slower
 template <int MODE>
 struct Tiles {
   using T256 = Cfg<256, 256, (MODE == M_Q4 || MODE == M_Q8W) ? 3 : 2, MODE, 4>;
   using T128 = Cfg<128, 128, 4, MODE>;
-  using T128x64 = Cfg<128, 64, 5, MODE>;
-  using T64 = Cfg<64, 64, 8, MODE>;
+  using T128x64 = Cfg<128, 64, 4, MODE>;
+  using T64 = Cfg<64, 64, 4, MODE>;
 };
 
 int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }

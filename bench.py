@@ -75,16 +75,28 @@ def gemm_mix(cfg):
     return run_mix
 
 
-def gemm_mix_timing(cfg, iters=50):
+def gemm_mix_timing(cfg, iters=50, replays=5):
     """Average launch time of the W8A8 GEMM over the step's per-block launch
-    mix, timed with HIP events on torch's current stream (the stream the
-    launches go to), with the algorithmic ops and bytes per launch."""
+    mix, with the algorithmic ops and bytes per launch.  The launches are
+    captured into a graph, as the step runs them (launched one by one from
+    Python, these short kernels would time the host instead), and the graph's
+    replays are timed with HIP events on torch's current stream, the stream
+    they run on."""
     import torch
     run_mix = gemm_mix(cfg)
-    stream = torch.cuda.current_stream()
-    for _ in range(3):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
         run_mix()
-    ms_mix = _events_time(run_mix, iters, stream)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for _ in range(iters):
+            run_mix()
+    gr.replay()
+    torch.cuda.synchronize()
+    ms_mix = _events_time(gr.replay, replays, torch.cuda.current_stream()) / iters
+    del gr
     M = cfg.tokens
     shapes = MIX_SHAPES(cfg.hidden, cfg.mlp)
     ops = sum(2.0 * M * N * K for K, N in shapes)
