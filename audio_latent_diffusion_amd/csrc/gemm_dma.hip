@@ -396,10 +396,54 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
+  // Epilogue through LDS, one wave-private region per wave: the raw
+  // accumulators of PW columns at a time go to LDS in [row][col] order (row
+  // stride padded by 16 bytes so the 32 rows written together fall on
+  // distinct banks); then each lane takes 8 consecutive columns of a row,
+  // for coalesced 16-byte loads and stores.  A pass issues all of its
+  // residual loads before any arithmetic, so their latency is paid once.
+  const EpiArgs& e = g.epi;
+  constexpr int PW = C::PW, RS = C::RS;
+  constexpr int LPR = PW / 8;       // lanes per row
+  constexpr int RPI = 64 / LPR;     // rows per iteration
+  constexpr int NIT = C::WM / RPI;  // iterations per pass
+  constexpr bool RES = EPI == EPI_RES || EPI == EPI_GELU_RES;
+  constexpr bool GELU = EPI == EPI_GELU || EPI == EPI_GELU_RES;
+  const bool vec = (g.N & 7) == 0 && (e.ldy & 7) == 0 && (!RES || (e.ldr & 7) == 0) && !e.acc;
+  const int cl = (lane % LPR) * 8;
+  const int rl0 = lane / LPR;
+  const int rbase = m0 + wm * C::WM;
+  const int lr = lane & 31;
+  uint4 resv[RES ? NIT : 1];
+  auto load_res = [&](int p) {
+    if constexpr (RES) {
+      const int col = n0 + wn * C::WN + p * PW + cl;
+      const int left = g.N - col;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int row = min(rbase + it * RPI + rl0, g.M - 1);
+        const uint16_t* rp = e.residual + (int64_t)row * e.ldr + min(col, g.N - 1);
+        if (vec && left >= 8) {
+          resv[it] = *reinterpret_cast<const uint4*>(rp);
+        } else {
+          uint16_t h[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) h[r] = r < left ? rp[r] : (uint16_t)0;
+          resv[it] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+        }
+      }
+    }
+  };
+  // Residual of the first epilogue pass, loaded before any copy when the
+  // registers allow (small tiles): its latency then hides behind the main
+  // loop instead of opening the epilogue.  Issued ahead of every stage copy,
+  // these loads are older than all of them, so the stage waits stay exact.
+  constexpr bool EARLY_RES = RES && NIT <= 4;
+  if constexpr (EARLY_RES) load_res(0);
+
   // the epilogue's per-row / per-column scalars travel to LDS first; they
   // are older than every stage copy, so the stage waits cover them too
   {
-    const EpiArgs& e = g.epi;
     float* sc = reinterpret_cast<float*>(smem + C::SC_OFF);
 #pragma unroll
     for (int i = wave; i < C::SC_LOADS; i += C::WAVES) {
@@ -448,45 +492,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
     }
   }
 
-  // Epilogue through LDS, one wave-private region per wave: the raw
-  // accumulators of PW columns at a time go to LDS in [row][col] order (row
-  // stride padded by 16 bytes so the 32 rows written together fall on
-  // distinct banks); then each lane takes 8 consecutive columns of a row,
-  // for coalesced 16-byte loads and stores.  A pass issues all of its
-  // residual loads before any arithmetic, so their latency is paid once.
-  const EpiArgs& e = g.epi;
-  constexpr int PW = C::PW, RS = C::RS;
-  constexpr int LPR = PW / 8;       // lanes per row
-  constexpr int RPI = 64 / LPR;     // rows per iteration
-  constexpr int NIT = C::WM / RPI;  // iterations per pass
-  constexpr bool RES = EPI == EPI_RES || EPI == EPI_GELU_RES;
-  constexpr bool GELU = EPI == EPI_GELU || EPI == EPI_GELU_RES;
-  const bool vec = (g.N & 7) == 0 && (e.ldy & 7) == 0 && (!RES || (e.ldr & 7) == 0) && !e.acc;
-  const int cl = (lane % LPR) * 8;
-  const int rl0 = lane / LPR;
-  const int rbase = m0 + wm * C::WM;
-  const int lr = lane & 31;
-  uint4 resv[RES ? NIT : 1];
-  auto load_res = [&](int p) {
-    if constexpr (RES) {
-      const int col = n0 + wn * C::WN + p * PW + cl;
-      const int left = g.N - col;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int row = min(rbase + it * RPI + rl0, g.M - 1);
-        const uint16_t* rp = e.residual + (int64_t)row * e.ldr + min(col, g.N - 1);
-        if (vec && left >= 8) {
-          resv[it] = *reinterpret_cast<const uint4*>(rp);
-        } else {
-          uint16_t h[8];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) h[r] = r < left ? rp[r] : (uint16_t)0;
-          resv[it] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        }
-      }
-    }
-  };
-  load_res(0);
+  // Epilogue (the residual of pass 0 was loaded up front for the small tiles)
+  if constexpr (!EARLY_RES) load_res(0);
   __syncthreads();  // every wave is done with the operand stages; the scalars have landed
   uint32_t* reg = reinterpret_cast<uint32_t*>(smem) + wave * (C::WM * (RS + 1));
   const float* sc = reinterpret_cast<const float*>(smem + C::SC_OFF);
