@@ -284,6 +284,23 @@ def test_packed_equals_single_requests(tiny, site, sampler):
         assert host(single.x).tobytes() == got[sl].tobytes(), f"request {r}"
 
 
+@pytest.mark.parametrize("site,sampler", [("text", "flow"), ("residual", "ddim")])
+def test_mid_step_sites_and_ddim(site, sampler):
+    """The full mid-size model (16 blocks, hidden 1024): one steered step with
+    text-site steering (K/V recomputed in the step), and one DDIM step."""
+    n = 200 if sampler == "ddim" else 8
+    step = 60 if sampler == "ddim" else 2
+    cfg = I.MID.replace(steer_site=site, sampler=sampler, n_steps=n, steer_steps=(step,))
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    run = _runner(runtime.DiTModel(cfg, p), inp)
+    run.step(step)
+    ref, _ = O.run_sampler(O.prepare_model(cfg, p), inp, resid_norm=RESID, steps=[step])
+    err = O.normwise_rel_err(host(run.x), ref)
+    print(f"mid step {step}, {site} site, {sampler}: err {err:.2e}")
+    assert err < TOL
+
+
 def test_mid_step_parity():
     """The mid-size model (16 blocks, hidden 1024): one steered step, full size."""
     cfg = I.MID

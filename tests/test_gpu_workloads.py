@@ -52,6 +52,17 @@ def test_serve_widths_two_blocks(wmode):
     assert _parity(cfg, [0]) < TOL
 
 
+@pytest.mark.parametrize("site,sampler,step", [("text", "flow", 0), ("latent", "ddim", 60), ("residual", "ddim", 199)])
+def test_serve_widths_sites_and_ddim(site, sampler, step):
+    """Serving widths (2 blocks, W8A8): steering at the text and latent sites,
+    and the DDIM sampler in the middle and at the last step of its 200-step
+    grid (the last returns the clean estimate)."""
+    n = 200 if sampler == "ddim" else 8
+    cfg = I.SERVE.replace(n_blocks=2, steer_block=1, steer_alpha=0.5, steer_steps=(step,), steer_site=site,
+                          sampler=sampler, n_steps=n)
+    assert _parity(cfg, [step]) < TOL
+
+
 def test_q4_widths_one_block():
     """4-bit weights (group 32, fp16 scales) at hidden 2048, 1024 latent tokens."""
     cfg = I.Q4.replace(n_blocks=1, steer_block=0, steer_alpha=0.5, steer_steps=(0,))
