@@ -80,11 +80,11 @@ constexpr int KB = 128;    // X bytes per stage and row (one cache line)
 enum { M_I8 = 0, M_F16 = 1, M_Q4 = 2, M_Q8W = 3 };                  // operand modes
 enum { EPI_PLAIN = 0, EPI_RES = 1, EPI_GELU = 2, EPI_GELU_RES = 3 };  // epilogue kinds
 
-template <int BM_, int BN_, int STAGES_, int MODE_, int WGN_ = 2>
+template <int BM_, int BN_, int STAGES_, int MODE_, int WGN_ = 2, int WGM_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, MODE = MODE_;
   static constexpr bool INT = MODE == M_I8, Q4 = MODE == M_Q4, Q8W = MODE == M_Q8W;
-  static constexpr int WGM = 2, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
+  static constexpr int WGM = WGM_, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int MI = WM / 32, NJ = WN / 32;  // 32x32 MFMA blocks per wave
   static constexpr int KS = 4;                      // 32-byte X slices per stage
@@ -108,10 +108,11 @@ struct Cfg {
   static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per copy instruction
   static_assert((BX + BW + SCL) % WAVES == 0, "copies must split evenly over the waves");
   static_assert(BX % WAVES == 0, "X copies take whole rounds over the waves");
-  static_assert(MI >= 1 && NJ >= 1, "wave tile");
+  static_assert(MI >= 1 && NJ >= 1 && WM == 32 * MI && WN == 32 * NJ, "wave tile");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "scalar copies cover whole tiles");
+  static_assert(WN % PW == 0 && PW % 32 == 0, "epilogue passes cover the wave tile");
 };
 
 // s_waitcnt vmcnt(N): expcnt and lgkmcnt fields left at their maxima
@@ -601,20 +602,25 @@ void prep_cfg() {
   for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
 }
 
-// tile configurations per mode (BM, BN, stages, waves along N): the 256 x 256
-// tile runs 8 waves, two per SIMD, 128 x 64 each (one wave per SIMD with
-// 128 x 128 each reads less from LDS but measured 4-13% slower on every
-// serving shape: the second wave covers the first one's LDS and copy-issue
-// stalls, the prologue and the epilogue, and overlaps the 4-bit
+// tile configurations per mode (BM, BN, stages, waves along N, waves along
+// M): the 256 x 256 tile runs 8 waves, two per SIMD, 128 x 64 each (one wave
+// per SIMD with 128 x 128 each reads less from LDS but measured 4-13% slower
+// on every serving shape: the second wave covers the first one's LDS and
+// copy-issue stalls, the prologue and the epilogue, and overlaps the 4-bit
 // dequantization with the MFMAs); a Q4 stage is smaller, so its 256 x 256
-// tile keeps three stages in flight.  The smaller tiles serve short launches
-// (M of a few hundred rows), where the launch is latency-bound: four stages
-// measured 3-13 % faster than five (128 x 64) and eight (64 x 64) stages on
-// those shapes in every operand mode, K = 4096 included; three or fewer
-// stages, and more, were slower
+// tile keeps three stages in flight.  The 256 x 192 tile (8 waves of
+// 64 x 96; int8 and fp16 operands) exists for wave quantization: hidden widths that are multiples of
+// 192 but not of 256 x (CUs / row tiles) leave a partial last round of
+// 256 x 256 tiles (N = 1536 at M = 8192 fills 192 of 256 CUs; N = 4608 runs
+// 2.25 rounds), which 256 x 192 tiles fill exactly.  The smaller tiles serve
+// short launches (M of a few hundred rows), where the launch is
+// latency-bound: four stages measured 3-13 % faster than five (128 x 64)
+// and eight (64 x 64) stages on those shapes in every operand mode,
+// K = 4096 included; three or fewer stages, and more, were slower
 template <int MODE>
 struct Tiles {
   using T256 = Cfg<256, 256, (MODE == M_Q4 || MODE == M_Q8W) ? 3 : 2, MODE, 4>;
+  using T256x192 = Cfg<256, 192, 2, MODE, 2, 4>;
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 4, MODE>;
   using T64 = Cfg<64, 64, 4, MODE>;
@@ -622,22 +628,55 @@ struct Tiles {
 
 int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
+// compute units of the current device (one query per process; one device
+// kind per process is assumed)
+int64_t device_cus() {
+  static int cus = 0;
+  if (cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      return 256;
+  }
+  return cus;
+}
+
 template <int MODE>
 void dispatch(const GemmArgs& g, hipStream_t st) {
-  // largest tile that still fills most of the 256 CUs with one workgroup each
+  // largest tile that still fills most of the CUs with one workgroup each
   // (one round of 192 large tiles beats three rounds of smaller ones)
   constexpr int64_t FILL = 180;
   using T = Tiles<MODE>;
-  if (tiles(g.M, g.N, 256, 256) >= FILL) launch_epi<typename T::T256>(g, st);
-  else if (tiles(g.M, g.N, 128, 128) >= FILL) launch_epi<typename T::T128>(g, st);
-  else if (tiles(g.M, g.N, 128, 64) >= FILL) launch_epi<typename T::T128x64>(g, st);
-  else launch_epi<typename T::T64>(g, st);
+  if (tiles(g.M, g.N, 256, 256) >= FILL) {
+    // among the large tiles, the one with the least tile area over whole
+    // rounds of one workgroup per CU (ties keep 256 x 256, whose main loop
+    // needs less LDS bandwidth per operation)
+    if constexpr (MODE == M_I8 || MODE == M_F16) {
+      const int64_t cus = device_cus();
+      const int64_t r256 = (tiles(g.M, g.N, 256, 256) + cus - 1) / cus;
+      const int64_t r192 = (tiles(g.M, g.N, 256, 192) + cus - 1) / cus;
+      if (r192 * 192 < r256 * 256) {
+        launch_epi<typename T::T256x192>(g, st);
+        return;
+      }
+    }
+    launch_epi<typename T::T256>(g, st);
+  } else if (tiles(g.M, g.N, 128, 128) >= FILL) {
+    launch_epi<typename T::T128>(g, st);
+  } else if (tiles(g.M, g.N, 128, 64) >= FILL) {
+    launch_epi<typename T::T128x64>(g, st);
+  } else {
+    launch_epi<typename T::T64>(g, st);
+  }
 }
 
 template <int MODE>
 void prep_mode() {
   using T = Tiles<MODE>;
   prep_cfg<typename T::T256>();
+  if constexpr (MODE == M_I8 || MODE == M_F16) prep_cfg<typename T::T256x192>();
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
   prep_cfg<typename T::T64>();

@@ -140,6 +140,54 @@ def test_w8a8_serve_shapes_sampled(M, K, N):
     f16_close(host(y)[rows], yo)
 
 
+# the two large tiles of the launch, ragged in M and N, K an odd number of
+# 128-byte stages: 256 x 192 (N = 1500 fills one round of 256 CUs with 256
+# such tiles, where 256 x 256 tiles would leave 64 CUs idle) and 256 x 256
+# (N = 6100: both need whole rounds of the same area, and the tie keeps
+# 256 x 256); checked on sampled rows, the ragged last rows included
+LARGE_TILE_SHAPES = [(8000, 640, 1500), (8000, 640, 6100)]
+
+
+def _sample_rows(M, seed, n=40):
+    return np.concatenate([np.sort(rng(seed).choice(M - 8, n, replace=False)), np.arange(M - 8, M)])
+
+
+@pytest.mark.parametrize("M,K,N", LARGE_TILE_SHAPES)
+def test_w8a8_large_tiles_ragged(M, K, N):
+    r = rng(M + 3 * K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    wq, ws = O.quantize_rows_q8(w)
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = B.w8a8_linear(dev(x), dev(wq), dev(ws), bias=dev(b), residual=dev(res), xq=xq, x_scale=xs, acc=acc)
+    rows = _sample_rows(M, N)
+    ro = O.w8a8_linear(x[rows], wq, ws, b, residual=res[rows])
+    assert np.array_equal(host(xq)[rows], ro.xq)
+    assert np.array_equal(host(xs)[rows], ro.x_scale)
+    assert np.array_equal(host(acc)[rows].astype(np.int64), ro.acc)
+    f16_close(host(y)[rows], ro.y)
+    g = B.w8a8_linear(dev(x), dev(wq), dev(ws), bias=dev(b), act=L.ALD_ACT_GELU)
+    f16_close(host(g)[rows], O.w8a8_linear(x[rows], wq, ws, b, act=1).y)
+
+
+@pytest.mark.parametrize("M,K,N", LARGE_TILE_SHAPES)
+def test_f16_large_tiles_ragged(M, K, N):
+    r = rng(M + 5 * K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.05 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    rows = _sample_rows(M, N + 1)
+    y = B.f16_linear(dev(x), dev(w), dev(b), residual=dev(res))
+    f16_close(host(y)[rows], O.f16_linear(x[rows], w, b, residual=res[rows]))
+    y = B.f16_linear(dev(x), dev(w), dev(b), act=L.ALD_ACT_GELU)
+    f16_close(host(y)[rows], O.f16_linear(x[rows], w, b, act=1))
+
+
 # ------------------------------------------------------------- fp16 and q4 GEMMs
 
 @pytest.mark.parametrize("M,K,N", [(1, 8, 1), (77, 264, 130), (256, 1024, 64), (300, 2048, 520)])
