@@ -651,13 +651,17 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
   using T = Tiles<MODE>;
   if (tiles(g.M, g.N, 256, 256) >= FILL) {
     // among the large tiles, the one with the least tile area over whole
-    // rounds of one workgroup per CU (ties keep 256 x 256, whose main loop
-    // needs less LDS bandwidth per operation)
+    // rounds of one workgroup per CU, 256 x 192 weighted by 9/8 for its
+    // costlier operations (more LDS reads per MFMA, ragged column tiles when
+    // N is not a multiple of 192): it wins where a partial last round of
+    // 256 x 256 tiles idles many CUs (serving shapes at M = 8192: N = 1536
+    // and 4608), not on long launches of many rounds (M = 37k, N = 4096
+    // measured 3 % slower with it)
     if constexpr (MODE == M_I8 || MODE == M_F16) {
       const int64_t cus = device_cus();
       const int64_t r256 = (tiles(g.M, g.N, 256, 256) + cus - 1) / cus;
       const int64_t r192 = (tiles(g.M, g.N, 256, 192) + cus - 1) / cus;
-      if (r192 * 192 < r256 * 256) {
+      if (r192 * 192 * 9 < r256 * 256 * 8) {
         launch_epi<typename T::T256x192>(g, st);
         return;
       }

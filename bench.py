@@ -354,14 +354,17 @@ def measured_traffic():
 
 def counter_legs(legs, reps):
     """Workloads for the rocprofv3 --pmc runs: the GEMM launch mix of the
-    step (same shapes and stream as the roofline timing) and a plain device
-    copy of known size that calibrates FETCH_SIZE / WRITE_SIZE."""
+    step (same shapes and stream as the roofline timing), the W8A8 GEMMs at
+    the serving shapes, and a plain device copy of known size that
+    calibrates FETCH_SIZE / WRITE_SIZE."""
     import torch
     import ald_inputs as I
     if "gemm" in legs:
         run_mix = gemm_mix(I.MID)
         for _ in range(reps):
             run_mix()
+    if "serve" in legs:
+        print(json.dumps({"w8a8_gemm_serve": serve_gemm(iters=reps)}))
     if "kernels" in legs:
         kernel_rooflines()
     if "copy" in legs:
@@ -452,7 +455,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=16, help="untimed denoise steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--leg", default="", help="counter legs only (gemm,kernels,copy) for rocprofv3 runs")
+    ap.add_argument("--leg", default="", help="counter legs only (gemm,serve,kernels,copy) for rocprofv3 runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
