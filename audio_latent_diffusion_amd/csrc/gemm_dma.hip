@@ -90,10 +90,14 @@ struct Cfg {
   static constexpr int KS = 4;                      // 32-byte X slices per stage
   static constexpr int BX = BM / 8;                 // X blocks per stage (8 rows x 128 B)
   static constexpr int BW = Q4 ? BN / 32 : (Q8W ? BN / 16 : BN / 8);  // W blocks per stage
-  // Q4 scale copies (64 rows each), padded so that the copies split evenly
+  // W copies padded with repeats of the last W block's copy (the same bytes
+  // to the same place) so that the copies split evenly over the waves
+  static constexpr int WPAD = Q4 ? 0 : (WAVES - (BX + BW) % WAVES) % WAVES;
+  static constexpr int BWC = BW + WPAD;  // W copy instructions per stage
+  // Q4 scale copies (64 rows each), padded the same way
   static constexpr int SC0 = Q4 ? BN / 64 : 0;
   static constexpr int SCL = Q4 ? SC0 + (WAVES - (BX + BW + SC0) % WAVES) % WAVES : 0;
-  static constexpr int LOADS = (BX + BW + SCL) / WAVES;  // copy instructions per wave and stage
+  static constexpr int LOADS = (BX + BWC + SCL) / WAVES;  // copy instructions per wave and stage
   static constexpr int W_OFF = BX * BLK;                 // offsets within a stage
   static constexpr int S_OFF = (BX + BW) * BLK;
   static constexpr int STAGE_BYTES = S_OFF + SCL * 256;
@@ -106,7 +110,7 @@ struct Cfg {
   static constexpr int SC_OFF = LDS > EPI_LDS ? LDS : EPI_LDS;
   static constexpr int LDS_TOTAL = SC_OFF + (BM + 2 * BN) * 4;
   static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per copy instruction
-  static_assert((BX + BW + SCL) % WAVES == 0, "copies must split evenly over the waves");
+  static_assert((BX + BWC + SCL) % WAVES == 0, "copies must split evenly over the waves");
   static_assert(BX % WAVES == 0, "X copies take whole rounds over the waves");
   static_assert(MI >= 1 && NJ >= 1 && WM == 32 * MI && WN == 32 * NJ, "wave tile");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
@@ -158,13 +162,15 @@ struct Loader {
   // kind of copy i of a wave: 0 = X, 1 = W, 2 = Q4 scales (uniform)
   __device__ __forceinline__ static int kind(int wave, int i) {
     const int b = wave + C::WAVES * i;
-    return b < C::BX ? 0 : (b < C::BX + C::BW ? 1 : 2);
+    return b < C::BX ? 0 : (b < C::BX + C::BWC ? 1 : 2);
   }
   __device__ __forceinline__ static int step(int k) {
     return k == 0 ? KB : (C::Q4 ? (k == 1 ? 32 : 4) : (C::Q8W ? 64 : KB));
   }
   __device__ __forceinline__ static int dst(int b) {
-    return b < C::BX + C::BW ? b * BLK : C::S_OFF + (b - C::BX - C::BW) * 256;
+    if (b < C::BX + C::BW) return b * BLK;
+    if (b < C::BX + C::BWC) return (C::BX + C::BW - 1) * BLK;  // padding: the last W block again
+    return C::S_OFF + (b - C::BX - C::BWC) * 256;
   }
 
   __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0, int wave, int lane) {
@@ -177,8 +183,8 @@ struct Loader {
         const int tr = b * 8 + (lane >> 3);
         const int r = min(m0 + tr, g.M - 1);  // rows past the edge re-read a valid row; results dropped
         off[i] = (uint32_t)r * ldx + ((lane & 7) ^ swz(tr)) * 16;
-      } else if (b < C::BX + C::BW) {
-        const int bw = b - C::BX;
+      } else if (b < C::BX + C::BWC) {
+        const int bw = min(b - C::BX, C::BW - 1);  // padding repeats the last W block
         if constexpr (C::Q8W) {  // int8 W of fp16 X: 64 bytes per row and stage, 16 rows per block
           const int tr = bw * 16 + (lane >> 2);
           const int r = min(n0 + tr, g.N - 1);
@@ -193,7 +199,7 @@ struct Loader {
           off[i] = (uint32_t)r * (uint32_t)(g.K / 2) + (lane >> 5) * 16;
         }
       } else {  // Q4 scales: both fp16 group scales of a row (4 bytes); padding repeats the last copy
-        const int sidx = min(b - C::BX - C::BW, C::SC0 - 1);
+        const int sidx = min(b - C::BX - C::BWC, C::SC0 - 1);
         const int r = min(n0 + sidx * 64 + lane, g.N - 1);
         off[i] = (uint32_t)r * (uint32_t)(g.K / 32) * 2;
       }
@@ -609,7 +615,8 @@ void prep_cfg() {
 // copy-issue stalls, the prologue and the epilogue, and overlaps the 4-bit
 // dequantization with the MFMAs); a Q4 stage is smaller, so its 256 x 256
 // tile keeps three stages in flight.  The 256 x 192 tile (8 waves of
-// 64 x 96; int8 and fp16 operands) exists for wave quantization: hidden widths that are multiples of
+// 64 x 96; int8, fp16 and 8-bit weight-only operands) exists for wave
+// quantization: hidden widths that are multiples of
 // 192 but not of 256 x (CUs / row tiles) leave a partial last round of
 // 256 x 256 tiles (N = 1536 at M = 8192 fills 192 of 256 CUs; N = 4608 runs
 // 2.25 rounds), which 256 x 192 tiles fill exactly.  The smaller tiles serve
@@ -620,7 +627,7 @@ void prep_cfg() {
 template <int MODE>
 struct Tiles {
   using T256 = Cfg<256, 256, (MODE == M_Q4 || MODE == M_Q8W) ? 3 : 2, MODE, 4>;
-  using T256x192 = Cfg<256, 192, 2, MODE, 2, 4>;
+  using T256x192 = Cfg<256, 192, MODE == M_Q8W ? 3 : 2, MODE, 2, 4>;
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 4, MODE>;
   using T64 = Cfg<64, 64, 4, MODE>;
@@ -657,7 +664,7 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
     // 256 x 256 tiles idles many CUs (serving shapes at M = 8192: N = 1536
     // and 4608), not on long launches of many rounds (M = 37k, N = 4096
     // measured 3 % slower with it)
-    if constexpr (MODE == M_I8 || MODE == M_F16) {
+    if constexpr (MODE != M_Q4) {
       const int64_t cus = device_cus();
       const int64_t r256 = (tiles(g.M, g.N, 256, 256) + cus - 1) / cus;
       const int64_t r192 = (tiles(g.M, g.N, 256, 192) + cus - 1) / cus;
@@ -680,7 +687,7 @@ template <int MODE>
 void prep_mode() {
   using T = Tiles<MODE>;
   prep_cfg<typename T::T256>();
-  if constexpr (MODE == M_I8 || MODE == M_F16) prep_cfg<typename T::T256x192>();
+  if constexpr (MODE != M_Q4) prep_cfg<typename T::T256x192>();
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
   prep_cfg<typename T::T64>();

@@ -175,6 +175,19 @@ def test_w8a8_large_tiles_ragged(M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", LARGE_TILE_SHAPES)
+def test_q8w_large_tiles_ragged(M, K, N):
+    r = rng(M + 7 * K + N)
+    x = r.standard_normal((M, K)).astype(np.float16)
+    w = (0.02 * r.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * r.standard_normal(N)).astype(np.float32)
+    res = r.standard_normal((M, N)).astype(np.float16)
+    q, s = O.quantize_rows_q8(w)
+    rows = _sample_rows(M, N + 2)
+    y = B.q8w_linear(dev(x), dev(q), dev(s), dev(b), residual=dev(res))
+    f16_close(host(y)[rows], O.q8w_linear(x[rows], q, s, b, residual=res[rows]))
+
+
+@pytest.mark.parametrize("M,K,N", LARGE_TILE_SHAPES)
 def test_f16_large_tiles_ragged(M, K, N):
     r = rng(M + 5 * K + N)
     x = r.standard_normal((M, K)).astype(np.float16)
@@ -234,7 +247,8 @@ def test_q4_full_shapes_sampled(M, K, N):
 # ------------------------------------------------------------- 8-bit weight-only GEMM
 
 # one shape per tile size of the launch (64x64, 128x64, 128x128 and the
-# 8-wave 256x256), ragged in M and N, K an odd number of 64-element slices
+# 8-wave 256x192, whose weight copies are padded to a multiple of the
+# waves), ragged in M and N, K an odd number of 64-element slices
 @pytest.mark.parametrize("M,K,N", [(1, 64, 1), (77, 192, 130), (200, 640, 203), (1100, 320, 1400),
                                    (1500, 576, 1900), (3000, 640, 3900)])
 def test_q8w_linear(M, K, N):
