@@ -313,3 +313,25 @@ def test_mid_step_parity():
     err = O.normwise_rel_err(host(run.x), ref)
     print(f"mid step 2: err {err:.2e}")
     assert err < TOL
+
+
+def test_mid_graph_replays_equal_eager():
+    """The mid-size model's 8-step loop as one graph (the bench's unit),
+    replayed three times with eager work in between: every replay equals the
+    eager loop bit for bit."""
+    cfg = I.MID
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, p)
+    eager = _runner(model, inp)
+    for i in range(cfg.n_steps):
+        eager.step(i)
+    want = host(eager.x).tobytes()
+    g = _runner(model, inp)
+    x_init = g.x.clone()
+    g.capture()
+    for _ in range(3):
+        g.x.copy_(x_init)
+        g.replay()
+        assert host(g.x).tobytes() == want
+        torch.randn(1 << 20, device="cuda").sum().item()  # unrelated eager work between replays
