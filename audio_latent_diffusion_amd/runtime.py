@@ -26,6 +26,8 @@ from . import binding as B
 
 
 def _t(a, dtype, device):
+    if isinstance(a, torch.Tensor):  # weights already drawn on a device
+        return a.to(device=device, dtype=dtype).contiguous()
     return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype)
 
 

@@ -426,6 +426,68 @@ def mixed_warm_start(resid, replays=2):
             "ms_per_loop": r["ms_per_loop"], "finite": r["finite"]}
 
 
+def device_params(cfg, seed):
+    """Random weights of cfg's architecture, drawn on the GPU with a seeded
+    generator (the same distributions as the seeded host draws: weights
+    N(0, 0.02) in fp16, biases N(0, 0.02), LayerNorm gain 1 + N(0, 0.02) and
+    shift N(0, 0.02)); for timing runs of the large models, whose host draws
+    would take minutes."""
+    import torch
+    import ald_inputs as I
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    H, C = cfg.hidden, cfg.channels
+
+    def nrm(shape, s=0.02):
+        return torch.randn(shape, generator=g, device="cuda") * s
+
+    def ln():
+        return 1.0 + nrm(H), nrm(H)
+
+    shapes = I.linear_shapes(cfg)
+    blocks = []
+    for _ in range(cfg.n_blocks):
+        (g1, b1), (g2, b2), (g3, b3) = ln(), ln(), ln()
+        w = {n: nrm(shapes[n]).half() for n in I.LINEARS}
+        b = {n: nrm(shapes[n][0]) for n in I.LINEARS}
+        blocks.append(I.BlockParams(g1, b1, g2, b2, g3, b3, w, b))
+    lg, lb = ln()
+    return I.DiTParams(nrm((H, C)).half(), nrm(H), lg, lb, nrm((C, H)).half(), nrm(C), blocks)
+
+
+def large_model_loops(replays=2):
+    """Step rates of the other model sizes: the serving model (24 blocks,
+    hidden 1536, 8 requests as 16 CFG rows of 512 latent tokens) with fp16,
+    W8A8 and 8-bit weight-only weights side by side on the same inputs, and
+    the 4-bit-weight model (24 blocks, hidden 2048, 4 requests as 8 CFG rows of
+    1024 tokens); 8 Euler steps as one graph each."""
+    import torch
+    import ald_inputs as I
+    from audio_latent_diffusion_amd import runtime
+    out = {}
+    for cfg, arms in ((I.SERVE, ("w8a8", "f16", "w8a16")), (I.Q4, ("q4",))):
+        params = device_params(cfg, cfg.seed)
+        inp = I.make_inputs(cfg)
+        tokens = 2 * cfg.requests * cfg.seq
+        # the six block linears of the step (the text K/V projection is hoisted)
+        lin_ops = 2.0 * tokens * sum(n * k for name, (n, k) in I.linear_shapes(cfg).items() if name != "kv") \
+            * cfg.n_blocks
+        for arm in arms:
+            model = runtime.DiTModel(cfg.replace(wmode=arm), params)
+            r = loop_rate(model, inp, 1.0, replays)
+            key = f"serve_{arm}" if cfg is I.SERVE else "q4_model"
+            out[key] = dict(
+                workload=f"{cfg.n_blocks} blocks, hidden {cfg.hidden}, {cfg.requests} requests x CFG pair of "
+                         f"{cfg.seq} latent tokens ({tokens} rows), {arm} weights, 8 Euler steps as one hipGraph",
+                linear_ops_per_step=lin_ops,
+                linear_rate=round(lin_ops * r["steps_per_s"] / 1e12, 1),
+                linear_rate_unit="TOP/s" if arm == "w8a8" else "TFLOP/s", **r)
+            del model
+            torch.cuda.empty_cache()
+        del params
+        torch.cuda.empty_cache()
+    return out
+
+
 def variant_loops(model, resid):
     """The mid-size model's loop under other settings: the DDIM sampler over
     the 200-step grid (the warm-start pages' backbone setting, steering in
@@ -525,6 +587,7 @@ def main():
 
     variants = variant_loops(model, resid)
     variants["warm_start_mixed"] = mixed_warm_start(resid)
+    variants.update(large_model_loops())
     ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
     floor_us = graph_floor_us()
     achieved = ops_launch / (ms_launch / 1e3) / 1e12
