@@ -506,7 +506,11 @@ template <bool PROJ, bool OOP>
 static void launch_steer_mode(const uint16_t* src, int64_t lds, uint16_t* dst, int64_t ldd, int M, int M_steer,
                               int H, RowMap map, const float* alpha, float resid_norm, const float* dir,
                               hipStream_t st) {
-  dim3 grid((unsigned)std::min<int64_t>((M + 3) / 4, 2048)), block(256);
+  // grid caps measured on 262144 rows of 1536: the add (a stream) prefers
+  // more workgroups, the projection (a row reduction before the store) fewer
+  // (add 71 -> 73 %, projection 69 -> 73 % of HBM bandwidth against a cap of
+  // 2048 for both)
+  dim3 grid((unsigned)std::min<int64_t>((M + 3) / 4, PROJ ? 1024 : 4096)), block(256);
   const int nv = (H + 511) / 512;
 #define ALD_STEER(NV)                                                                                          \
   hipLaunchKernelGGL((steer_kernel<NV, PROJ, OOP>), grid, block, 0, st, src, lds, dst, ldd, M, M_steer, H, map, \

@@ -281,8 +281,12 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint16_t* __restrict
 
 // ---------------------------------------------------------------- launchers
 
-// at most this many 4-row workgroups: about what the 256 CUs keep resident
-constexpr int64_t ROW_GRID_CAP = 2048;
+// at most this many 4-row workgroups (each wave then walks 4 or more rows on
+// the large shapes, with the next row's loads in flight): on 262144 rows of
+// 1536 and 65536 rows of 6144 this measured faster than 2048 or 8192 (the
+// activation quantization 73 -> 78 % of HBM bandwidth) and than one row per
+// wave (LayerNorm + quantization 63 -> 53 %)
+constexpr int64_t ROW_GRID_CAP = 16384;
 
 #define ALD_ROW_LAUNCH(KERNEL, NV, K, GRID, ST, ...)                                                 \
   do {                                                                                               \
