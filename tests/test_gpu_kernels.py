@@ -403,6 +403,48 @@ def test_steer_project(H):
     assert got[untouched].tobytes() == h[untouched].tobytes()
 
 
+# The row kernels cap their grids (16384 four-row workgroups for the
+# quantizers and LayerNorms, 4096 for the steering add, 1024 for the
+# projection) and walk the remaining rows with the grid stride, the next
+# row's loads in flight; these row counts make each wave take several rows,
+# with a ragged last round.
+def test_row_kernels_grid_stride():
+    r = rng(77)
+    M, K = 4 * 16384 * 2 + 37, 64
+    x = (r.standard_normal((M, K)) * r.uniform(0.01, 30, (M, 1))).astype(np.float16)
+    q, s = B.quantize_rows_q8(dev(x))
+    qo, so = O.quantize_rows_q8(x)
+    assert np.array_equal(host(q), qo)
+    assert host(s).tobytes() == so.tobytes()
+    g = (1 + 0.02 * r.standard_normal(K)).astype(np.float32)
+    b = (0.02 * r.standard_normal(K)).astype(np.float32)
+    u = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    q, s = B.ln_quant(dev(x), dev(g), dev(b), 1e-5, u_out=u)
+    ug = host(u)
+    f16_close(ug, O.layer_norm(x, g, b, 1e-5), rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    qo, so = O.quantize_rows_q8(ug)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s), so)
+
+
+@pytest.mark.parametrize("mode", [L.ALD_STEER_ADD, L.ALD_STEER_PROJECT])
+def test_steer_grid_stride(mode):
+    r = rng(78 + mode)
+    M, H, S, R = 4 * 4096 * 3 + 96, 128, 96, 2
+    h = r.standard_normal((M, H)).astype(np.float16)
+    d = r.standard_normal(H)
+    d = (d / np.linalg.norm(d)).astype(np.float32)
+    a = np.array([0.5, 0.0], np.float32)
+    ht = dev(h)
+    B.steer_add(ht, dev(a), 2.5, dev(d), rows_per_req=S, R=R, mode=mode)
+    got = host(ht)
+    row_req = (np.arange(M) // S) % R
+    ref = O.steer_add(h, a[row_req], 2.5, d) if mode == L.ALD_STEER_ADD else O.steer_project(h, a[row_req], d)
+    f16_close(got, ref, rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    untouched = row_req == 1
+    assert got[untouched].tobytes() == h[untouched].tobytes()
+
+
 # C / 4 dividing 64 takes the one-vector-per-thread kernel (C = 8, 64, 256),
 # the others the wave-per-token kernel (C = 200, 512)
 @pytest.mark.parametrize("C,mode", [(64, L.ALD_STEER_ADD), (64, L.ALD_STEER_PROJECT), (8, L.ALD_STEER_PROJECT),
