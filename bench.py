@@ -153,14 +153,36 @@ def serve_gemm(iters=20):
         for _ in range(3):
             fq()
         ms_q = _events_time(fq, iters, torch.cuda.current_stream())
+        # the vendor library on the same operands (hipBLASLt behind torch._int_mm:
+        # int32 output, no dequantization epilogue), for comparison
+        wt = wq.t()
+        fv = lambda: torch._int_mm(xq, wt)  # noqa: E731
+        for _ in range(3):
+            fv()
+        ms_v = _events_time(fv, iters, torch.cuda.current_stream())
         ops = 2.0 * M * N * K
         out[name] = {"M": M, "K": K, "N": N, "ms": round(ms, 4), "tops": round(ops / ms / 1e9, 1),
                      "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4),
-                     "quant_plus_gemm_ms": round(ms_q, 4)}
+                     "quant_plus_gemm_ms": round(ms_q, 4), "vendor_int_mm_ms": round(ms_v, 4)}
         total_ops += ops
         total_ms += ms
     tops = total_ops / total_ms / 1e9
-    return {"shapes": out, "tops": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    res = {"shapes": out, "tops": round(tops, 1), "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)}
+    # a long square launch, where the fixed start and finish of a round amortize
+    M = K = N = 8192
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    xs = torch.rand(M, device="cuda", generator=g) * 1e-2
+    ws = torch.rand(N, device="cuda", generator=g) * 1e-3
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    fn = lambda: B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, y=y, prequant=True)  # noqa: E731
+    for _ in range(2):
+        fn()
+    ms = _events_time(fn, 5, torch.cuda.current_stream())
+    ops = 2.0 * M * N * K
+    res["square_8192"] = {"ms": round(ms, 4), "tops": round(ops / ms / 1e9, 1),
+                          "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4)}
+    return res
 
 
 def _timed(fn, iters=10):
