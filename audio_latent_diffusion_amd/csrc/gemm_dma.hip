@@ -616,14 +616,13 @@ void prep_cfg() {
 // dequantization with the MFMAs); a Q4 stage is smaller, so its 256 x 256
 // tile keeps three stages in flight.  The 256 x 192 tile (8 waves of
 // 64 x 96; int8, fp16 and 8-bit weight-only operands) exists for wave
-// quantization: hidden widths that are multiples of
-// 192 but not of 256 x (CUs / row tiles) leave a partial last round of
-// 256 x 256 tiles (N = 1536 at M = 8192 fills 192 of 256 CUs; N = 4608 runs
-// 2.25 rounds), which 256 x 192 tiles fill exactly.  The smaller tiles serve
-// short launches (M of a few hundred rows), where the launch is
-// latency-bound: four stages measured 3-13 % faster than five (128 x 64)
-// and eight (64 x 64) stages on those shapes in every operand mode,
-// K = 4096 included; three or fewer stages, and more, were slower
+// quantization: widths that are multiples of 192 can leave a partial last
+// round of 256 x 256 tiles (N = 1536 at M = 8192 fills 192 of 256 CUs,
+// N = 4608 runs 2.25 rounds) that 256 x 192 tiles fill exactly.  The
+// smaller tiles serve short launches (M of a few hundred rows), where the
+// launch is latency-bound: four stages measured 3-13 % faster than five
+// (128 x 64) and eight (64 x 64) stages on those shapes in every operand
+// mode, K = 4096 included; three or fewer stages, and more, were slower
 template <int MODE>
 struct Tiles {
   using T256 = Cfg<256, 256, (MODE == M_Q4 || MODE == M_Q8W) ? 3 : 2, MODE, 4>;
