@@ -542,8 +542,9 @@ def main():
     ap.add_argument("--leg", default="", help="counter legs only (gemm,serve,kernels,copy) for rocprofv3 runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requests shard across GPUs with no per-step exchange; see the design notes).", file=sys.stderr)
+        print("bench.py runs on one GPU only; --gpus N > 1 is not supported. The step shards by request "
+              "(each GPU would hold the weights and run its own requests' CFG pairs with no per-step "
+              "exchange), and no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
     if args.leg:
         counter_legs(args.leg.split(","), 20)

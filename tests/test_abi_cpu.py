@@ -214,3 +214,15 @@ def test_ddim_alpha_bar_host_helper_matches_oracle():
                               None) == L.ALD_E_INVALID
     assert lib.sampler_update(L.ALD_RENOISE_VP, FAKE, None, FAKE, None, 10, 64, 10, None, FAKE, None, None,
                               None) == L.ALD_E_INVALID
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with a message before
+    any device work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
