@@ -150,6 +150,14 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 // index cover distinct banks
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// 8-bit weight rows of the weight-only mode are 64 bytes (four 16-byte
+// chunks), two rows per 128-byte bank period: chunk c of row r sits at slot
+// c ^ ((r >> 1) & 3), so the 32 rows of one fragment read (same chunk) cover
+// all eight 16-byte positions of the period, four rows each, the fewest any
+// 64-byte row layout allows (with c ^ (r & 3) the slot repeats the row's
+// half of the period and only four positions were used, eight rows each)
+__device__ __forceinline__ int q8w_swz(int r) { return (r >> 1) & 3; }
+
 // The copies of one stage, dealt round-robin to the waves: X blocks, then W
 // blocks, then (Q4) scale copies.  Each lane keeps a 32-bit byte offset of
 // its source at K stage 0 from the operand's base pointer (uniform, so the
@@ -188,7 +196,7 @@ struct Loader {
         if constexpr (C::Q8W) {  // int8 W of fp16 X: 64 bytes per row and stage, 16 rows per block
           const int tr = bw * 16 + (lane >> 2);
           const int r = min(n0 + tr, g.N - 1);
-          off[i] = (uint32_t)r * (uint32_t)g.K + ((lane & 3) ^ (tr & 3)) * 16;
+          off[i] = (uint32_t)r * (uint32_t)g.K + ((lane & 3) ^ q8w_swz(tr)) * 16;
         } else if constexpr (!C::Q4) {  // int8 / fp16 W: same layout as X
           const int tr = bw * 8 + (lane >> 3);
           const int r = min(n0 + tr, g.N - 1);
@@ -331,7 +339,7 @@ __device__ __forceinline__ void mfma_slice(AccT<C> (&acc)[C::NJ][C::MI], const v
 // swizzled bytes per lane.  Q4 W: slice ks covers values 16 ks .. 16 ks + 15
 // of the stage, i.e. bytes 8 (ks % 2) .. 8 (ks % 2) + 7 of group ks / 2; lane
 // l takes the 4 bytes at 4 (l / 32) of those and its row's scale.  Q8W W
-// (64-byte rows, chunk c at slot c ^ (row & 3)): slice ks is chunk ks; lane l
+// (64-byte rows, chunk c at slot c ^ q8w_swz(row)): slice ks is chunk ks; lane l
 // takes its 8 bytes at 8 (l / 32) and widens them to fp16.
 template <class C>
 struct Frags {
@@ -356,7 +364,7 @@ struct Frags {
     for (int i = 0; i < C::MI; ++i) xf[i] = *reinterpret_cast<const v4i*>(sx + i * B32 + off[ks]);
     if constexpr (C::Q8W) {
       const int lr = threadIdx.x & 31, h = (threadIdx.x >> 5) & 1;
-      const uint8_t* sw = stage + C::W_OFF + (wn * C::WN + lr) * 64 + ((ks ^ (lr & 3)) << 4) + 8 * h;
+      const uint8_t* sw = stage + C::W_OFF + (wn * C::WN + lr) * 64 + ((ks ^ q8w_swz(lr)) << 4) + 8 * h;
 #pragma unroll
       for (int j = 0; j < C::NJ; ++j) wf[j] = widen_i8x8(*reinterpret_cast<const uint2*>(sw + j * 32 * 64));
     } else if constexpr (!C::Q4) {
