@@ -408,86 +408,84 @@ __device__ __forceinline__ float temb_value(float t, int col, int H) {
   return __builtin_amdgcn_sinf(turns);
 }
 
-constexpr int IP_T = 64;
+// 32 x 32 output tiles, 256 threads of 2 x 2 outputs: at the 512-token step
+// (hidden 1024) that is 512 workgroups over all CUs, where 64 x 64 tiles gave
+// 128 and spent their time in LDS reads and FMAs of 16 outputs per thread
+constexpr int IP_T = 32;
+constexpr int IP_K = 64;  // K slab per pass
 
 __global__ __launch_bounds__(256) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M, int C,
                                                      const uint16_t* __restrict__ w, int H,
                                                      const float* __restrict__ bias, const float* __restrict__ t_cur,
                                                      RowMap map, uint16_t* __restrict__ h) {
-  __shared__ float xs[IP_T][IP_T + 1];
-  __shared__ float wsm[IP_T][IP_T + 1];
+  __shared__ float xs[IP_T][IP_K + 1];
+  __shared__ float wsm[IP_T][IP_K + 1];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * IP_T, n0 = blockIdx.x * IP_T;
-  const int tr = (tid >> 4) * 4, tc = (tid & 15) * 4;
-  float acc[4][4];
+  const int n0 = blockIdx.x * IP_T;
+  const int tr = (tid >> 4) * 2, tc = (tid & 15) * 2;
+  // row tiles beyond the grid's y extent (65535) are walked with its stride
+  for (int m0 = blockIdx.y * IP_T; m0 < M; m0 += gridDim.y * IP_T) {
+    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    for (int k0 = 0; k0 < C; k0 += IP_K) {
+      // every load of the slab is issued before any is used: 2 x 16 bytes of
+      // latent and 16 bytes of weights per thread (C % 8 == 0)
+      float4 xv[2];
+      v4i wv;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 2; ++q) {
+        const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4, m = m0 + r;
+        xv[q] = (m < M && k0 + k < C) ? *reinterpret_cast<const float4*>(x + (m % n_tok) * C + k0 + k)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      {
+        const int r = tid >> 3, k = (tid & 7) * 8, n = n0 + r;
+        wv = (n < H && k0 + k < C) ? ld16(w + (int64_t)n * C + k0 + k) : v4i{0, 0, 0, 0};
+      }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int k0 = 0; k0 < C; k0 += IP_T) {
-    // every load of the stage is issued before any is used: 4 x 16 bytes of
-    // latent and 2 x 16 bytes of weights per thread (C % 8 == 0)
-    float4 xv[4];
-    v4i wv[2];
+      for (int q = 0; q < 2; ++q) {
+        const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4;
+        xs[r][k] = h2f(f2h(xv[q].x));
+        xs[r][k + 1] = h2f(f2h(xv[q].y));
+        xs[r][k + 2] = h2f(f2h(xv[q].z));
+        xs[r][k + 3] = h2f(f2h(xv[q].w));
+      }
+      {
+        const int r = tid >> 3, k = (tid & 7) * 8;
+        const uint16_t* hv = reinterpret_cast<const uint16_t*>(&wv);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4, m = m0 + r;
-      xv[q] = (m < M && k0 + k < C) ? *reinterpret_cast<const float4*>(x + (m % n_tok) * C + k0 + k)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int e = 0; e < 8; ++e) wsm[r][k + e] = h2f(hv[e]);
+      }
+      __syncthreads();
+#pragma unroll 16
+      for (int k = 0; k < IP_K; ++k) {
+        const float xa0 = xs[tr][k], xa1 = xs[tr + 1][k];
+        const float wb0 = wsm[tc][k], wb1 = wsm[tc + 1][k];
+        acc[0][0] = fmaf(xa0, wb0, acc[0][0]);
+        acc[0][1] = fmaf(xa0, wb1, acc[0][1]);
+        acc[1][0] = fmaf(xa1, wb0, acc[1][0]);
+        acc[1][1] = fmaf(xa1, wb1, acc[1][1]);
+      }
+      __syncthreads();
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = tid + 256 * q, r = i >> 3, k = (i & 7) * 8, n = n0 + r;
-      wv[q] = (n < H && k0 + k < C) ? ld16(w + (int64_t)n * C + k0 + k) : v4i{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 2; ++i) {
+      const int m = m0 + tr + i;
+      if (m >= M) continue;
+      const float t = t_cur[req_of(map, m)];
+      uint16_t o[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4;
-      xs[r][k] = h2f(f2h(xv[q].x));
-      xs[r][k + 1] = h2f(f2h(xv[q].y));
-      xs[r][k + 2] = h2f(f2h(xv[q].z));
-      xs[r][k + 3] = h2f(f2h(xv[q].w));
-    }
+      for (int j = 0; j < 2; ++j) {
+        const int n = min(n0 + tc + j, H - 1);
+        o[j] = f2h(acc[i][j] + bias[n] + temb_value(t, n, H));
+      }
+      uint16_t* hp = h + (int64_t)m * H + n0 + tc;
+      if (n0 + tc + 1 < H && (H & 1) == 0) {
+        *reinterpret_cast<uint32_t*>(hp) = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+      } else {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = tid + 256 * q, r = i >> 3, k = (i & 7) * 8;
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&wv[q]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wsm[r][k + e] = h2f(hv[e]);
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < IP_T; ++k) {
-      float xa[4], wb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = xs[tr + i][k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wb[j] = wsm[tc + j][k];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xa[i], wb[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + tr + i;
-    if (m >= M) continue;
-    const float t = t_cur[req_of(map, m)];
-    uint16_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = min(n0 + tc + j, H - 1);
-      o[j] = f2h(acc[i][j] + bias[n] + temb_value(t, n, H));
-    }
-    uint16_t* hp = h + (int64_t)m * H + n0 + tc;
-    if (n0 + tc + 3 < H && (H & 3) == 0) {
-      *reinterpret_cast<uint2*>(hp) = *reinterpret_cast<const uint2*>(o);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (n0 + tc + j < H) hp[j] = o[j];
+        for (int j = 0; j < 2; ++j)
+          if (n0 + tc + j < H) hp[j] = o[j];
+      }
     }
   }
 }
@@ -495,7 +493,7 @@ __global__ __launch_bounds__(256) void inproj_kernel(const float* __restrict__ x
 void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* w, int H, const float* bias,
                    const float* t_cur, RowMap map, uint16_t* h, hipStream_t st) {
   if (M <= 0 || H <= 0) return;
-  dim3 grid((unsigned)((H + IP_T - 1) / IP_T), (unsigned)((M + IP_T - 1) / IP_T));
+  dim3 grid((unsigned)((H + IP_T - 1) / IP_T), (unsigned)std::min<int64_t>((M + IP_T - 1) / IP_T, 65535));
   hipLaunchKernelGGL(inproj_kernel, grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
 }
 
