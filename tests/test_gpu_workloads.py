@@ -7,9 +7,11 @@ the 4-bit widths (hidden 2048, MLP 8192, 4 requests x 1024 tokens) in
 seconds, so those are checked element by element on the step's output latent
 (bar 2e-2, max |g - o| / max |o|).  The mixed warm-start batch runs the full
 16-block mid-size model on a 4-request packed sub-batch (lengths 128, 129,
-577, 1024; two cold, two warm, one re-noised inside the checked steps).  At
-the full 24-block serving size the oracle is out of reach; there the graph
-replay must equal eager execution bit for bit and the latent stays finite.
+577, 1024; two cold, two warm, one re-noised inside the checked steps); the
+full 32-request batch must give each request, bit for bit, what it gives
+alone.  At the full 24-block serving size the oracle is out of reach; there
+the graph replay must equal eager execution bit for bit and the latent stays
+finite.
 """
 import numpy as np
 import pytest
@@ -99,3 +101,40 @@ def test_serve_full_size_graph_equals_eager():
     assert a.tobytes() == b.tobytes()
     # the step moved the latent by the guided velocity times the step size
     assert not np.array_equal(a, inp.x)
+
+
+def test_mixed_full_batch_requests_independent():
+    """The full mixed warm-start batch (32 packed requests of 128..1024 latent
+    tokens on the mid-size model, about 37k CFG rows per launch, the launch
+    shapes the bench times): two steps, the warm half re-noised at the second
+    one, steering in both; cold and warm requests give, bit for bit, what each
+    gives run alone (its own small launches).  Exact int32 accumulators and
+    per-row, per-sequence kernels make the result independent of the batch."""
+    cfg = I.MIXED
+    model = runtime.DiTModel(cfg, I.make_params(cfg))
+    inp = I.make_mixed_inputs(cfg)
+    R = len(inp.seqlens)
+    warm = np.arange(R) >= R // 2
+    inp.start_step = np.where(warm, 1, 0)
+    inp.alpha[:2] = 0.5
+    packed = _runner(model, inp)
+    packed.step(0)
+    packed.step(1)
+    got = host(packed.x)
+    assert np.all(np.isfinite(got))
+    cu = np.concatenate([[0], np.cumsum(inp.seqlens)])
+    for r in (0, 13, R // 2, R - 1):
+        sl = slice(cu[r], cu[r + 1])
+        one = I.make_mixed_inputs(cfg.replace(requests=1), seqlens=inp.seqlens[r:r + 1], warm=warm[r:r + 1])
+        one.x = inp.x[sl]
+        one.x0 = inp.x0[sl]
+        one.eps = inp.eps[sl]
+        one.text = inp.text[[r, R + r]]
+        one.guidance = inp.guidance[r:r + 1]
+        one.alpha = inp.alpha[:, r:r + 1]
+        one.start_step = inp.start_step[r:r + 1]
+        one.direction = inp.direction
+        single = _runner(model, one)
+        single.step(0)
+        single.step(1)
+        assert host(single.x).tobytes() == got[sl].tobytes(), f"request {r} (warm {bool(warm[r])})"
