@@ -9,9 +9,9 @@ seconds, so those are checked element by element on the step's output latent
 16-block mid-size model on a 4-request packed sub-batch (lengths 128, 129,
 577, 1024; two cold, two warm, one re-noised inside the checked steps); the
 full 32-request batch must give each request, bit for bit, what it gives
-alone.  At the full 24-block serving size the oracle is out of reach; there
-the graph replay must equal eager execution bit for bit and the latent stays
-finite.
+alone.  At the full 24-block serving and 4-bit sizes the oracle is out of
+reach; there the graph replay must equal eager execution bit for bit and the
+latent stays finite.
 """
 import numpy as np
 import pytest
@@ -100,6 +100,27 @@ def test_serve_full_size_graph_equals_eager():
     assert np.all(np.isfinite(a))
     assert a.tobytes() == b.tobytes()
     # the step moved the latent by the guided velocity times the step size
+    assert not np.array_equal(a, inp.x)
+
+
+def test_q4_full_size_graph_equals_eager():
+    """The full 24-block 4-bit-weight model (hidden 2048, 4 requests x 1024
+    latent tokens = 8192 CFG rows): two steps replayed as one graph equal the
+    same two steps run eagerly, bit for bit, and the latent stays finite."""
+    cfg = I.Q4
+    p = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    model = runtime.DiTModel(cfg, p)
+    del p
+    eager = _runner(model, inp)
+    eager.step(0)
+    eager.step(1)
+    graph = _runner(model, inp)
+    graph.capture([0, 1])
+    graph.replay()
+    a, b = host(eager.x), host(graph.x)
+    assert np.all(np.isfinite(a))
+    assert a.tobytes() == b.tobytes()
     assert not np.array_equal(a, inp.x)
 
 
