@@ -334,9 +334,39 @@ def cpu_baseline(cfg, params, inp, resid, budget_s=20.0):
         if time.perf_counter() - t0 >= budget_s or n >= cfg.n_steps:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} denoise step(s) of the mid-size DiT (same shapes, CFG pair) in {dt:.1f} s; "
-                      f"fp64 numpy oracle with BLAS matmuls, text K/V and weight packing excluded"}
+    out = {"value": round(n / dt, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n} denoise step(s) of the mid-size DiT (same shapes, CFG pair) in {dt:.1f} s; "
+                     f"fp64 numpy oracle with BLAS matmuls, text K/V and weight packing excluded"}
+    out["tiny_step"] = tiny_oracle_rates()
+    return out
+
+
+def tiny_oracle_rates(reps=3):
+    """The oracle on one step of the tiny DiT (2 blocks, hidden 256, a CFG pair
+    of 64 latent tokens), on all host threads and on one: steps/s each."""
+    import ald_inputs as I
+    from oracle import ald_oracle as O
+    cfg = I.TINY
+    params = I.make_params(cfg)
+    inp = I.make_inputs(cfg)
+    om = O.prepare_model(cfg, params)
+    kv = O.text_kv(om, inp.text)
+
+    def rate():
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            O.dit_step(om, inp.x, inp.seqlens, kv, np.full(1, inp.t_grid[0], np.float32),
+                       np.full(1, inp.t_grid[1], np.float32), inp.guidance, inp.alpha[0], 5.0, inp.direction)
+        return round(reps / (time.perf_counter() - t0), 2)
+
+    res = {"all_threads_steps_per_s": rate()}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            res["one_thread_steps_per_s"] = rate()
+    except Exception:
+        res["one_thread_steps_per_s"] = None
+    return res
 
 
 GEMM_SOURCE = os.path.join(ROOT, "audio_latent_diffusion_amd", "csrc", "gemm_dma.hip")
