@@ -83,13 +83,19 @@ def test_mixed_warm_start_subbatch():
     assert err < TOL
 
 
-def test_serve_full_size_graph_equals_eager():
-    """The full 24-block serving model (8192 CFG rows, W8A8): two steps
-    replayed as one graph equal the same two steps run eagerly, bit for bit."""
-    cfg = I.SERVE
-    p = I.make_params(cfg)
+@pytest.fixture(scope="module")
+def serve_params():
+    return I.make_params(I.SERVE)
+
+
+@pytest.mark.parametrize("wmode", ["w8a8", "f16", "w8a16"])
+def test_serve_full_size_graph_equals_eager(serve_params, wmode):
+    """The full 24-block serving model (8192 CFG rows) in each weight
+    precision: two steps replayed as one graph equal the same two steps run
+    eagerly, bit for bit."""
+    cfg = I.SERVE.replace(wmode=wmode)
     inp = I.make_inputs(cfg)
-    model = runtime.DiTModel(cfg, p)
+    model = runtime.DiTModel(cfg, serve_params)
     eager = _runner(model, inp)
     eager.step(0)
     eager.step(1)
