@@ -61,7 +61,8 @@ class dit_block_weights(ctypes.Structure):
 
 class dit_weights(ctypes.Structure):
     _fields_ = [("blocks", POINTER(dit_block_weights)), ("w_in", c_void_p), ("b_in", c_void_p),
-                ("lnf_g", c_void_p), ("lnf_b", c_void_p), ("w_out", c_void_p), ("b_out", c_void_p)]
+                ("lnf_g", c_void_p), ("lnf_b", c_void_p), ("w_out", c_void_p), ("b_out", c_void_p),
+                ("kv_all", dit_linear)]
 
 
 class dit_step_args(ctypes.Structure):

@@ -75,7 +75,8 @@ struct StepBuffers {
   uint16_t* text_s;  // text site: steered text [2R*T, D_t]
   int8_t* tcodes;    // text site, W8A8: its int8 codes and row scales
   float* tscale;
-  uint16_t* kv;      // text site: one block's K/V of the steered text [2R*T, 2H]
+  uint16_t* kv;      // text site: K/V of the steered text, [2R*T, n_blocks*2H] (one block's in its first 2H
+                     // columns when the linears are not stacked)
 };
 
 bool steers(const dit_config* c, int site) { return c->steer_block >= 0 && c->steer_site == site; }
@@ -104,7 +105,7 @@ size_t carve_step(const dit_config* c, int64_t n_tok, int R, uint8_t* base, size
       t.tcodes = cv.take<int8_t>(rows_t * c->text_dim);
       t.tscale = cv.take<float>(rows_t);
     }
-    t.kv = cv.take<uint16_t>(rows_t * 2 * H);
+    t.kv = cv.take<uint16_t>(rows_t * 2 * H * std::max(1, c->n_blocks));  // every block's (stacked linears)
   }
   if (b) *b = t;
   return cv.off;
@@ -158,6 +159,10 @@ int check_weights(const dit_config* c, const dit_weights* w) {
       int e = check_linear(*p, c->wmode);
       if (e) return e;
     }
+  }
+  if (w->kv_all.w) {
+    int e = check_linear(w->kv_all, c->wmode);
+    if (e) return e;
   }
   return ALD_OK;
 }
@@ -300,11 +305,20 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     }
   }
 
+  // text site with the blocks' K/V linears stacked: the steered text's K/V of
+  // every block in one launch, block l's in columns [l 2H, (l + 1) 2H)
+  const bool kv_stacked = text_site && w->kv_all.w && c->n_blocks > 0;
+  const int64_t kv_ld = kv_stacked ? 2 * (int64_t)H * c->n_blocks : 2 * H;
+  if (kv_stacked)
+    run_linear(w->kv_all, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, (int)kv_ld, nullptr, 0, 0, b.kv,
+               kv_ld, st);
+
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   for (int l = 0; l < c->n_blocks; ++l) {
     const dit_block_weights& bw = w->blocks[l];
-    const uint16_t* kv = text_site ? b.kv : a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
-    if (text_site)  // the same linear dit_text_kv applies, on the steered text
+    const uint16_t* kv = text_site ? (kv_stacked ? b.kv + (int64_t)l * 2 * H : b.kv)
+                                   : a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
+    if (text_site && !kv_stacked)  // the same linear dit_text_kv applies, on the steered text
       run_linear(bw.kv, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, 2 * H, nullptr, 0, 0, b.kv, 2 * H, st);
     // self-attention
     ActIn in = layernorm_in(wm, b.h, M, H, bw.ln1_g, bw.ln1_b, c->ln_eps, b, st);
@@ -316,7 +330,7 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     // cross-attention to the text
     in = layernorm_in(wm, b.h, M, H, bw.ln2_g, bw.ln2_b, c->ln_eps, b, st);
     run_linear(bw.q, wm, in.A, in.lda, in.xs, M, H, H, nullptr, 0, 0, b.big, H, st);
-    AttnArgs ax{b.big, kv, kv + H, b.ao, H, 2 * H, H, nh, a->seq, T, cu2, nullptr, sl2};
+    AttnArgs ax{b.big, kv, kv + H, b.ao, H, text_site ? kv_ld : 2 * H, H, nh, a->seq, T, cu2, nullptr, sl2};
     launch_attn(ax, 2 * R, max_sq, st);
     in = quantize_in(wm, b.ao, H, M, H, b, st);
     run_linear(bw.ox, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st);

@@ -65,6 +65,15 @@ class DiTModel:
                     d[name] = (wt, None, bias)
                 del wt  # free-after-pack: the fp16 copy is released once packed
             self.blocks.append(d)
+        # the blocks' text K/V linears stacked along N (per-row formats stack
+        # as they are), for one-launch re-projection of a steered text
+        if self.blocks:
+            kvs = [d["kv"] for d in self.blocks]
+            self.kv_all = tuple(None if kvs[0][i] is None else torch.cat([k[i] for k in kvs]).contiguous()
+                                for i in range(3))
+        else:
+            self.kv_all = None
+        self.stack_kv = True
         torch.cuda.synchronize(dev)
         self._build_structs()
 
@@ -83,9 +92,13 @@ class DiTModel:
                 w, s, b = d[name]
                 setattr(bw, name, L.dit_linear(w.data_ptr(), None if s is None else s.data_ptr(), b.data_ptr()))
         self.c_blocks = arr
+        kv_all = L.dit_linear(None, None, None)
+        if self.kv_all is not None and self.stack_kv:
+            w, s, b = self.kv_all
+            kv_all = L.dit_linear(w.data_ptr(), None if s is None else s.data_ptr(), b.data_ptr())
         self.c_weights = L.dit_weights(ctypes.cast(arr, ctypes.POINTER(L.dit_block_weights)), self.w_in.data_ptr(),
                                        self.b_in.data_ptr(), self.lnf_g.data_ptr(), self.lnf_b.data_ptr(),
-                                       self.w_out.data_ptr(), self.b_out.data_ptr())
+                                       self.w_out.data_ptr(), self.b_out.data_ptr(), kv_all)
 
     def with_steer_block(self, steer_block: int) -> "DiTModel":
         """Same weights, another steered block (-1: none)."""
@@ -96,6 +109,16 @@ class DiTModel:
         other = object.__new__(DiTModel)
         other.__dict__.update(self.__dict__)
         other.cfg = self.cfg.replace(**kw)
+        other._build_structs()
+        return other
+
+    def with_stacked_kv(self, on: bool) -> "DiTModel":
+        """Same weights, with or without the stacked text K/V linears handed
+        to the step (a text-site step then re-projects the steered text in one
+        launch, or in one per block)."""
+        other = object.__new__(DiTModel)
+        other.__dict__.update(self.__dict__)
+        other.stack_kv = bool(on)
         other._build_structs()
         return other
 

@@ -47,7 +47,8 @@
 extern "C" {
 #endif
 
-#define ALD_VERSION 200  /* 200: steering sites, W8A16, the DDIM sampler (new config and step fields) */
+#define ALD_VERSION 201  /* 200: steering sites, W8A16, the DDIM sampler (new config and step fields);
+                            201: dit_weights.kv_all (stacked text K/V linears) */
 
 enum {
   ALD_OK = 0,
@@ -316,6 +317,13 @@ typedef struct {
   const float* lnf_b;
   const uint16_t* w_out; /* fp16 [C, H]  output projection           */
   const float* b_out;    /* fp32 [C]                                  */
+  /* Optional (w == NULL: unused): the text K/V linears of every block stacked
+   * along N, in the blocks' weight format: block l's output rows are
+   * [l * 2H, (l + 1) * 2H) of w [n_blocks * 2H, D_t], with its scales and
+   * biases in the same order.  With it, a step that steers the text site
+   * projects the steered text for every block in one launch instead of one
+   * per block; the results are bit-identical either way. */
+  dit_linear kv_all;
 } dit_weights;
 
 /* Arguments of one step over R requests (2R CFG rows).

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.ald_version() == 200
+    assert lib.ald_version() == 201
     assert lib.ald_strerror(L.ALD_E_WORKSPACE) == b"workspace too small"
 
 

@@ -335,3 +335,22 @@ def test_mid_graph_replays_equal_eager():
         g.replay()
         assert host(g.x).tobytes() == want
         torch.randn(1 << 20, device="cuda").sum().item()  # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("wmode", ["w8a8", "f16", "q4", "w8a16"])
+def test_text_site_stacked_kv_bit_identical(tiny, wmode):
+    """Text-site steering re-projects the steered text's K/V in the step: with
+    the blocks' K/V linears stacked (one launch for every block) the step is
+    bit-identical to one launch per block, in every weight precision."""
+    cfg, p, _, _ = tiny
+    cfg = cfg.replace(wmode=wmode, steer_site="text")
+    model = runtime.DiTModel(cfg, p)
+    inp = I.make_inputs(cfg)
+    unit = float(np.mean(np.linalg.norm(inp.text[:cfg.requests].reshape(-1, cfg.text_dim).astype(np.float64),
+                                        axis=1)))
+    outs = []
+    for m in (model, model.with_stacked_kv(False)):
+        run = _runner(m, inp, resid=unit)
+        run.step(0)
+        outs.append(host(run.x).tobytes())
+    assert outs[0] == outs[1]
