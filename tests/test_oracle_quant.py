@@ -244,3 +244,168 @@ def test_q8w_residual_and_gelu():
     from math import erf, sqrt
     ref = np.vectorize(lambda v: 0.5 * v * (1 + erf(v / sqrt(2))))(lin)
     assert np.allclose(O.q8w_linear(x, q, s, act=1).astype(np.float64), ref, atol=1e-3, rtol=1e-3)
+
+
+def _exact_linear(x, w, b=None, res=None):
+    """fp16(sum_k x[m, k] w[n, k] + b[n] + res[m, n]) from exact rational
+    arithmetic on the given operand values (a plain triple loop)."""
+    M, K = x.shape
+    N = w.shape[0]
+    out = np.empty((M, N), np.float16)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(x[m, k])) * Fraction(float(w[n, k]))
+            if b is not None:
+                acc += Fraction(float(b[n]))
+            if res is not None:
+                acc += Fraction(float(res[m, n]))
+            out[m, n] = np.float16(float(acc))  # acc is a short dyadic rational: float() is exact
+    return out
+
+
+@pytest.mark.parametrize("N", [48, 5])
+def test_f16_linear_brute_force_exact(N):
+    """fp16-weight linear against a plain triple loop, on a square (N = K) and
+    a non-square weight.  Dyadic operands keep every product and sum exact, so
+    the result must equal the exact value rounded once to fp16; the square
+    weight is far from symmetric, so x . W (no transpose) fails."""
+    rng = np.random.default_rng(21)
+    M, K = 6, 48
+    x = (rng.integers(-16, 17, size=(M, K)) / 8).astype(np.float16)
+    w = (rng.integers(-64, 65, size=(N, K)) / 256).astype(np.float16)
+    b = (rng.integers(-8, 9, size=N) / 16).astype(np.float32)
+    res = (rng.integers(-8, 9, size=(M, N)) / 4).astype(np.float16)
+    if N == K:
+        assert np.abs(w.astype(np.float64) - w.astype(np.float64).T).max() > 0.1
+        assert not np.array_equal(O.f16_linear(x, w), O.f16_linear(x, w.T.copy()))
+    assert np.array_equal(O.f16_linear(x, w, b), _exact_linear(x, w, b))
+    assert np.array_equal(O.f16_linear(x, w, b, residual=res), _exact_linear(x, w, b, res))
+    assert np.array_equal(O.f16_linear(x, w), _exact_linear(x, w))
+
+
+def _pack_nibbles(codes):
+    """Two's-complement nibbles by hand: byte j holds k = 2j low, 2j + 1 high."""
+    c = np.asarray(codes, np.int64) & 0xF
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("N", [64, 9])
+def test_q4_linear_brute_force_exact(N):
+    """4-bit-weight linear against a plain triple loop over the weight each
+    code and its group's scale stand for (q * s, exact here: powers of two),
+    on a square (N = K) and a non-square weight.  Every group of 32 along K has
+    its own scale, so a scale read from the wrong group or channel, a nibble
+    order swap or a transposed weight changes the result."""
+    rng = np.random.default_rng(22)
+    M, K = 5, 64
+    codes = rng.integers(-7, 8, size=(N, K))
+    scales = (2.0 ** -rng.integers(3, 9, size=(N, K // 32))).astype(np.float16)
+    assert (scales[:, 0] != scales[:, 1]).any()
+    packed = _pack_nibbles(codes)
+    w_eff = (codes * np.repeat(scales.astype(np.float64), 32, axis=1)).astype(np.float16)
+    x = (rng.integers(-16, 17, size=(M, K)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=N) / 16).astype(np.float32)
+    assert np.array_equal(O.q4_linear(x, packed, scales, b), _exact_linear(x, w_eff, b))
+    # swapped nibbles (k = 2j in the high half) would give another result
+    swapped = ((packed >> 4) | (packed << 4)).astype(np.uint8)
+    assert not np.array_equal(O.q4_linear(x, swapped, scales, b), _exact_linear(x, w_eff, b))
+
+
+def test_prepared_linear_modes_route_to_their_own_linear():
+    """Each weight mode of a prepared linear computes its own arithmetic:
+    W8A8 = exact product of both operands' q8 values; W8A16 = fp16 x times
+    the weight's q8 values; q4 = fp16 x times the 4-bit values; f16 = the
+    plain fp16 product (each against the brute-force loop), and the four
+    results differ pairwise, so a mode routed to another's linear fails."""
+    rng = np.random.default_rng(23)
+    M, K, N = 4, 64, 6
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    w = (0.05 * rng.standard_normal((N, K))).astype(np.float16)
+    b = (0.02 * rng.standard_normal(N)).astype(np.float32)
+    xq, xs = O.quantize_rows_q8(x)
+    wq, ws = O.quantize_rows_q8(w)
+    q4p, q4s = O.quantize_q4(w)
+
+    def deq(q, s):
+        return (q.astype(np.float64) * s.astype(np.float64)[:, None])
+
+    def exact(xv, wv):  # exact sum, then one rounding; operands as fp64 values
+        out = np.empty((M, N), np.float16)
+        for m in range(M):
+            for n in range(N):
+                acc = sum((Fraction(float(xv[m, k])) * Fraction(float(wv[n, k])) for k in range(K)), Fraction(0))
+                acc += Fraction(float(b[n]))
+                out[m, n] = np.float16(float(acc))
+        return out
+
+    want = {"f16": exact(x.astype(np.float64), w.astype(np.float64)),
+            "w8a16": exact(x.astype(np.float64), deq(wq, ws)),
+            "q4": exact(x.astype(np.float64), O.dequantize_q4(q4p, q4s).astype(np.float64)),
+            "w8a8": exact(deq(xq, xs), deq(wq, ws))}
+    got = {mode: O.prepare_linear(w, b, mode)(x) for mode in want}
+    for mode in want:
+        # fp64 evaluation of the exact sum may differ from it in the last bits,
+        # so allow one fp16 ulp where rounding sits on a tie
+        d = np.abs(got[mode].astype(np.float64) - want[mode].astype(np.float64))
+        assert np.all(d <= np.spacing(np.abs(want[mode])).astype(np.float64)), mode
+    modes = list(want)
+    for i in range(len(modes)):
+        for j in range(i + 1, len(modes)):
+            assert not np.array_equal(got[modes[i]], got[modes[j]]), (modes[i], modes[j])
+
+
+def test_prepared_linear_dispatch_calls(monkeypatch):
+    """The mode dispatch itself: each mode calls its own linear with that
+    mode's packed operands (and the residual and activation passed through)."""
+    calls = []
+    for name in ("w8a8_linear", "q4_linear", "q8w_linear", "f16_linear"):
+        def rec(*a, _n=name, **k):
+            calls.append((_n, a, k))
+            return O.W8A8Result(np.zeros(1), None, None, None) if _n == "w8a8_linear" else np.zeros(1)
+        monkeypatch.setattr(O, name, rec)
+    rng = np.random.default_rng(24)
+    w = (0.05 * rng.standard_normal((4, 64))).astype(np.float16)
+    b = np.zeros(4, np.float32)
+    x = rng.standard_normal((2, 64)).astype(np.float16)
+    r = rng.standard_normal((2, 4)).astype(np.float16)
+    expect = {"w8a8": "w8a8_linear", "w8a16": "q8w_linear", "q4": "q4_linear", "f16": "f16_linear"}
+    for mode, fn in expect.items():
+        p = O.prepare_linear(w, b, mode)
+        calls.clear()
+        p(x, residual=r, act=1)
+        assert len(calls) == 1 and calls[0][0] == fn, (mode, calls)
+        args = calls[0][1]
+        if mode in ("w8a8", "w8a16"):
+            assert args[1] is p.wq and args[2] is p.ws
+        elif mode == "q4":
+            assert args[1] is p.q4 and args[2] is p.q4s
+        else:
+            assert args[1] is p.w16
+        assert args[-2] is r and args[-1] == 1
+
+
+def test_planted_linear_mistakes_are_caught(monkeypatch):
+    """An f16 linear without the transpose, and a q4 mode that computes the
+    fp16 weights instead of the 4-bit ones, must each fail a pin above."""
+    real_f16 = O.f16_linear
+
+    def no_transpose(x16, w16, bias=None, residual=None, act=0):
+        y64 = np.asarray(x16, np.float16).astype(np.float64) @ np.asarray(w16, np.float16).astype(np.float64)
+        return O._epilogue(y64, bias, residual, act)
+
+    monkeypatch.setattr(O, "f16_linear", no_transpose)
+    with pytest.raises(AssertionError):
+        test_f16_linear_brute_force_exact(48)
+    monkeypatch.setattr(O, "f16_linear", real_f16)
+
+    def q4_as_f16(self, x16, residual=None, act=0):
+        if self.mode == "q4":
+            return real_f16(x16, self.w16, self.bias, residual, act)
+        return real_call(self, x16, residual, act)
+
+    real_call = O.PreparedLinear.__call__
+    monkeypatch.setattr(O.PreparedLinear, "__call__", q4_as_f16)
+    with pytest.raises(AssertionError):
+        test_prepared_linear_modes_route_to_their_own_linear()
