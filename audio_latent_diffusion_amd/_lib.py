@@ -31,7 +31,7 @@ EXPORTS = (
     "ald_strerror", "ald_version", "quantize_rows_q8", "quantize_q4", "ln_quant", "ln_f16",
     "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "steer_latent", "cfg_merge",
     "sampler_update", "ddim_alpha_bar", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
-    "dit_graph_launch", "dit_graph_destroy",
+    "dit_graph_launch", "dit_graph_nodes", "dit_graph_destroy",
 )
 
 
@@ -103,6 +103,7 @@ def _declare(lib):
         "dit_graph_capture": (I, [POINTER(dit_config), POINTER(dit_weights), POINTER(dit_step_args), I, V,
                                   c_size_t, V, POINTER(c_void_p)]),
         "dit_graph_launch": (I, [V, V]),
+        "dit_graph_nodes": (I, [V, POINTER(c_size_t)]),
         "dit_graph_destroy": (I, [V]),
     }
     for name, (res, args) in sig.items():

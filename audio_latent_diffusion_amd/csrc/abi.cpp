@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -31,14 +32,6 @@ inline int launched() {
   do {                    \
     if (!(cond)) return (code); \
   } while (0)
-
-// linear layer in any precision, A given as fp16 (F16/Q4) or int8 codes (W8A8)
-struct Lin {
-  int wmode;
-  const void* w;
-  const void* scale;
-  const float* bias;
-};
 
 int check_epilogue(int M, int N, const uint16_t* residual, int64_t ldr, int act, const uint16_t* y, int64_t ldy) {
   CHECK(act == ALD_ACT_NONE || act == ALD_ACT_GELU, ALD_E_INVALID);
@@ -167,10 +160,13 @@ int check_weights(const dit_config* c, const dit_weights* w) {
   return ALD_OK;
 }
 
-// y[M, N] = epilogue(A . W^T) for one block linear; A is int8 codes (W8A8,
-// with per-row scales xs) or fp16 (F16 / Q4 / W8A16)
-void run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, const float* xs, int M, int K, int N,
-                const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy, hipStream_t st) {
+int akind_of(int wmode) { return wmode == ALD_W8A8 ? A_I8 : A_F16; }
+int bkind_of(int wmode) { return wmode == ALD_Q4 ? B_Q4 : (wmode == ALD_F16 ? B_F16 : B_I8); }
+
+// the GEMM of one block linear: A is int8 codes (W8A8, with per-row scales
+// xs) or fp16 (F16 / Q4 / W8A16)
+GemmArgs linear_args(const dit_linear& L, int wmode, const void* A, int64_t lda, const float* xs, int M, int K,
+                     int N, const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy) {
   GemmArgs g;
   g.A = A;
   g.lda = lda;
@@ -187,16 +183,24 @@ void run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, cons
   if (wmode == ALD_W8A8) {
     g.epi.x_scale = xs;
     g.epi.w_scale = static_cast<const float*>(L.scale);
-    launch_gemm(A_I8, B_I8, g, st);
   } else if (wmode == ALD_Q4) {
     g.b_scale = static_cast<const uint16_t*>(L.scale);
-    launch_gemm(A_F16, B_Q4, g, st);
   } else if (wmode == ALD_W8A16) {
     g.epi.w_scale = static_cast<const float*>(L.scale);
-    launch_gemm(A_F16, B_I8, g, st);
-  } else {
-    launch_gemm(A_F16, B_F16, g, st);
   }
+  return g;
+}
+
+// y[M, N] = epilogue(A . W^T); false (nothing enqueued) when no kernel covers it
+bool run_linear(const dit_linear& L, int wmode, const void* A, int64_t lda, const float* xs, int M, int K, int N,
+                const uint16_t* residual, int64_t ldr, int act, uint16_t* y, int64_t ldy, hipStream_t st) {
+  return launch_gemm(akind_of(wmode), bkind_of(wmode),
+                     linear_args(L, wmode, A, lda, xs, M, K, N, residual, ldr, act, y, ldy), st);
+}
+
+bool linear_ok(const dit_linear& L, int wmode, const void* A, int M, int K, int N) {
+  return gemm_supported(akind_of(wmode), bkind_of(wmode),
+                        linear_args(L, wmode, A, K, nullptr, M, K, N, nullptr, 0, 0, nullptr, 0));
 }
 
 // activation input of a linear: W8A8 quantizes per token, else fp16 as is
@@ -224,6 +228,40 @@ ActIn layernorm_in(int wmode, const uint16_t* x, int M, int H, const float* g, c
   return {b.u, H, nullptr};
 }
 
+// Every GEMM the step will launch has a kernel for its operands and shape
+// (the 8-bit weight-only operand pair exists only in the direct-to-LDS
+// kernel, which addresses operands with 32-bit byte offsets); checked before
+// any launch so that an unsupported step enqueues nothing.
+int check_step_gemms(const dit_config* c, const dit_weights* w, int M, int rows_t, const StepBuffers& b) {
+  const int wm = c->wmode, H = c->hidden, F = c->mlp, Dt = c->text_dim;
+  const bool q = wm == ALD_W8A8;
+  const void* ln_in = q ? static_cast<const void*>(b.codes) : b.u;    // after a LayerNorm
+  const void* ao_in = q ? static_cast<const void*>(b.codes) : b.ao;   // after an attention
+  const void* mlp_in = q ? static_cast<const void*>(b.codes) : b.big; // after the GELU
+  bool ok = true;
+  for (int l = 0; l < c->n_blocks; ++l) {
+    const dit_block_weights& bw = w->blocks[l];
+    ok = ok && linear_ok(bw.qkv, wm, ln_in, M, H, 3 * H) && linear_ok(bw.o, wm, ao_in, M, H, H) &&
+         linear_ok(bw.q, wm, ln_in, M, H, H) && linear_ok(bw.ox, wm, ao_in, M, H, H) &&
+         linear_ok(bw.up, wm, ln_in, M, H, F) && linear_ok(bw.down, wm, mlp_in, M, F, H);
+  }
+  if (steers(c, ALD_SITE_TEXT) && c->n_blocks > 0) {
+    const void* tin = q ? static_cast<const void*>(b.tcodes) : b.text_s;
+    if (w->kv_all.w) ok = ok && linear_ok(w->kv_all, wm, tin, rows_t, Dt, 2 * H * c->n_blocks);
+    else
+      for (int l = 0; l < c->n_blocks; ++l) ok = ok && linear_ok(w->blocks[l].kv, wm, tin, rows_t, Dt, 2 * H);
+  }
+  GemmArgs out;  // output projection: fp16 x fp16
+  out.A = b.u;
+  out.lda = H;
+  out.B = w->w_out;
+  out.M = M;
+  out.N = c->channels;
+  out.K = H;
+  ok = ok && gemm_supported(A_F16, B_F16, out);
+  return ok ? ALD_OK : ALD_E_UNSUPPORTED;
+}
+
 int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args* a, void* ws, size_t ws_bytes,
                  hipStream_t st) {
   int e = check_config(c);
@@ -232,7 +270,9 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   if (e) return e;
   CHECK(a, ALD_E_INVALID);
   CHECK(a->R > 0 && a->n_tok > 0, ALD_E_INVALID);
-  CHECK(a->x && al16(a->x) && a->text_kv && al16(a->text_kv), ALD_E_INVALID);
+  CHECK(a->x && al16(a->x), ALD_E_INVALID);
+  // the text site recomputes the K/V from the steered text: text_kv unused
+  if (!steers(c, ALD_SITE_TEXT)) CHECK(a->text_kv && al16(a->text_kv), ALD_E_INVALID);
   CHECK(a->t_cur && a->t_next && a->guidance, ALD_E_INVALID);
   const bool ddim = c->sampler == ALD_SAMPLER_DDIM;
   if (ddim) CHECK(a->abar_cur && a->abar_next, ALD_E_INVALID);
@@ -249,16 +289,12 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   CHECK(2 * a->n_tok <= INT32_MAX, ALD_E_UNSUPPORTED);
   // the latent kernels index vectors of 4 values with 32-bit arithmetic
   CHECK(a->n_tok * (c->channels / 4) < ((int64_t)1 << 31), ALD_E_UNSUPPORTED);
-  // W8A16: the DMA GEMM addresses activations with 32-bit byte offsets
-  if (c->wmode == ALD_W8A16) {
-    CHECK(2 * a->n_tok * 2 * (int64_t)std::max(c->hidden, c->mlp) < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
-    if (steers(c, ALD_SITE_TEXT))
-      CHECK(2 * (int64_t)a->R * c->text_tokens * c->text_dim * 2 < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
-  }
   CHECK(ws && al16(ws), ALD_E_INVALID);
   StepBuffers b;
   size_t need = carve_step(c, a->n_tok, a->R, static_cast<uint8_t*>(ws), ws_bytes, &b);
   CHECK(need <= ws_bytes, ALD_E_WORKSPACE);
+  e = check_step_gemms(c, w, (int)(2 * a->n_tok), 2 * a->R * c->text_tokens, b);
+  if (e) return e;
   prepare();
 
   const int H = c->hidden, F = c->mlp, C = c->channels, T = c->text_tokens, nh = c->n_heads;
@@ -310,8 +346,9 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
   const bool kv_stacked = text_site && w->kv_all.w && c->n_blocks > 0;
   const int64_t kv_ld = kv_stacked ? 2 * (int64_t)H * c->n_blocks : 2 * H;
   if (kv_stacked)
-    run_linear(w->kv_all, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, (int)kv_ld, nullptr, 0, 0, b.kv,
-               kv_ld, st);
+    CHECK(run_linear(w->kv_all, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, (int)kv_ld, nullptr, 0, 0, b.kv,
+                     kv_ld, st),
+          ALD_E_UNSUPPORTED);
 
   const float sl2 = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e)
   for (int l = 0; l < c->n_blocks; ++l) {
@@ -319,26 +356,27 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     const uint16_t* kv = text_site ? (kv_stacked ? b.kv + (int64_t)l * 2 * H : b.kv)
                                    : a->text_kv + (int64_t)l * (2 * (int64_t)R * T) * (2 * H);
     if (text_site && !kv_stacked)  // the same linear dit_text_kv applies, on the steered text
-      run_linear(bw.kv, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, 2 * H, nullptr, 0, 0, b.kv, 2 * H, st);
+      CHECK(run_linear(bw.kv, wm, tin.A, tin.lda, tin.xs, rows_t, c->text_dim, 2 * H, nullptr, 0, 0, b.kv, 2 * H, st),
+            ALD_E_UNSUPPORTED);
     // self-attention
     ActIn in = layernorm_in(wm, b.h, M, H, bw.ln1_g, bw.ln1_b, c->ln_eps, b, st);
-    run_linear(bw.qkv, wm, in.A, in.lda, in.xs, M, H, 3 * H, nullptr, 0, 0, b.big, 3 * H, st);
+    CHECK(run_linear(bw.qkv, wm, in.A, in.lda, in.xs, M, H, 3 * H, nullptr, 0, 0, b.big, 3 * H, st), ALD_E_UNSUPPORTED);
     AttnArgs at{b.big, b.big + H, b.big + 2 * H, b.ao, 3 * H, 3 * H, H, nh, a->seq, a->seq, cu2, cu2, sl2};
     launch_attn(at, 2 * R, max_sq, st);
     in = quantize_in(wm, b.ao, H, M, H, b, st);
-    run_linear(bw.o, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st);
+    CHECK(run_linear(bw.o, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st), ALD_E_UNSUPPORTED);
     // cross-attention to the text
     in = layernorm_in(wm, b.h, M, H, bw.ln2_g, bw.ln2_b, c->ln_eps, b, st);
-    run_linear(bw.q, wm, in.A, in.lda, in.xs, M, H, H, nullptr, 0, 0, b.big, H, st);
+    CHECK(run_linear(bw.q, wm, in.A, in.lda, in.xs, M, H, H, nullptr, 0, 0, b.big, H, st), ALD_E_UNSUPPORTED);
     AttnArgs ax{b.big, kv, kv + H, b.ao, H, text_site ? kv_ld : 2 * H, H, nh, a->seq, T, cu2, nullptr, sl2};
     launch_attn(ax, 2 * R, max_sq, st);
     in = quantize_in(wm, b.ao, H, M, H, b, st);
-    run_linear(bw.ox, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st);
+    CHECK(run_linear(bw.ox, wm, in.A, in.lda, in.xs, M, H, H, b.h, H, 0, b.h, H, st), ALD_E_UNSUPPORTED);
     // GELU MLP
     in = layernorm_in(wm, b.h, M, H, bw.ln3_g, bw.ln3_b, c->ln_eps, b, st);
-    run_linear(bw.up, wm, in.A, in.lda, in.xs, M, H, F, nullptr, 0, ALD_ACT_GELU, b.big, F, st);
+    CHECK(run_linear(bw.up, wm, in.A, in.lda, in.xs, M, H, F, nullptr, 0, ALD_ACT_GELU, b.big, F, st), ALD_E_UNSUPPORTED);
     in = quantize_in(wm, b.big, F, M, F, b, st);
-    run_linear(bw.down, wm, in.A, in.lda, in.xs, M, F, H, b.h, H, 0, b.h, H, st);
+    CHECK(run_linear(bw.down, wm, in.A, in.lda, in.xs, M, F, H, b.h, H, 0, b.h, H, st), ALD_E_UNSUPPORTED);
     if (steers(c, ALD_SITE_RESIDUAL) && l == c->steer_block) {
       if (a->block_norms) launch_row_norms(b.h, H, M, H, a->block_norms, st);
       launch_steer(b.h, H, M, H, map, a->alpha, a->resid_norm, a->direction, project, st);
@@ -359,7 +397,7 @@ int enqueue_step(const dit_config* c, const dit_weights* w, const dit_step_args*
     g.epi.bias = w->b_out;
     g.epi.y = v;
     g.epi.ldy = C;
-    launch_gemm(A_F16, B_F16, g, st);
+    CHECK(launch_gemm(A_F16, B_F16, g, st), ALD_E_UNSUPPORTED);
   }
   if (ddim) launch_cfg_ddim(v, a->x, n_tok, C, map, a->guidance, a->abar_cur, a->abar_next, a->active, st);
   else launch_cfg_euler(v, a->x, n_tok, C, map, a->guidance, a->t_cur, a->t_next, a->active, st);
@@ -447,8 +485,6 @@ int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, 
   if (!(flags & ALD_PREQUANT)) {
     CHECK(x && al16(x) && ldx >= K && ldx % 8 == 0, ALD_E_INVALID);
   }
-  prepare();
-  if (!(flags & ALD_PREQUANT)) launch_row_quant(x, ldx, M, K, xq, K, x_scale, stream);
   GemmArgs g;
   g.A = xq;
   g.lda = K;
@@ -465,7 +501,10 @@ int w8a8_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, 
   g.epi.ldy = ldy;
   g.epi.acc = acc;
   g.epi.act = act;
-  launch_gemm(A_I8, B_I8, g, stream);
+  CHECK(gemm_supported(A_I8, B_I8, g), ALD_E_UNSUPPORTED);
+  prepare();
+  if (!(flags & ALD_PREQUANT)) launch_row_quant(x, ldx, M, K, xq, K, x_scale, stream);
+  CHECK(launch_gemm(A_I8, B_I8, g, stream), ALD_E_UNSUPPORTED);
   return launched();
 }
 
@@ -493,10 +532,10 @@ int q8w_linear(const uint16_t* x, int64_t ldx, int M, int K, const int8_t* wq, c
   g.epi.y = y;
   g.epi.ldy = ldy;
   g.epi.act = act;
-  // only the DMA GEMM implements this operand pair
-  CHECK(gemm_dma_applicable(A_F16, B_I8, g), ALD_E_UNSUPPORTED);
+  // only the direct-to-LDS GEMM implements this operand pair
+  CHECK(gemm_supported(A_F16, B_I8, g), ALD_E_UNSUPPORTED);
   prepare();
-  launch_gemm(A_F16, B_I8, g, stream);
+  CHECK(launch_gemm(A_F16, B_I8, g, stream), ALD_E_UNSUPPORTED);
   return launched();
 }
 
@@ -525,7 +564,8 @@ int q4_linear(const uint16_t* x, int64_t ldx, int M, int K, const uint8_t* wq4, 
   g.epi.y = y;
   g.epi.ldy = ldy;
   g.epi.act = act;
-  launch_gemm(A_F16, B_Q4, g, stream);
+  CHECK(gemm_supported(A_F16, B_Q4, g), ALD_E_UNSUPPORTED);
+  CHECK(launch_gemm(A_F16, B_Q4, g, stream), ALD_E_UNSUPPORTED);
   return launched();
 }
 
@@ -551,7 +591,8 @@ int f16_linear(const uint16_t* x, int64_t ldx, int M, int K, const uint16_t* w, 
   g.epi.y = y;
   g.epi.ldy = ldy;
   g.epi.act = act;
-  launch_gemm(A_F16, B_F16, g, stream);
+  CHECK(gemm_supported(A_F16, B_F16, g), ALD_E_UNSUPPORTED);
+  CHECK(launch_gemm(A_F16, B_F16, g, stream), ALD_E_UNSUPPORTED);
   return launched();
 }
 
@@ -561,6 +602,9 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t q_
              hipStream_t stream) {
   CHECK(n_heads > 0 && batch >= 0, ALD_E_INVALID);
   CHECK(head_dim == 64, ALD_E_UNSUPPORTED);
+  // the softmax keeps a running reference maximum in units of the scaled
+  // score, which assumes a finite positive scale
+  CHECK(std::isfinite(scale) && scale > 0.0f, ALD_E_INVALID);
   if (batch == 0) return ALD_OK;
   CHECK(q && k && v && out && al16(q) && al16(k) && al16(v) && al16(out), ALD_E_INVALID);
   const int64_t width = (int64_t)n_heads * 64;
@@ -676,19 +720,16 @@ int dit_text_kv(const dit_config* c, const dit_weights* w, const uint16_t* text,
   const int Dt = c->text_dim, H = c->hidden;
   size_t need = align256((size_t)rows * Dt) + align256((size_t)rows * 4);
   CHECK(need <= ws_bytes, ALD_E_WORKSPACE);
-  if (c->wmode == ALD_W8A16) CHECK((int64_t)rows * Dt * 2 < ((int64_t)1 << 32), ALD_E_UNSUPPORTED);
-  prepare();
   int8_t* codes = static_cast<int8_t*>(ws);
   float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align256((size_t)rows * Dt));
-  const void* A = text;
-  int64_t lda = Dt;
-  if (c->wmode == ALD_W8A8) {
-    launch_row_quant(text, Dt, rows, Dt, codes, Dt, xs, stream);
-    A = codes;
-  }
+  const void* A = c->wmode == ALD_W8A8 ? static_cast<const void*>(codes) : text;
+  for (int l = 0; l < c->n_blocks; ++l) CHECK(linear_ok(w->blocks[l].kv, c->wmode, A, rows, Dt, 2 * H), ALD_E_UNSUPPORTED);
+  prepare();
+  if (c->wmode == ALD_W8A8) launch_row_quant(text, Dt, rows, Dt, codes, Dt, xs, stream);
   for (int l = 0; l < c->n_blocks; ++l)
-    run_linear(w->blocks[l].kv, c->wmode, A, lda, xs, rows, Dt, 2 * H, nullptr, 0, 0,
-               kv_out + (int64_t)l * rows * 2 * H, 2 * H, stream);
+    CHECK(run_linear(w->blocks[l].kv, c->wmode, A, Dt, xs, rows, Dt, 2 * H, nullptr, 0, 0,
+                     kv_out + (int64_t)l * rows * 2 * H, 2 * H, stream),
+          ALD_E_UNSUPPORTED);
   return launched();
 }
 
@@ -736,6 +777,15 @@ int dit_graph_launch(void* graph, hipStream_t stream) {
   CHECK(graph, ALD_E_INVALID);
   GraphHandle* gh = static_cast<GraphHandle*>(graph);
   return hipGraphLaunch(gh->exec, stream) == hipSuccess ? ALD_OK : ALD_E_LAUNCH;
+}
+
+int dit_graph_nodes(void* graph, size_t* n_nodes) {
+  CHECK(graph && n_nodes, ALD_E_INVALID);
+  GraphHandle* gh = static_cast<GraphHandle*>(graph);
+  size_t n = 0;
+  if (hipGraphGetNodes(gh->graph, nullptr, &n) != hipSuccess) return ALD_E_LAUNCH;
+  *n_nodes = n;
+  return ALD_OK;
 }
 
 int dit_graph_destroy(void* graph) {

@@ -311,11 +311,19 @@ void gemm_prepare() {
   set_lds<A_F16, B_Q4, 128, 64>();
 }
 
-void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
-  if (g.M <= 0 || g.N <= 0) return;
+bool gemm_supported(int akind, int bkind, const GemmArgs& g) {
+  if (g.M <= 0 || g.N <= 0) return true;  // nothing to compute
+  if (gemm_dma_applicable(akind, bkind, g)) return true;
+  // the register-staged kernel covers int8 x int8, fp16 x fp16 and fp16 x 4-bit;
+  // fp16 x int8 (8-bit weight-only) exists only in the direct-to-LDS kernel
+  return (akind == A_I8 && bkind == B_I8) || (akind == A_F16 && (bkind == B_F16 || bkind == B_Q4));
+}
+
+bool launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0) return true;
   if (gemm_dma_applicable(akind, bkind, g)) {
     launch_gemm_dma(akind, bkind, g, st);
-    return;
+    return true;
   }
   const bool narrow = g.N <= 64;
   if (akind == A_I8 && bkind == B_I8) {
@@ -327,7 +335,10 @@ void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st) {
   } else if (akind == A_F16 && bkind == B_Q4) {
     if (narrow) launch_tile<A_F16, B_Q4, 128, 64>(g, st);
     else launch_tile<A_F16, B_Q4, 128, 128>(g, st);
+  } else {
+    return false;  // no kernel for this operand pair and shape: nothing enqueued
   }
+  return true;
 }
 
 }  // namespace ald

@@ -280,9 +280,13 @@ __device__ __forceinline__ void unpack_h8(uint4 raw, float f[8]) {
 // 8 packed two's-complement nibbles (value e in bits 4e..4e+3) -> 8 x
 // fp16(q * s).  With the sign bit flipped a nibble is q + 8; the fp16 with
 // bit pattern 0x6400 | (q + 8) is 1024 + q + 8, so subtracting 1032 gives q
-// exactly, and the product with s is rounded once.  v_perm_b32 pairs
-// value 2i (byte i of the even nibbles) with value 2i + 1 (byte i of the odd
-// ones) as the two halves of register i.
+// exactly, and the product with s is rounded once.  (Placing small integers
+// under a fixed fp16 exponent and subtracting the offset is the
+// integer-to-half conversion without conversion instructions described by
+// Kim et al., "Who Says Elephants Can't Run: Bringing Large Scale MoE Models
+// into Cloud Scale Production", 2022.)  v_perm_b32 pairs value 2i (byte i of
+// the even nibbles) with value 2i + 1 (byte i of the odd ones) as the two
+// halves of register i.
 __device__ __forceinline__ v4i dequant8(uint32_t packed, v2h s2) {
   const uint32_t w = packed ^ 0x88888888u;
   const uint32_t ev = w & 0x0F0F0F0Fu;

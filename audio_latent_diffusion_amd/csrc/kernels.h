@@ -57,7 +57,10 @@ void launch_ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* g,
                    uint16_t* y, int64_t ldy, hipStream_t st);
 void launch_q4_pack(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* scales, hipStream_t st);
 
-void launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st);
+// false (and nothing enqueued) when no kernel covers the operand pair and
+// shape; gemm_supported answers the same question without launching
+bool launch_gemm(int akind, int bkind, const GemmArgs& g, hipStream_t st);
+bool gemm_supported(int akind, int bkind, const GemmArgs& g);
 void gemm_prepare();  // one-time kernel attributes (large dynamic LDS)
 
 // pipelined direct-to-LDS MFMA GEMM (gemm_dma.hip): int8 x int8, fp16 x fp16 or

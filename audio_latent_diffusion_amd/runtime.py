@@ -264,6 +264,12 @@ class StepRunner:
         self._graphs.append(handle)
         return handle
 
+    def graph_nodes(self, handle: ctypes.c_void_p) -> int:
+        """Kernel launches recorded in a captured graph."""
+        n = ctypes.c_size_t()
+        L.check("dit_graph_nodes", L.lib().dit_graph_nodes(handle, ctypes.byref(n)))
+        return int(n.value)
+
     def launch_graph(self, handle: ctypes.c_void_p) -> None:
         L.check("dit_graph_launch", L.lib().dit_graph_launch(handle, B._stream()))
 

@@ -47,13 +47,16 @@
 extern "C" {
 #endif
 
-#define ALD_VERSION 201  /* 200: steering sites, W8A16, the DDIM sampler (new config and step fields);
-                            201: dit_weights.kv_all (stacked text K/V linears) */
+#define ALD_VERSION 202  /* 200: steering sites, W8A16, the DDIM sampler (new config and step fields);
+                            201: dit_weights.kv_all (stacked text K/V linears);
+                            202: dit_graph_nodes; attn_fwd rejects a non-positive scale; text_kv
+                                 optional under text-site steering */
 
 enum {
   ALD_OK = 0,
   ALD_E_INVALID = -1,      /* null pointer, misalignment, negative size, bad enum   */
-  ALD_E_UNSUPPORTED = -2,  /* shape the kernels do not cover (e.g. head_dim != 64)  */
+  ALD_E_UNSUPPORTED = -2,  /* shape or operand pair the kernels do not cover
+                              (e.g. head_dim != 64)                              */
   ALD_E_WORKSPACE = -3,    /* workspace smaller than dit_workspace_size()          */
   ALD_E_LAUNCH = -4        /* the HIP runtime reported an error after a launch      */
 };
@@ -163,16 +166,19 @@ int q8w_linear(const uint16_t* x, int64_t ldx, int M, int K,
                const float* bias, const uint16_t* residual, int64_t ldr,
                int act, uint16_t* y, int64_t ldy, hipStream_t stream);
 
-/* 4-bit weight-only linear: W = fp16(q * s) dequantized inside the GEMM main
- * loop, fp16 x fp16 -> fp32 on MFMA.  wq4 [N, K/2], w_scale [N, K/32] fp16
- * (layout of quantize_q4).  K % 32 == 0. */
+/* 4-bit weight-only linear (aria, Section III-A: the weights stored as 4-bit
+ * integers, the rung of the precision ladder that fits the larger model on
+ * small devices; the activations stay half precision): W = fp16(q * s)
+ * dequantized inside the GEMM main loop, fp16 x fp16 -> fp32 on MFMA.
+ * wq4 [N, K/2], w_scale [N, K/32] fp16 (layout of quantize_q4).  K % 32 == 0. */
 int q4_linear(const uint16_t* x, int64_t ldx, int M, int K,
               const uint8_t* wq4, const uint16_t* w_scale, int N,
               const float* bias, const uint16_t* residual, int64_t ldr,
               int act, uint16_t* y, int64_t ldy, hipStream_t stream);
 
-/* fp16-weight linear (aria: half-precision matrix multiplies), fp32
- * accumulation.  w [N, K] fp16 dense.  K % 8 == 0. */
+/* fp16-weight linear (aria, Section III-A: the GPU path's half-precision
+ * tensor-core matrix multiplies), fp32 accumulation.  w [N, K] fp16 dense.
+ * K % 8 == 0. */
 int f16_linear(const uint16_t* x, int64_t ldx, int M, int K,
                const uint16_t* w, int N, const float* bias,
                const uint16_t* residual, int64_t ldr, int act, uint16_t* y,
@@ -192,7 +198,8 @@ int f16_linear(const uint16_t* x, int64_t ldx, int M, int K,
  *   cu_seqlens_k ? [cu_k[b], cu_k[b+1]) : [b * Sk, (b+1) * Sk).
  * With cu_seqlens, max_sq / max_sk bound the lengths (host values); lengths
  * above them are a caller error (rows beyond are not computed).  A sequence
- * with no keys writes zeros.  scale multiplies q.k (e.g. 1/sqrt(64)).
+ * with no keys writes zeros.  scale multiplies q.k (e.g. 1/sqrt(64)); it must
+ * be finite and > 0 (ALD_E_INVALID otherwise).
  * head_dim must be 64 (ALD_E_UNSUPPORTED otherwise); strides % 8 == 0. */
 int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
              int64_t q_stride, int64_t kv_stride, int n_heads, int head_dim,
@@ -333,7 +340,8 @@ typedef struct {
  * All per-request arrays are device fp32 [R] read at execution time. */
 typedef struct {
   float* x;                   /* fp32 [n_tok, C] latent state, updated in place */
-  const uint16_t* text_kv;    /* fp16 [n_blocks][2R * T, 2H] from dit_text_kv */
+  const uint16_t* text_kv;    /* fp16 [n_blocks][2R * T, 2H] from dit_text_kv;
+                                 unused (may be NULL) with text-site steering    */
   int R;
   int seq;                    /* tokens per request when cu_seqlens == NULL     */
   const int32_t* cu_seqlens;  /* int32 [R + 1] or NULL                          */
@@ -410,6 +418,9 @@ int dit_graph_capture(const dit_config* cfg, const dit_weights* w,
                       const dit_step_args* args, int n_steps, void* ws,
                       size_t ws_bytes, hipStream_t stream, void** graph_out);
 int dit_graph_launch(void* graph, hipStream_t stream);
+/* Number of nodes (kernel launches: the step records no copies or memsets)
+ * in a captured graph, written to *n_nodes (host). */
+int dit_graph_nodes(void* graph, size_t* n_nodes);
 int dit_graph_destroy(void* graph);
 
 #ifdef __cplusplus

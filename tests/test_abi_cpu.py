@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.ald_version() == 201
+    assert lib.ald_version() == 202
     assert lib.ald_strerror(L.ALD_E_WORKSPACE) == b"workspace too small"
 
 
@@ -178,7 +178,58 @@ def test_step_validation():
     assert lib.dit_graph_capture(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), 0, FAKE, need, FAKE,
                                  ctypes.byref(h)) == L.ALD_E_INVALID
     assert lib.dit_graph_launch(None, None) == L.ALD_E_INVALID
+    n = ctypes.c_size_t()
+    assert lib.dit_graph_nodes(None, ctypes.byref(n)) == L.ALD_E_INVALID
     assert lib.dit_graph_destroy(None) == L.ALD_E_INVALID
+
+
+def test_attention_scale_must_be_finite_and_positive():
+    """The softmax's running reference maximum is kept in units of the scaled
+    score: a zero, negative or non-finite scale is rejected before launch."""
+    lib = L.lib()
+    for scale in (0.0, -0.125, float("nan"), float("inf")):
+        assert lib.attn_fwd(FAKE, FAKE, FAKE, 128, 128, 2, 64, 1, 8, 8, None, None, 0, 0, scale, FAKE, 128,
+                            None) == L.ALD_E_INVALID, scale
+
+
+def test_text_kv_required_only_where_read():
+    """text_kv is read unless the step steers the text site (which recomputes
+    the K/V from the steered text): NULL is invalid at the residual site and
+    passes validation at the text site (here the step then stops at the
+    too-small workspace, before any launch)."""
+    lib = L.lib()
+    w, arr = _weights(2)
+    a = L.dit_step_args(x=FAKE, text_kv=None, R=1, seq=64, n_tok=64, max_seq=64, t_cur=FAKE, t_next=FAKE,
+                        guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE, text=FAKE)
+    c = _cfg()
+    need = lib.dit_workspace_size(ctypes.byref(c), 64, 1)
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_INVALID
+    txt = _cfg(steer_site=L.ALD_SITE_TEXT)
+    need_t = lib.dit_workspace_size(ctypes.byref(txt), 64, 1)
+    assert lib.dit_step(ctypes.byref(txt), ctypes.byref(w), ctypes.byref(a), FAKE, need_t - 1,
+                        None) == L.ALD_E_WORKSPACE
+
+
+def test_w8a16_stacked_text_kv_weight_bytes_checked():
+    """The 8-bit weight-only GEMM addresses its weights with 32-bit byte
+    offsets: stacked text K/V linears of n_blocks * 2H * D_t >= 2^32 bytes have
+    no kernel, and the text-site step says so before any launch (one block's
+    K/V linear, 2H * D_t bytes, is fine)."""
+    lib = L.lib()
+    nb, H, Dt = 32, 8192, 8192
+    c = _cfg(n_blocks=nb, hidden=H, n_heads=H // 64, mlp=H, text_dim=Dt, text_tokens=32, wmode=L.ALD_W8A16,
+             steer_site=L.ALD_SITE_TEXT, steer_block=0)
+    assert nb * 2 * H * Dt >= 1 << 32
+    w, arr = _weights(nb)
+    w.kv_all = L.dit_linear(FAKE, FAKE, FAKE)
+    a = L.dit_step_args(x=FAKE, text_kv=None, R=1, seq=32, n_tok=32, max_seq=32, t_cur=FAKE, t_next=FAKE,
+                        guidance=FAKE, alpha=FAKE, resid_norm=1.0, direction=FAKE, text=FAKE)
+    need = lib.dit_workspace_size(ctypes.byref(c), 32, 1)
+    assert need > 0
+    assert lib.dit_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(a), FAKE, need, None) == L.ALD_E_UNSUPPORTED
+    # the same weights as one q8w_linear call are rejected the same way
+    assert lib.q8w_linear(FAKE, Dt, 64, Dt, FAKE, FAKE, nb * 2 * H, None, None, 0, 0, FAKE, nb * 2 * H,
+                          None) == L.ALD_E_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
