@@ -24,13 +24,15 @@ STEER_MODES = {"add": ALD_STEER_ADD, "project": ALD_STEER_PROJECT}
 ALD_SITE_RESIDUAL, ALD_SITE_LATENT, ALD_SITE_TEXT = 0, 1, 2
 STEER_SITES = {"residual": ALD_SITE_RESIDUAL, "latent": ALD_SITE_LATENT, "text": ALD_SITE_TEXT}
 
+ALD_STATIC_SCRATCH_BYTES = 64 << 20  # scratch array of dit_step_static, per device
+
 WMODES = {"w8a8": ALD_W8A8, "f16": ALD_F16, "q4": ALD_Q4, "w8a16": ALD_W8A16}
 
 # every extern "C" entry point of include/ald.h
 EXPORTS = (
     "ald_strerror", "ald_version", "quantize_rows_q8", "quantize_q4", "ln_quant", "ln_f16",
     "w8a8_linear", "q8w_linear", "q4_linear", "f16_linear", "attn_fwd", "steer_add", "steer_latent", "cfg_merge",
-    "sampler_update", "ddim_alpha_bar", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_graph_capture",
+    "sampler_update", "ddim_alpha_bar", "dit_workspace_size", "dit_text_kv", "dit_step", "dit_step_static", "dit_graph_capture",
     "dit_graph_launch", "dit_graph_nodes", "dit_graph_destroy",
 )
 
@@ -100,6 +102,7 @@ def _declare(lib):
         "dit_workspace_size": (c_size_t, [POINTER(dit_config), I64, I]),
         "dit_text_kv": (I, [POINTER(dit_config), POINTER(dit_weights), V, I, V, V, c_size_t, V]),
         "dit_step": (I, [POINTER(dit_config), POINTER(dit_weights), POINTER(dit_step_args), V, c_size_t, V]),
+        "dit_step_static": (I, [POINTER(dit_config), POINTER(dit_weights), POINTER(dit_step_args), V]),
         "dit_graph_capture": (I, [POINTER(dit_config), POINTER(dit_weights), POINTER(dit_step_args), I, V,
                                   c_size_t, V, POINTER(c_void_p)]),
         "dit_graph_launch": (I, [V, V]),

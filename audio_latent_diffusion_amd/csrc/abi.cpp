@@ -409,6 +409,31 @@ struct GraphHandle {
   hipGraphExec_t exec;
 };
 
+// Scratch of dit_step_static: a file-scope device array, one copy per device,
+// held until the process ends.  On the host, `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept in g_scratch; only that address is ever handed to a kernel.
+__device__ __align__(256) uint8_t scratch[ALD_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ALD_E_LAUNCH;
+  CHECK(dev >= 0 && dev < kMaxDevices, ALD_E_UNSUPPORTED);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ALD_E_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ALD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -736,6 +761,20 @@ int dit_text_kv(const dit_config* c, const dit_weights* w, const uint16_t* text,
 int dit_step(const dit_config* cfg, const dit_weights* w, const dit_step_args* args, void* ws, size_t ws_bytes,
              hipStream_t stream) {
   return enqueue_step(cfg, w, args, ws, ws_bytes, stream);
+}
+
+int dit_step_static(const dit_config* cfg, const dit_weights* w, const dit_step_args* args, hipStream_t stream) {
+  int e = check_config(cfg);
+  if (e) return e;
+  CHECK(args && args->R > 0 && args->n_tok > 0, ALD_E_INVALID);
+  // the same carve dit_step takes from a caller workspace, here from the
+  // device's scratch array; too large a step is refused before any launch
+  const size_t need = carve_step(cfg, args->n_tok, args->R, nullptr, SIZE_MAX, nullptr);
+  CHECK(need <= ALD_STATIC_SCRATCH_BYTES, ALD_E_WORKSPACE);
+  void* ws = nullptr;
+  e = device_scratch(&ws);
+  if (e) return e;
+  return enqueue_step(cfg, w, args, ws, ALD_STATIC_SCRATCH_BYTES, stream);
 }
 
 int dit_graph_capture(const dit_config* cfg, const dit_weights* w, const dit_step_args* args, int n_steps, void* ws,

@@ -409,6 +409,26 @@ int dit_step(const dit_config* cfg, const dit_weights* w,
              const dit_step_args* args, void* ws, size_t ws_bytes,
              hipStream_t stream);
 
+/* Largest workspace dit_step_static serves (bytes): dit_workspace_size() of
+ * the call's config, tokens and requests must not exceed it (64 MiB covers
+ * the mid-size model up to about 1800 latent tokens, or one request of the
+ * serving model). */
+#define ALD_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* dit_step without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The step's scratch is a device array inside the
+ * library, ALD_STATIC_SCRATCH_BYTES per device, held by every device the
+ * library runs on until the process ends; the call itself allocates nothing.
+ * Same arguments, arithmetic and results as dit_step.  Every call on one
+ * device shares that device's array, and nothing in it needs to start
+ * cleared (each region is written before it is read within a call): calls
+ * (or replays of graphs that captured them) that overlap on one device race.
+ * Returns ALD_E_WORKSPACE, before any launch, when the step needs more than
+ * ALD_STATIC_SCRATCH_BYTES. */
+int dit_step_static(const dit_config* cfg, const dit_weights* w,
+                    const dit_step_args* args, hipStream_t stream);
+
 /* Capture n_steps consecutive dit_step calls (args: HOST array [n_steps])
  * into one hipGraph on `stream` (aria: the per-step denoising loop is
  * captured once and replayed as a single GPU graph; per-step t, alpha and w
