@@ -203,3 +203,79 @@ def test_ddim_step_and_skip_arm_warm_start():
     assert np.array_equal(x[:n0], O.ddim_update(x19, tr[1].v_hat[:n0], ab[20], ab[21]))
     # the model input time of grid point i is timesteps[i] / T
     assert inp.t_grid[20] == np.float32(inp.timesteps[20] / cfg.train_steps)
+
+
+def test_step_metrics_catch_a_five_percent_model_error(tiny):
+    """The step checks run against the GPU see the model: a 5 % error in the
+    model output fails the velocity and increment checks, while the latent
+    it produces stays inside the 2e-2 bar (oracle outputs only)."""
+    from tests import _stepcheck as S
+    m, inp, kv = tiny
+    x_prev, x_new, tr = S.oracle_steps(m, inp, [0], 5.0, kv)
+    N = int(np.sum(inp.seqlens))
+    v_bad = (tr.v.astype(np.float64) * 1.05).astype(np.float16)
+    v_hat = O.cfg_merge(v_bad[:N], v_bad[N:], inp.guidance[0])
+    x_bad = O.euler_update(x_prev, v_hat, inp.t_grid[0], inp.t_grid[1])
+    errs = S.step_errors(x_prev, x_bad, v_bad, x_prev, x_new, tr.v)
+    assert errs["latent"] < S.STEP_TOL
+    assert errs["velocity"] > S.STEP_TOL and errs["increment"] > S.STEP_TOL
+
+
+@pytest.mark.slow
+def test_step_metrics_catch_a_missing_steering_add():
+    """On the mid-size model (steering at block 12 of 16), leaving the
+    steering add out moves the latent by well under the 2e-2 bar; the
+    steering-effect check (steered minus unsteered model output against the
+    oracle's) reads a relative error of 1 (oracle outputs only)."""
+    from tests import _stepcheck as S
+    cfg = I.MID
+    p = I.make_params(cfg)
+    m = O.prepare_model(cfg, p)
+    m_off = O.PreparedModel(cfg.replace(steer_block=-1), p, m.lin)
+    inp = I.make_inputs(cfg)
+    kv = O.text_kv(m, inp.text)
+    x_prev, x_on, tr_on = S.oracle_steps(m, inp, [2], 5.0, kv)
+    _, x_off, tr_off = S.oracle_steps(m_off, inp, [2], 5.0, kv)
+    forgot = S.step_errors(x_prev, x_off, tr_off.v, x_prev, x_on, tr_on.v)
+    print(forgot)
+    assert forgot["latent"] < S.STEP_TOL
+    eff, size = S.effect_error(tr_off.v, tr_off.v, tr_on.v, tr_off.v)
+    assert size > 0 and eff == 1.0 and eff > S.EFFECT_TOL
+
+
+def test_w8a8_spread_of_two_valid_evaluations_comes_from_quantization():
+    """The W8A8 step bars rest on the spread between two valid oracle
+    evaluations (fp64 or fp32 LayerNorm statistics).  With fp16 weights the
+    two agree to 1e-3 in the model output; with W8A8 they differ more (the
+    per-token quantizer turns 1-ulp differences into whole codes), and at
+    the tiny model's depth the bars stay at the fixed 2e-2, so a 5 % model
+    error is still caught there."""
+    from tests import _stepcheck as S
+    out = {}
+    for wm in ("f16", "w8a8"):
+        cfg = CFG.replace(wmode=wm)
+        m = O.prepare_model(cfg, I.make_params(cfg))
+        inp = I.make_inputs(cfg)
+        ref = S.oracle_steps(m, inp, [0], 5.0)
+        bars, trb = S.step_bars(wm, m, inp, [0], 5.0, ref)
+        with S.fp32_layer_norm():
+            xb0, xb, tb = S.oracle_steps(m, inp, [0], 5.0)
+        out[wm] = S.step_errors(xb0, xb, tb.v, ref[0], ref[1], ref[2].v)
+        if wm == "w8a8":
+            assert trb is not None and bars["velocity"] == S.STEP_TOL and bars["increment"] == S.STEP_TOL
+            x_prev, _, tr = ref
+            N = int(np.sum(inp.seqlens))
+            v_bad = (tr.v.astype(np.float64) * 1.05).astype(np.float16)
+            x_bad = O.euler_update(x_prev, O.cfg_merge(v_bad[:N], v_bad[N:], inp.guidance[0]), inp.t_grid[0],
+                                   inp.t_grid[1])
+            errs = S.step_errors(x_prev, x_bad, v_bad, x_prev, ref[1], tr.v)
+            assert errs["velocity"] > bars["velocity"] and errs["increment"] > bars["increment"]
+        else:
+            assert trb is None
+    assert out["f16"]["velocity"] < 1e-3
+    assert out["w8a8"]["velocity"] > 2 * out["f16"]["velocity"]
+    # the fp32-statistics LayerNorm differs from the fp64 one by at most one fp16 rounding
+    x = np.random.default_rng(0).standard_normal((64, 256)).astype(np.float16)
+    g, b = np.ones(256, np.float32), np.zeros(256, np.float32)
+    a, c = O.layer_norm(x, g, b).astype(np.float64), S.layer_norm_fp32(x, g, b).astype(np.float64)
+    assert np.all(np.abs(a - c) <= np.spacing(np.abs(a).astype(np.float16)).astype(np.float64))
