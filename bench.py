@@ -1,21 +1,30 @@
 """Denoise-step throughput of the DiT hot path on one MI355X.
 
-Workload (mid-size DiT): 16 blocks, hidden 1024, 16 heads, MLP 4096 (GELU),
-latent 256 x 64, cross-attention to 128 text tokens of dim 768, one request
-as a CFG pair (batch 2, guidance 3), W8A8 weights with per-token dynamic
-activation scales, 8 Euler steps on the uniform t grid captured once as one
-hipGraph, steering (alpha 0.5 at block 12) active in steps 2-5 only.
-Synthetic seeded inputs and random weights of that shape.
+Headline workload (the serving batch): 24 DiT blocks, hidden 1536, 24 heads,
+MLP 6144 (GELU), 8 requests as 16 CFG rows (cond + null-prompt companion) of
+512 latent tokens x 64 channels (8192 rows per launch), cross-attention to
+128 text tokens of dim 768, W8A8 block linears (per-output-channel int8
+weights, per-token dynamic activation scales, int32 accumulation), fp16
+attention, guidance 3, 8 Euler steps on the uniform t grid captured once as
+one hipGraph, the steering node present at block 12 (strength 0 in every
+step, read from device memory).  Synthetic seeded inputs; random weights of
+that architecture drawn on the device.
 
-One timed unit is one replay of the 8-step graph (a whole sampler pass of a
-fresh request: the latent is reset from its initial noise first); `value` is
-denoise steps per second.  The JSON line also carries the roofline of the
-dominant kernel (the W8A8 GEMM, timed live with HIP events on its own launch
-stream at the step's shapes), the W8A8 GEMM at the serving-batch shapes
-(hidden 1536, 8192 tokens) as % of the int8 MFMA peak, per-kernel rooflines
-(attention, fp16- and 4-bit-weight GEMMs at the large workload shapes; the
-HBM-bound kernels on stress shapes beyond the last-level cache), and the CPU
-oracle timed on a bounded sample on the host cores.
+One timed unit is one replay of the 8-step graph: the latent restarts from
+its initial noise before each replay; the text K/V projection, done once per
+request outside the step loop (0.7 % of a request's work), is not repeated.
+`value` is denoise steps per second from the median of per-replay HIP-event
+times (each replay bracketed by events on the stream it runs on), over
+exactly --steps timed steps after --warmup untimed ones.
+
+The JSON line also carries: the roofline of the dominant kernel (the W8A8
+GEMM over the serving block's six launches with the step's own epilogues,
+timed live with HIP events inside a graph); the GEMM alone at those shapes
+against the vendor library; a steering-overhead A/B (no steering node,
+strength 0 in every step, an active span); the mid-size model's loop and its
+variants; the tiny model's one-step graph; per-kernel rooflines; launches per
+step against the floor of an empty launch; and the CPU oracle on the host
+cores (the serving step extrapolated from one of its 24 blocks).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -24,6 +33,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +45,17 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 MFMA, TFLOP/s
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+# the pages' end-to-end figures (RTX 3070, warm generation of a 10 s stereo
+# clip with 8 sampling steps, text encoder and decoder included): context only
+PAGES_CONTEXT = {
+    "source": "A Quantized Native Runtime for On-Device Semantic Audio Generation (Chinese summary, results table)",
+    "hardware": "RTX 3070 8 GB",
+    "seconds_per_10s_clip": {"small_runtime": 0.13, "small_pytorch": 0.146, "medium_runtime": 0.37,
+                             "medium_pytorch": 0.443},
+    "note": "whole clips including text encoding and decoding on another GPU; not a per-step or like-for-like "
+            "figure",
+}
 
 
 def _events_time(fn, iters, stream):
@@ -49,59 +70,96 @@ def _events_time(fn, iters, stream):
     return start.elapsed_time(end) / iters  # ms
 
 
+def _median(xs):
+    return float(statistics.median(xs))
+
+
 MIX_SHAPES = lambda H, F: [(H, 3 * H), (H, H), (H, H), (H, H), (H, F), (F, H)]  # (K, N) per block
+MIX_NAMES = ("qkv", "o", "q", "ox", "up", "down")
+# the epilogue each block linear runs in the step: residual add in place (o,
+# ox, down), GELU (up), plain (qkv, q)
+MIX_EPI = {"qkv": "plain", "o": "residual", "q": "plain", "ox": "residual", "up": "gelu", "down": "residual"}
 
 
-def gemm_mix(cfg):
-    """The W8A8 GEMM launches of one DiT block at M = 2 R S tokens (qkv, o, q,
-    ox, up, down), pre-quantized inputs, each launched through the C ABI on
-    torch's current stream; returns a callable that enqueues the six."""
+def gemm_mix(M, H, F, epilogues=True, seed=0):
+    """The W8A8 GEMM launches of one DiT block at M rows (qkv, o, q, ox, up,
+    down), pre-quantized inputs, with the step's epilogues (bias everywhere,
+    in-place residual for o, ox and down, GELU for up) or the plain one;
+    returns one callable per launch, each enqueued through the C ABI on
+    torch's current stream."""
     import torch
     from audio_latent_diffusion_amd import binding as B
-    M = cfg.tokens
-    g = torch.Generator(device="cuda").manual_seed(0)
-    bufs = []
-    for K, N in MIX_SHAPES(cfg.hidden, cfg.mlp):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    calls = []
+    for name, (K, N) in zip(MIX_NAMES, MIX_SHAPES(H, F)):
         xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
         wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
         xs = torch.rand(M, device="cuda", generator=g) * 1e-2
         ws = torch.rand(N, device="cuda", generator=g) * 1e-3
-        y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        bufs.append((xq, wq, xs, ws, y))
+        b = torch.randn(N, device="cuda", generator=g) * 0.02
+        y = torch.randn((M, N), device="cuda", generator=g).half()
+        epi = MIX_EPI[name] if epilogues else "plain"
+        res = y if epi == "residual" else None
+        act = 1 if epi == "gelu" else 0
+        calls.append(lambda xq=xq, wq=wq, xs=xs, ws=ws, b=b, y=y, res=res, act=act: B.w8a8_linear(
+            None, wq, ws, bias=b, residual=res, act=act, y=y, xq=xq, x_scale=xs, prequant=True))
+    return calls
 
-    def run_mix():
-        for xq, wq, xs, ws, y in bufs:
-            B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, y=y, prequant=True)
-    return run_mix
 
-
-def gemm_mix_timing(cfg, iters=50, replays=5):
-    """Average launch time of the W8A8 GEMM over the step's per-block launch
-    mix, with the algorithmic ops and bytes per launch.  The launches are
-    captured into a graph, as the step runs them (launched one by one from
-    Python, these short kernels would time the host instead), and the graph's
-    replays are timed with HIP events on torch's current stream, the stream
-    they run on."""
+def _graph_of(fns, reps):
+    """fns captured `reps` times into one graph on a side stream."""
     import torch
-    run_mix = gemm_mix(cfg)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        run_mix()
+        for f in fns:
+            f()
     torch.cuda.synchronize()
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr, stream=s):
-        for _ in range(iters):
-            run_mix()
+        for _ in range(reps):
+            for f in fns:
+                f()
     gr.replay()
     torch.cuda.synchronize()
-    ms_mix = _events_time(gr.replay, replays, torch.cuda.current_stream()) / iters
-    del gr
-    M = cfg.tokens
-    shapes = MIX_SHAPES(cfg.hidden, cfg.mlp)
-    ops = sum(2.0 * M * N * K for K, N in shapes)
-    byts = sum(M * K + N * K + 2 * M * N + 4 * (M + N) for K, N in shapes)
-    return ms_mix / len(shapes), ops / len(shapes), byts / len(shapes)
+    return gr
+
+
+def gemm_mix_timing(M, H, F, epilogues=True, reps=20, replays=5):
+    """Per-launch times of one block's six W8A8 GEMMs at M rows, each shape
+    captured `reps` times into a graph (the step runs them inside a graph;
+    launched one by one from Python, short kernels would time the host) and
+    timed with HIP events on the stream the graph replays on; returns
+    per-shape launch times, ops and algorithmic bytes."""
+    import torch
+    calls = gemm_mix(M, H, F, epilogues)
+    out = {}
+    for name, (K, N), f in zip(MIX_NAMES, MIX_SHAPES(H, F), calls):
+        gr = _graph_of([f], reps)
+        ms = [_events_time(gr.replay, 1, torch.cuda.current_stream()) / reps for _ in range(replays)]
+        epi = MIX_EPI[name] if epilogues else "plain"
+        byts = M * K + N * K + 2 * M * N + 4 * (M + 2 * N) + (2 * M * N if epi == "residual" else 0)
+        out[name] = {"M": M, "K": K, "N": N, "epilogue": epi, "us": round(_median(ms) * 1e3, 2),
+                     "ops": 2.0 * M * N * K, "bytes": byts}
+        del gr
+    del calls
+    torch.cuda.synchronize()
+    return out
+
+
+def mix_roofline(per_shape):
+    """Algorithmic ops (and bytes) per launch over the average launch time of the mix."""
+    n = len(per_shape)
+    us = sum(v["us"] for v in per_shape.values()) / n
+    ops = sum(v["ops"] for v in per_shape.values()) / n
+    byts = sum(v["bytes"] for v in per_shape.values()) / n
+    tops = ops / (us * 1e-6) / 1e12
+    return {"avg_launch_us": round(us, 2), "algorithmic_ops_per_launch": ops, "algorithmic_bytes_per_launch": byts,
+            "achieved": round(tops, 1), "frac": round(tops / INT8_PEAK_TOPS, 4),
+            "per_shape": {k: {kk: vv for kk, vv in v.items() if kk not in ("ops", "bytes")} |
+                          {"tops": round(v["ops"] / (v["us"] * 1e-6) / 1e12, 1),
+                           "frac_int8_peak": round(v["ops"] / (v["us"] * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
+                          for k, v in per_shape.items()}}
 
 
 def graph_floor_us(n=200, replays=5):
@@ -311,34 +369,291 @@ def kernel_rooflines():
     return out
 
 
-def cpu_baseline(cfg, params, inp, resid, budget_s=20.0):
-    """The oracle, as it stands, on the host cores: denoise steps of the same
-    workload, as many whole steps as fit the budget (at least one)."""
-    from oracle import ald_oracle as O
+def device_params(cfg, seed):
+    """Random weights of cfg's architecture, drawn on the GPU with a seeded
+    generator (the same distributions as the seeded host draws: weights
+    N(0, 0.02) in fp16, biases N(0, 0.02), LayerNorm gain 1 + N(0, 0.02) and
+    shift N(0, 0.02)); for timing runs of the large models, whose host draws
+    would take minutes."""
+    import torch
+    import ald_inputs as I
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    H, C = cfg.hidden, cfg.channels
+
+    def nrm(shape, s=0.02):
+        return torch.randn(shape, generator=g, device="cuda") * s
+
+    def ln():
+        return 1.0 + nrm(H), nrm(H)
+
+    shapes = I.linear_shapes(cfg)
+    blocks = []
+    for _ in range(cfg.n_blocks):
+        (g1, b1), (g2, b2), (g3, b3) = ln(), ln(), ln()
+        w = {n: nrm(shapes[n]).half() for n in I.LINEARS}
+        b = {n: nrm(shapes[n][0]) for n in I.LINEARS}
+        blocks.append(I.BlockParams(g1, b1, g2, b2, g3, b3, w, b))
+    lg, lb = ln()
+    return I.DiTParams(nrm((H, C)).half(), nrm(H), lg, lb, nrm((C, H)).half(), nrm(C), blocks)
+
+
+class Loop:
+    """A step runner whose whole sampler loop is captured once as one graph
+    (plus, when a step count needs one, a graph of the loop's first k steps);
+    each replay restarts the latent from its initial noise."""
+
+    def __init__(self, model, inp, resid):
+        from audio_latent_diffusion_amd import runtime
+        self.run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
+                                      inp.direction, resid, start_step=inp.start_step, x0=inp.x0, eps=inp.eps,
+                                      timesteps=inp.timesteps)
+        self.n = self.run.n_steps
+        self.x_init = self.run.x.clone()
+        self.graphs = {self.n: self.run.capture_graph(range(self.n))}
+
+    def schedule(self, steps):
+        """Replays (each a step count) that add up to exactly `steps` steps."""
+        sched = [self.n] * (steps // self.n)
+        if steps % self.n:
+            sched.append(steps % self.n)
+        for k in sched:
+            if k not in self.graphs:
+                self.graphs[k] = self.run.capture_graph(range(k))
+        return sched
+
+    def replay(self, k, stream, ev=None):
+        self.run.x.copy_(self.x_init)
+        if ev is not None:
+            ev[0].record(stream)
+        self.run.launch_graph(self.graphs[k])
+        if ev is not None:
+            ev[1].record(stream)
+
+    def event_times(self, sched):
+        """ms per step of each replay, from HIP events around the graph launch."""
+        import torch
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sched]
+        for k, ev in zip(sched, evs):
+            self.replay(k, stream, ev)
+        torch.cuda.synchronize()
+        return [ev[0].elapsed_time(ev[1]) / k for k, ev in zip(sched, evs)]
+
+    def timed(self, steps, warmup):
+        """Exactly `steps` timed steps after `warmup` untimed ones: median of
+        the per-replay event times, and the wall clock around them with a
+        device synchronisation on both sides."""
+        import torch
+        stream = torch.cuda.current_stream()
+        warm, sched = self.schedule(warmup), self.schedule(steps)
+        for k in warm:
+            self.replay(k, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        per_step = self.event_times(sched)
+        wall = time.perf_counter() - t0
+        med = _median(per_step)
+        ok = bool(torch.isfinite(self.run.x).all().item())
+        return {"steps": steps, "replays": len(sched), "median_ms_per_step": round(med, 4),
+                "steps_per_s": round(1e3 / med, 2), "wall_steps_per_s": round(steps / wall, 2),
+                "min_ms_per_step": round(min(per_step), 4), "max_ms_per_step": round(max(per_step), 4),
+                "finite": ok}
+
+    def launches_per_step(self):
+        return self.run.graph_nodes(self.graphs[self.n]) / self.n
+
+    def close(self):
+        self.run.destroy_graph()
+
+
+def steering_ab(model, inp, resid, span_alpha, span_steps, replays):
+    """The same loop three ways, replays interleaved so that drift in the
+    chip's clock falls on all three alike: no steering node (steer_block -1),
+    the node with strength 0 in every step, and strength `span_alpha` in
+    `span_steps` (the node reads the strength from device memory at run
+    time).  Median ms per step of each, and the differences."""
+    import dataclasses
+    zero = np.zeros_like(inp.alpha)
+    span = np.zeros_like(inp.alpha)
+    span[list(span_steps), :] = span_alpha
+    arms = {"no_node": Loop(model.with_steer_block(-1), dataclasses.replace(inp, alpha=zero), resid),
+            "alpha_zero": Loop(model, dataclasses.replace(inp, alpha=zero), resid),
+            "active_span": Loop(model, dataclasses.replace(inp, alpha=span), resid)}
+    times = {k: [] for k in arms}
+    for loop in arms.values():
+        loop.event_times([loop.n])
+    for _ in range(replays):
+        for k, loop in arms.items():
+            times[k] += loop.event_times([loop.n])
+    out = {k: round(_median(v), 4) for k, v in times.items()}
+    base = out["no_node"]
+    res = {"median_ms_per_step": out,
+           "steps_per_s": {k: round(1e3 / v, 2) for k, v in out.items()},
+           "overhead_vs_no_node_pct": {k: round(100.0 * (v - base) / base, 2) for k, v in out.items()
+                                       if k != "no_node"},
+           "launches_per_step": {k: loop.launches_per_step() for k, loop in arms.items()},
+           "replays_each": replays, "span": {"alpha": span_alpha, "steps": list(span_steps)}}
+    for loop in arms.values():
+        loop.close()
+    return res
+
+
+def loop_rate(model, inp, resid, replays):
+    """steps/s of whole replays of the run's full sampler loop as one graph
+    (median of the per-replay event times)."""
+    loop = Loop(model, inp, resid)
+    r = loop.timed(replays * loop.n, loop.n)
+    r["launches_per_step"] = loop.launches_per_step()
+    loop.close()
+    return r
+
+
+def mixed_warm_start(resid, replays=5):
+    """The warm-start serving batch: 32 packed requests of 128..1024 latent
+    tokens on the mid-size architecture, half of them warm-started (re-noised
+    at a skipped step), 16 Euler steps as one graph; request-steps/s and
+    token-steps/s over the rows each step actually advances."""
+    import ald_inputs as I
+    from audio_latent_diffusion_amd import runtime
+    cfg = I.MIXED
+    inp = I.make_mixed_inputs(cfg)
+    model = runtime.DiTModel(cfg, I.make_params(cfg))
+    r = loop_rate(model, inp, resid, replays)
+    active = cfg.n_steps - np.asarray(inp.start_step)
+    req_steps = int(active.sum())
+    tok_steps = int((np.asarray(inp.seqlens) * active).sum())
+    sec = r["median_ms_per_step"] * cfg.n_steps / 1e3
+    del model
+    return {"workload": f"{len(inp.seqlens)} packed requests, latent lengths 128..1024 (total "
+                        f"{int(np.sum(inp.seqlens))} tokens), half warm-started, {cfg.n_steps} Euler steps as one "
+                        f"hipGraph, W8A8", "request_steps_per_s": round(req_steps / sec, 1),
+            "token_steps_per_s": round(tok_steps / sec), "active_request_steps": req_steps,
+            "ms_per_loop": round(sec * 1e3, 2), "replays": r["replays"], "finite": r["finite"]}
+
+
+def variant_loops(model, resid):
+    """The mid-size model's loop under other settings: the DDIM sampler over
+    the 200-step grid (the warm-start pages' backbone setting, steering in
+    steps 40-79), and steering at the latent and text sites (8 Euler steps;
+    the text site re-projects the steered text's K/V in every step)."""
+    import ald_inputs as I
+    out = {}
+    cfg = I.MID_DDIM
+    r = loop_rate(model.with_config(sampler="ddim", n_steps=cfg.n_steps), I.make_inputs(cfg), resid, 3)
+    out["ddim_200"] = dict(workload="DDIM sampler, 200 steps as one hipGraph, steering alpha 0.5 at block 12 "
+                                    "in steps 40-79", **r)
+    for site in ("latent", "text"):
+        cfg = I.MID.replace(steer_site=site)
+        inp = I.make_inputs(cfg)
+        unit = float(np.mean(np.linalg.norm(inp.x, axis=1))) if site == "latent" else \
+            float(np.mean(np.linalg.norm(inp.text[:cfg.requests].reshape(-1, cfg.text_dim).astype(np.float64), axis=1)))
+        r = loop_rate(model.with_config(steer_site=site), inp, unit, 30)
+        out[f"steer_{site}_site"] = dict(workload=f"8 Euler steps as one hipGraph, steering alpha 0.5 at the "
+                                                  f"{site} site in steps 2-5", **r)
+    return out
+
+
+def other_arms(params, inp, replays=5):
+    """The serving model with fp16 and 8-bit weight-only weights on the same
+    inputs as the W8A8 headline, and the 4-bit-weight model (24 blocks,
+    hidden 2048, 4 requests as 8 CFG rows of 1024 tokens); 8 Euler steps as
+    one graph each, and the six block linears' algorithmic work times the
+    rate."""
+    import torch
+    import ald_inputs as I
+    from audio_latent_diffusion_amd import runtime
+    out = {}
+
+    def lin_ops(cfg):
+        tokens = 2 * cfg.requests * cfg.seq
+        return 2.0 * tokens * sum(n * k for name, (n, k) in I.linear_shapes(cfg).items() if name != "kv") * \
+            cfg.n_blocks
+
+    for arm in ("f16", "w8a16"):
+        cfg = I.SERVE.replace(wmode=arm)
+        model = runtime.DiTModel(cfg, params)
+        r = loop_rate(model, inp, 1.0, replays)
+        out[f"serve_{arm}"] = dict(workload=f"serving model, {arm} weights, 8 Euler steps as one hipGraph",
+                                   linear_ops_per_step=lin_ops(cfg),
+                                   linear_tflops=round(lin_ops(cfg) * r["steps_per_s"] / 1e12, 1), **r)
+        del model
+        torch.cuda.empty_cache()
+    cfg = I.Q4
+    qp = device_params(cfg, cfg.seed)
+    model = runtime.DiTModel(cfg, qp)
+    del qp
+    torch.cuda.empty_cache()
+    r = loop_rate(model, I.make_inputs(cfg), 1.0, replays)
+    out["q4_model"] = dict(workload="24 blocks, hidden 2048, 4 requests x CFG pair of 1024 latent tokens (8192 "
+                                    "rows), 4-bit weights (group 32), 8 Euler steps as one hipGraph",
+                           linear_ops_per_step=lin_ops(cfg),
+                           linear_tflops=round(lin_ops(cfg) * r["steps_per_s"] / 1e12, 1), **r)
+    del model
+    torch.cuda.empty_cache()
+    return out
+
+
+def _source_hash(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _oracle_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    om = O.prepare_model(cfg, params)
+        return None
+
+
+def _oracle_step_seconds(cfg, inp=None, steps=(0,)):
+    """Wall seconds of the oracle's step(s) on cfg's model (text K/V and
+    weight packing excluded)."""
+    import ald_inputs as I
+    from oracle import ald_oracle as O
+    om = O.prepare_model(cfg, I.make_params(cfg))
+    inp = I.make_inputs(cfg) if inp is None else inp
     kv = O.text_kv(om, inp.text)
-    x = inp.x
     t0 = time.perf_counter()
-    n = 0
-    while True:
-        i = n % cfg.n_steps
-        x, _ = O.dit_step(om, x, inp.seqlens, kv, np.full(1, inp.t_grid[i], np.float32),
-                          np.full(1, inp.t_grid[i + 1], np.float32), inp.guidance, inp.alpha[i], resid,
-                          inp.direction)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s or n >= cfg.n_steps:
-            break
-    dt = time.perf_counter() - t0
-    out = {"value": round(n / dt, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"{n} denoise step(s) of the mid-size DiT (same shapes, CFG pair) in {dt:.1f} s; "
-                     f"fp64 numpy oracle with BLAS matmuls, text K/V and weight packing excluded"}
-    out["tiny_step"] = tiny_oracle_rates()
-    return out
+    O.run_sampler(om, inp, kv, resid_norm=1.0, steps=list(steps))
+    return time.perf_counter() - t0
+
+
+def cpu_baseline():
+    """The oracle as it stands (fp64 numpy, BLAS matmuls) on the host cores.
+
+    value: the headline workload, extrapolated -- one step of the serving
+    model cut to one of its 24 blocks over the full batch (8 requests, 8192
+    CFG rows), times 24 (the input and output projections, CFG merge and
+    Euler update, under 1 % of the work, are counted 24 times).  Beside it:
+    the 4-bit-weight model the same way, a full step of the mid-size model,
+    the tiny model on all threads and on one, and one global step of a
+    4-request packed sub-batch of the mixed warm-start workload (lengths 128,
+    129, 577, 1024; two cold, two warm, one re-noised in that step)."""
+    import ald_inputs as I
+    cores = len(os.sched_getaffinity(0))
+    legs = {}
+    t_serve = _oracle_step_seconds(I.SERVE.replace(n_blocks=1, steer_block=0))
+    legs["q4_model_x24"] = {"seconds_one_block": round((t4 := _oracle_step_seconds(
+        I.Q4.replace(n_blocks=1, steer_block=0))), 2), "steps_per_s": round(1.0 / (24 * t4), 5),
+        "extrapolated": True}
+    t_mid = _oracle_step_seconds(I.MID, steps=(2,))
+    legs["mid_step"] = {"seconds": round(t_mid, 2), "steps_per_s": round(1.0 / t_mid, 4)}
+    legs["tiny_step"] = tiny_oracle_rates()
+    cfg = I.MIXED
+    sub = I.make_mixed_inputs(cfg, seqlens=np.array([128, 129, 577, 1024]),
+                              warm=np.array([False, False, True, True]))
+    sub.start_step = np.array([0, 0, 5, 7])
+    t_mix = _oracle_step_seconds(cfg, sub, steps=(7,))
+    legs["mixed_subbatch_step"] = {"seconds": round(t_mix, 2), "request_steps_per_s": round(4 / t_mix, 4),
+                                   "token_steps_per_s": round(int(np.sum(sub.seqlens)) / t_mix, 1)}
+    return {"value": round(1.0 / (24 * t_serve), 5), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"one step of the serving model cut to 1 of its 24 blocks (8 requests, 8192 CFG rows, "
+                      f"W8A8) took {t_serve:.1f} s; value = 1 / (24 x that), an extrapolation to the full "
+                      f"24-block step",
+            "blas_threads": _oracle_threads(), "seconds_one_block": round(t_serve, 2), "extrapolated": True,
+            "legs": legs}
 
 
 def tiny_oracle_rates(reps=3):
@@ -370,20 +685,15 @@ def tiny_oracle_rates(reps=3):
 
 
 GEMM_SOURCE = os.path.join(ROOT, "audio_latent_diffusion_amd", "csrc", "gemm_dma.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_mid_launch_mix_traffic.txt")
-
-
-def _source_hash(path):
-    import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_serve_mix_traffic.txt")
 
 
 def measured_traffic():
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE of the launch-mix leg, each scaled by what the
-    same counter reads for a plain copy of known size); None when the file is
-    missing or the kernel source changed since the counters were taken."""
+    (FETCH_SIZE and WRITE_SIZE of the serving launch mix, each scaled by what
+    the same counter reads for a plain copy of known size); None when the
+    file is missing or the kernel source changed since the counters were
+    taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -405,16 +715,34 @@ def measured_traffic():
 
 
 def counter_legs(legs, reps):
-    """Workloads for the rocprofv3 --pmc runs: the GEMM launch mix of the
-    step (same shapes and stream as the roofline timing), the W8A8 GEMMs at
-    the serving shapes, and a plain device copy of known size that
-    calibrates FETCH_SIZE / WRITE_SIZE."""
+    """Workloads for the rocprofv3 runs: the headline loop (two replays),
+    the serving block's W8A8 GEMM mix
+    with the step's epilogues (the roofline's kernel), the same mix at the
+    mid-size model's 512 rows, the plain-epilogue serving GEMMs, the
+    per-kernel legs, and a plain device copy of known size that calibrates
+    FETCH_SIZE / WRITE_SIZE."""
     import torch
-    import ald_inputs as I
-    if "gemm" in legs:
-        run_mix = gemm_mix(I.MID)
-        for _ in range(reps):
-            run_mix()
+    if "serve_step" in legs:
+        # the headline loop itself: two replays of the serving W8A8 8-step graph
+        import ald_inputs as I
+        from audio_latent_diffusion_amd import runtime
+        cfg = I.SERVE
+        params = device_params(cfg, cfg.seed)
+        model = runtime.DiTModel(cfg, params)
+        del params
+        loop = Loop(model, I.make_inputs(cfg), 1.0)
+        loop.timed(2 * loop.n, loop.n)
+        loop.close()
+        del model
+        torch.cuda.empty_cache()
+    if "serve_mix" in legs:
+        for f in gemm_mix(8192, 1536, 6144):
+            for _ in range(reps):
+                f()
+    if "mid_mix" in legs:
+        for f in gemm_mix(512, 1024, 4096):
+            for _ in range(reps):
+                f()
     if "serve" in legs:
         print(json.dumps({"w8a8_gemm_serve": serve_gemm(iters=reps)}))
     if "kernels" in legs:
@@ -431,150 +759,22 @@ def counter_legs(legs, reps):
     torch.cuda.synchronize()
 
 
-def loop_rate(model, inp, resid, replays):
-    """steps/s of whole replays of the run's full sampler loop as one graph."""
-    import torch
-    from audio_latent_diffusion_amd import runtime
-    run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
-                             inp.direction, resid, timesteps=inp.timesteps)
-    n = run.n_steps
-    x_init = run.x.clone()
-    graph = run.capture_graph(range(n))
-    run.x.copy_(x_init)
-    run.launch_graph(graph)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        run.x.copy_(x_init)
-        run.launch_graph(graph)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ok = bool(torch.isfinite(run.x).all().item())
-    run.destroy_graph()
-    return {"steps_per_s": round(replays * n / wall, 2), "ms_per_loop": round(wall * 1e3 / replays, 2),
-            "finite": ok}
-
-
-def mixed_warm_start(resid, replays=2):
-    """The warm-start serving batch: 32 packed requests of 128..1024 latent
-    tokens on the mid-size architecture, half of them warm-started (re-noised
-    at a skipped step), 16 Euler steps as one graph; request-steps/s and
-    token-steps/s over the rows each step actually advances."""
-    import ald_inputs as I
-    from audio_latent_diffusion_amd import runtime
-    cfg = I.MIXED
-    inp = I.make_mixed_inputs(cfg)
-    model = runtime.DiTModel(cfg, I.make_params(cfg))
-    r = loop_rate(model, inp, resid, replays)
-    active = cfg.n_steps - np.asarray(inp.start_step)
-    req_steps = int(active.sum())
-    tok_steps = int((np.asarray(inp.seqlens) * active).sum())
-    sec = r["ms_per_loop"] / 1e3
-    del model
-    return {"workload": f"{len(inp.seqlens)} packed requests, latent lengths 128..1024 (total "
-                        f"{int(np.sum(inp.seqlens))} tokens), half warm-started, {cfg.n_steps} Euler steps as one "
-                        f"hipGraph, W8A8", "request_steps_per_s": round(req_steps / sec, 1),
-            "token_steps_per_s": round(tok_steps / sec), "active_request_steps": req_steps,
-            "ms_per_loop": r["ms_per_loop"], "finite": r["finite"]}
-
-
-def device_params(cfg, seed):
-    """Random weights of cfg's architecture, drawn on the GPU with a seeded
-    generator (the same distributions as the seeded host draws: weights
-    N(0, 0.02) in fp16, biases N(0, 0.02), LayerNorm gain 1 + N(0, 0.02) and
-    shift N(0, 0.02)); for timing runs of the large models, whose host draws
-    would take minutes."""
-    import torch
-    import ald_inputs as I
-    g = torch.Generator(device="cuda").manual_seed(seed)
-    H, C = cfg.hidden, cfg.channels
-
-    def nrm(shape, s=0.02):
-        return torch.randn(shape, generator=g, device="cuda") * s
-
-    def ln():
-        return 1.0 + nrm(H), nrm(H)
-
-    shapes = I.linear_shapes(cfg)
-    blocks = []
-    for _ in range(cfg.n_blocks):
-        (g1, b1), (g2, b2), (g3, b3) = ln(), ln(), ln()
-        w = {n: nrm(shapes[n]).half() for n in I.LINEARS}
-        b = {n: nrm(shapes[n][0]) for n in I.LINEARS}
-        blocks.append(I.BlockParams(g1, b1, g2, b2, g3, b3, w, b))
-    lg, lb = ln()
-    return I.DiTParams(nrm((H, C)).half(), nrm(H), lg, lb, nrm((C, H)).half(), nrm(C), blocks)
-
-
-def large_model_loops(replays=2):
-    """Step rates of the other model sizes: the serving model (24 blocks,
-    hidden 1536, 8 requests as 16 CFG rows of 512 latent tokens) with fp16,
-    W8A8 and 8-bit weight-only weights side by side on the same inputs, and
-    the 4-bit-weight model (24 blocks, hidden 2048, 4 requests as 8 CFG rows of
-    1024 tokens); 8 Euler steps as one graph each."""
-    import torch
-    import ald_inputs as I
-    from audio_latent_diffusion_amd import runtime
-    out = {}
-    for cfg, arms in ((I.SERVE, ("w8a8", "f16", "w8a16")), (I.Q4, ("q4",))):
-        params = device_params(cfg, cfg.seed)
-        inp = I.make_inputs(cfg)
-        tokens = 2 * cfg.requests * cfg.seq
-        # the six block linears of the step (the text K/V projection is hoisted)
-        lin_ops = 2.0 * tokens * sum(n * k for name, (n, k) in I.linear_shapes(cfg).items() if name != "kv") \
-            * cfg.n_blocks
-        for arm in arms:
-            model = runtime.DiTModel(cfg.replace(wmode=arm), params)
-            r = loop_rate(model, inp, 1.0, replays)
-            key = f"serve_{arm}" if cfg is I.SERVE else "q4_model"
-            out[key] = dict(
-                workload=f"{cfg.n_blocks} blocks, hidden {cfg.hidden}, {cfg.requests} requests x CFG pair of "
-                         f"{cfg.seq} latent tokens ({tokens} rows), {arm} weights, 8 Euler steps as one hipGraph",
-                linear_ops_per_step=lin_ops,
-                linear_rate=round(lin_ops * r["steps_per_s"] / 1e12, 1),
-                linear_rate_unit="TOP/s" if arm == "w8a8" else "TFLOP/s", **r)
-            del model
-            torch.cuda.empty_cache()
-        del params
-        torch.cuda.empty_cache()
-    return out
-
-
-def variant_loops(model, resid):
-    """The mid-size model's loop under other settings: the DDIM sampler over
-    the 200-step grid (the warm-start pages' backbone setting, steering in
-    steps 40-79), and steering at the latent and text sites (8 Euler steps;
-    the text site re-projects the steered text's K/V in every step)."""
-    import ald_inputs as I
-    out = {}
-    cfg = I.MID_DDIM
-    r = loop_rate(model.with_config(sampler="ddim", n_steps=cfg.n_steps), I.make_inputs(cfg), resid, 2)
-    out["ddim_200"] = dict(workload="DDIM sampler, 200 steps as one hipGraph, steering alpha 0.5 at block 12 "
-                                    "in steps 40-79", **r)
-    for site in ("latent", "text"):
-        cfg = I.MID.replace(steer_site=site)
-        inp = I.make_inputs(cfg)
-        unit = float(np.mean(np.linalg.norm(inp.x, axis=1))) if site == "latent" else \
-            float(np.mean(np.linalg.norm(inp.text[:cfg.requests].reshape(-1, cfg.text_dim).astype(np.float64), axis=1)))
-        r = loop_rate(model.with_config(steer_site=site), inp, unit, 20)
-        out[f"steer_{site}_site"] = dict(workload=f"8 Euler steps as one hipGraph, steering alpha 0.5 at the "
-                                                  f"{site} site in steps 2-5", **r)
-    return out
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=160, help="timed denoise steps")
-    ap.add_argument("--warmup", type=int, default=16, help="untimed denoise steps")
+    ap.add_argument("--steps", type=int, default=400, help="timed denoise steps (8 per replay)")
+    ap.add_argument("--warmup", type=int, default=80, help="untimed denoise steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--leg", default="", help="counter legs only (gemm,serve,kernels,copy) for rocprofv3 runs")
+    ap.add_argument("--leg", default="", help="profiling legs only (serve_step,serve_mix,mid_mix,serve,kernels,"
+                                              "copy) for rocprofv3 runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only; --gpus N > 1 is not supported. The step shards by request "
               "(each GPU would hold the weights and run its own requests' CFG pairs with no per-step "
               "exchange), and no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         sys.exit(2)
     if args.leg:
         counter_legs(args.leg.split(","), 20)
@@ -584,112 +784,132 @@ def main():
     import ald_inputs as I
     from audio_latent_diffusion_amd import runtime
 
-    cfg = I.MID
-    params = I.make_params(cfg)
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---- headline: the serving batch, W8A8, 8 steps as one graph ----
+    cfg = I.SERVE
+    params = device_params(cfg, cfg.seed)
     inp = I.make_inputs(cfg)
     model = runtime.DiTModel(cfg, params)
+    loop = Loop(model, inp, 1.0)  # strength 0 in every step: the steering unit is never used
+    head = loop.timed(args.steps, args.warmup)
+    launches = loop.launches_per_step()
+    loop.close()
+    log(f"serving W8A8 step: {head['steps_per_s']} steps/s (median of {head['replays']} replays)")
+    steer_serve = steering_ab(model, inp, 62.0, 0.5, (2, 3, 4, 5), 5)
+    log("serving steering A/B done")
+    del model
+    torch.cuda.empty_cache()
+    arms = other_arms(params, inp)
+    del params
+    torch.cuda.empty_cache()
+    log("serving fp16 / 8-bit weight-only arms and the 4-bit model done")
 
-    # steering unit: mean per-token residual norm at the steered block over the
-    # 8 steps of the alpha = 0 run (a calibration input, outside the timed region)
-    zero = I.make_inputs(cfg)
+    # ---- the W8A8 GEMM: the serving block's launch mix with its epilogues ----
+    serve_mix = mix_roofline(gemm_mix_timing(8192, 1536, 6144, epilogues=True))
+    traffic = measured_traffic()
+    serve_plain = serve_gemm()
+    floor_us = graph_floor_us()
+    log(f"serving GEMM mix: {serve_mix['frac']} of the int8 peak")
+
+    # ---- mid-size model (16 blocks, hidden 1024, one CFG pair of 256 tokens) ----
+    mcfg = I.MID
+    mparams = I.make_params(mcfg)
+    minp = I.make_inputs(mcfg)
+    mmodel = runtime.DiTModel(mcfg, mparams)
+    zero = I.make_inputs(mcfg)
     zero.alpha[:] = 0
-    cal = runtime.StepRunner(model, zero.x, zero.text, zero.seqlens, zero.t_grid, zero.guidance, zero.alpha,
+    cal = runtime.StepRunner(mmodel, zero.x, zero.text, zero.seqlens, zero.t_grid, zero.guidance, zero.alpha,
                              zero.direction, 0.0)
     cal.collect_block_norms()
     norms = []
-    for i in range(cfg.n_steps):
+    for i in range(mcfg.n_steps):
         cal.step(i)
         norms.append(cal.block_norms.double().mean().item())
-    resid = float(np.mean(norms))
+    resid = float(np.mean(norms))  # steering unit: mean token norm of block 12's output, unsteered run
     del cal
-
-    # the whole 8-step sampler loop is one graph; a partial graph of the first
-    # K mod 8 steps makes the timed count exactly K denoise steps
-    run = runtime.StepRunner(model, inp.x, inp.text, inp.seqlens, inp.t_grid, inp.guidance, inp.alpha,
-                             inp.direction, resid)
-    x_init = run.x.clone()
-    full_graph = run.capture_graph(range(cfg.n_steps))
-
-    def replay(graph):
-        run.x.copy_(x_init)  # a fresh request: the latent restarts from its noise
-        run.launch_graph(graph)
-
-    def schedule(k):
-        sched = [full_graph] * (k // cfg.n_steps)
-        if k % cfg.n_steps:
-            sched.append(run.capture_graph(range(k % cfg.n_steps)))
-        return sched
-
-    warm, timed = schedule(args.warmup), schedule(args.steps)
-    for gr in warm:
-        replay(gr)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for gr in timed:
-        replay(gr)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = start.elapsed_time(end)
-    steps_per_s = args.steps / wall
-    ok = bool(torch.isfinite(run.x).all().item())
-
-    variants = variant_loops(model, resid)
+    mloop = Loop(mmodel, minp, resid)
+    mid = mloop.timed(50 * mloop.n, 10 * mloop.n)
+    mid["launches_per_step"] = mloop.launches_per_step()
+    mid["us_per_launch"] = round(mid["median_ms_per_step"] * 1e3 / mid["launches_per_step"], 2)
+    mid["graph_noop_launch_us"] = round(floor_us, 2)
+    mloop.close()
+    mid["steering_ab"] = steering_ab(mmodel, minp, resid, mcfg.steer_alpha, mcfg.steer_steps, 30)
+    mid["gemm_mix_m512"] = mix_roofline(gemm_mix_timing(512, 1024, 4096, epilogues=True))
+    variants = variant_loops(mmodel, resid)
     variants["warm_start_mixed"] = mixed_warm_start(resid)
-    variants.update(large_model_loops())
-    ms_launch, ops_launch, bytes_launch = gemm_mix_timing(cfg)
-    floor_us = graph_floor_us()
-    achieved = ops_launch / (ms_launch / 1e3) / 1e12
-    traffic = measured_traffic()
-    serve = serve_gemm()
-    kernels = kernel_rooflines()
+    del mmodel
+    torch.cuda.empty_cache()
+    log("mid-size loops done")
 
-    # the step's algorithmic work: int8 GEMM ops of the block linears (the text
-    # K/V projection is hoisted out of the step) and attention flops
+    # ---- tiny model: one step as its own graph ----
+    tcfg = I.TINY.replace(n_steps=1)
+    tmodel = runtime.DiTModel(tcfg, I.make_params(tcfg))
+    tiny = loop_rate(tmodel, I.make_inputs(tcfg), 5.0, 200)
+    del tmodel
+
+    kernels = kernel_rooflines()
+    log("per-kernel legs done")
+
+    # the serving step's algorithmic work: int8 GEMM ops of the six block
+    # linears (the text K/V projection is hoisted) and attention flops
     M, H, F, S, T, nh = cfg.tokens, cfg.hidden, cfg.mlp, cfg.seq, cfg.text_tokens, cfg.n_heads
     int8_ops = cfg.n_blocks * sum(2.0 * M * N * K for K, N in MIX_SHAPES(H, F))
     attn_flops = cfg.n_blocks * cfg.cfg_rows * nh * 4.0 * 64 * (S * S + S * T)
-    step_s = 1.0 / steps_per_s
+    step_s = head["median_ms_per_step"] / 1e3
+    gemm_block_us = sum(v["us"] for v in serve_mix["per_shape"].values())
     line = {
         "metric": "DiT denoise steps/s (CFG batch) + W8A8 GEMM % of int8 MFMA peak on 1 GPU",
-        "value": round(steps_per_s, 2),
+        "value": head["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": head["median_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "mid-size DiT, 16 blocks, hidden 1024, 16 heads, MLP 4096, latent 256x64, "
-                               "text 128x768, CFG batch 2, W8A8, 8 Euler steps as one hipGraph, "
-                               "steering alpha 0.5 at block 12 in steps 2-5",
+        "config": {"workload": "serving batch: 24-block DiT, hidden 1536, 24 heads, MLP 6144, 8 requests x CFG "
+                               "pair = 16 rows x 512 latent tokens x 64 channels (8192 rows), text 128 x 768, W8A8 "
+                               "block linears, fp16 attention, 8 Euler steps as one hipGraph, steering node at "
+                               "block 12 with strength 0",
                    "global_batch": cfg.cfg_rows, "seq_len": cfg.seq, "parallelism": "none",
-                   "denoise_steps_per_replay": cfg.n_steps, "attention_dtype": "fp16"},
-        "event_steps_per_s": round(args.steps / (ev_ms / 1e3), 2),
-        "finite": ok,
-        "roofline": {"bound": "mfma", "kernel": "W8A8 GEMM (int8 MFMA), the step's launch mix at M = 512",
-                     "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4),
-                     "traffic": None if traffic is None else round(traffic),
-                     "avg_launch_us": round(ms_launch * 1e3, 2),
-                     "graph_noop_launch_us": round(floor_us, 2),
-                     "algorithmic_ops_per_launch": ops_launch, "algorithmic_bytes_per_launch": bytes_launch},
+                   "denoise_steps_per_replay": cfg.n_steps, "attention_dtype": "fp16",
+                   "timing": "median of per-replay HIP-event times; each replay restarts the latent from its "
+                             "noise and reuses the request's text K/V (projected once per request, 0.7 % of its "
+                             "work)"},
+        "wall_steps_per_s": head["wall_steps_per_s"],
+        "timing": head,
+        "launches_per_step": launches,
+        "roofline": {"bound": "mfma", "kernel": "W8A8 GEMM (int8 MFMA): the serving block's six launches "
+                                                "(M 8192; qkv, o, q, ox, up, down) with the step's epilogues",
+                     "achieved": serve_mix["achieved"], "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": serve_mix["frac"], "traffic": None if traffic is None else round(traffic),
+                     "avg_launch_us": serve_mix["avg_launch_us"],
+                     "algorithmic_ops_per_launch": serve_mix["algorithmic_ops_per_launch"],
+                     "algorithmic_bytes_per_launch": serve_mix["algorithmic_bytes_per_launch"],
+                     "per_shape": serve_mix["per_shape"]},
         "step_rates": {"int8_gemm_tops": round(int8_ops / step_s / 1e12, 1),
                        "attention_tflops": round(attn_flops / step_s / 1e12, 2),
-                       "int8_gemm_ops_per_step": int8_ops, "attention_flops_per_step": attn_flops},
-        "w8a8_gemm_serve": serve,
-        "loop_variants": variants,
+                       "int8_gemm_ops_per_step": int8_ops, "attention_flops_per_step": attn_flops,
+                       "gemm_share_of_step": round(cfg.n_blocks * gemm_block_us * 1e-6 / step_s, 3)},
+        "steering_ab": steer_serve,
+        "w8a8_gemm_serve": serve_plain,
+        "mid_model": dict(workload="mid-size DiT, 16 blocks, hidden 1024, 16 heads, MLP 4096, one CFG pair of 256 "
+                                   "latent tokens (512 rows), text 128 x 768, W8A8, 8 Euler steps as one hipGraph, "
+                                   "steering alpha 0.5 at block 12 in steps 2-5", **mid),
+        "tiny_one_step_graph": dict(workload="tiny DiT, 2 blocks, hidden 256, one CFG pair of 64 latent tokens, "
+                                             "W8A8, one step as its own hipGraph", **tiny),
+        "loop_variants": {**variants, **arms},
         "kernels": kernels,
+        "context_pages": PAGES_CONTEXT,
     }
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(cfg, params, inp, resid, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline()
+        log("CPU oracle done")
     print(json.dumps(line))
 
 
