@@ -60,10 +60,20 @@
 // stores); the epilogue kind (plain, residual, GELU) is a template parameter
 // so no kernel carries code it does not run.
 //
+// The int8 256 x 192 tile (the serving model's qkv, o, q, ox and down
+// projections) adds 4 producer waves to its 8 MFMA waves: they issue every
+// stage copy, so an MFMA wave never stalls on a copy instruction's issue (with
+// the copies spread over the MFMA waves, issuing them cost 15-20 % of the main
+// loop even when nothing waited for them; measured on MI355X).  12 waves fit
+// 3 per SIMD.
+//
 // Workgroups are mapped XCD-aware: consecutive workgroup ids land on
-// different XCDs (round-robin), so tile ids are remapped to give each XCD one
-// contiguous run of tiles, and that run is a compact block of the output
-// (grouped order), so the X and W panels it touches stay few and in its L2.
+// different XCDs (round-robin).  Large tiles over an X at least as large as W
+// take row bands (band_tile): each XCD owns a band of tile rows across all
+// columns, so the band's X panels stay in its L2 over all rounds (qkv at the
+// serving shapes: 9 % faster).  Other launches remap tile ids to give each XCD
+// one contiguous run of tiles that is a compact block of the output (grouped
+// order), so the X and W panels it touches stay few and in its L2.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -157,6 +167,18 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // 64-byte row layout allows (with c ^ (r & 3) the slot repeats the row's
 // half of the period and only four positions were used, eight rows each)
 __device__ __forceinline__ int q8w_swz(int r) { return (r >> 1) & 3; }
+
+// The copy layout of config C dealt to P dedicated producer waves (int8 and
+// fp16 operands: X blocks then W blocks, no padding needed when P divides
+// their count).
+template <class C, int P>
+struct ProducerCfg {
+  static constexpr bool INT = C::INT, Q4 = C::Q4, Q8W = C::Q8W;
+  static constexpr int WAVES = P, BX = C::BX, BW = C::BW, BWC = C::BW, SC0 = C::SC0, S_OFF = C::S_OFF;
+  static constexpr int LOADS = (BX + BWC) / P;
+  static_assert(!Q4 && !Q8W && (BX + BWC) % P == 0, "producer copies split evenly");
+  static_assert(LOADS * (C::STAGES - 2) < 64, "vmcnt range");
+};
 
 // The copies of one stage, dealt round-robin to the waves: X blocks, then W
 // blocks, then (Q4) scale copies.  Each lane keeps a 32-bit byte offset of
@@ -254,6 +276,17 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   const int r = t - grp * per_group;
   tm = first + r % rows;
   tn = r / rows;
+}
+
+// Row bands: XCD x (consecutive workgroup ids go round-robin to the 8 XCDs)
+// takes tile rows [x R, (x + 1) R), R = tiles_m / 8, across every tile
+// column, walked column-major, so that each round of its CUs covers R rows x
+// (CUs / R) columns and the band's X panels stay in its L2 for every round
+// (used when tiles_m is a multiple of 8 and X is the larger operand).
+__device__ __forceinline__ void band_tile(int bid, int tiles_m, int& tm, int& tn) {
+  const int R = tiles_m >> 3, x = bid & 7, loc = bid >> 3;
+  tm = x * R + loc % R;
+  tn = loc / R;
 }
 
 // GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
@@ -388,8 +421,13 @@ struct Frags {
   }
 };
 
-template <class C, int EPI>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm) {
+// P > 0: P more waves (after the C::WAVES MFMA waves) issue every stage copy,
+// so the MFMA waves never stall on copy issue; the copies of a stage are
+// still issued one stage ahead and made visible by the stage barrier.
+// bands != 0: row-band tile order (gm ignored), see band_tile.
+template <class C, int EPI, int P = 0>
+__global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm,
+                                                                          int bands) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -399,13 +437,34 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   const uint8_t* const sb = reinterpret_cast<const uint8_t*>(g.b_scale);
   const int nt = gridDim.x;
   int tm, tn;
-  tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
+  if (bands) band_tile(blockIdx.x, nt / tiles_n, tm, tn);
+  else tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   constexpr bool INT = C::INT;
   const int nk = g.K * (INT ? 1 : 2) / KB;
 
+  if constexpr (P > 0) {
+    if (wave >= C::WAVES) {  // producer: stage copies one stage ahead, one barrier per stage
+      using PC = ProducerCfg<C, P>;
+      Loader<PC> pl;
+      const int pw = wave - C::WAVES;
+      pl.init(g, m0, n0, pw, lane);
+      for (int s = 0; s < C::STAGES - 1; ++s)
+        if (s < nk) pl.issue(xb, wb, sb, pw, smem + s * C::STAGE_BYTES, s);
+      for (int kt = 0; kt < nk; ++kt) {
+        wait_stages<PC::LOADS, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
+        __builtin_amdgcn_s_barrier();
+        const int kn = kt + C::STAGES - 1;
+        if (kn < nk) pl.issue(xb, wb, sb, pw, smem + (kn % C::STAGES) * C::STAGE_BYTES, kn);
+      }
+      vm_wait<0>();
+      __syncthreads();  // the barrier that opens the MFMA waves' epilogue
+      return;
+    }
+  }
+
   Loader<C> ld;
-  ld.init(g, m0, n0, wave, lane);
+  if constexpr (P == 0) ld.init(g, m0, n0, wave, lane);
 
   AccT<C> acc[C::NJ][C::MI];
 #pragma unroll
@@ -480,7 +539,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   }
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (s < nk) ld.issue(xb, wb, sb, wave, smem + s * C::STAGE_BYTES, s);
+    if (P == 0 && s < nk) ld.issue(xb, wb, sb, wave, smem + s * C::STAGE_BYTES, s);
 
   Frags<C> fr;
   fr.init(lane, wn);
@@ -490,7 +549,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   // (a long burst of copy issues stalls the wave while the matrix pipe
   // idles), and the fragments of slice s + 1 are read during slice s.
   for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<C::LOADS, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
+    if constexpr (P == 0) wait_stages<C::LOADS, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
     __builtin_amdgcn_s_barrier();
     const int kn = kt + C::STAGES - 1;
     const bool more = kn < nk;
@@ -500,7 +559,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
     fr.read(stage, wm, wn, 0, xf[0], wf[0]);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      if (more) {
+      if (P == 0 && more) {
         if (ks == 0) ld.template issue_part<0, C::KS>(xb, wb, sb, wave, snext, kn);
         if (ks == 1) ld.template issue_part<1, C::KS>(xb, wb, sb, wave, snext, kn);
         if (ks == 2) ld.template issue_part<2, C::KS>(xb, wb, sb, wave, snext, kn);
@@ -511,6 +570,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
     }
   }
 
+  // with producers, this wave's own loads are only the epilogue scalars
+  if constexpr (P > 0) vm_wait<0>();
   // Epilogue (the residual of pass 0 was loaded up front for the small tiles)
   if constexpr (!EARLY_RES) load_res(0);
   __syncthreads();  // every wave is done with the operand stages; the scalars have landed
@@ -589,34 +650,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_dma_kernel(GemmArgs g, int
   }
 }
 
-template <class C, int EPI>
+template <class C, int EPI, int P>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + C::BM - 1) / C::BM, tn = (g.N + C::BN - 1) / C::BN;
-  // each XCD gets about tiles / 8 consecutive tiles; make that run a block of
+  // large tiles over an X larger than W: row bands per XCD (band_tile);
+  // otherwise each XCD gets about tiles / 8 consecutive tiles, a block of
   // about sqrt(run) x sqrt(run) tiles, as tall as needed to fit tn columns
+  const int bands = (C::BM == 256 && tm % 8 == 0 && g.N <= g.M) ? 1 : 0;
   const int run = (tm * tn + 7) / 8;
   int gm = (int)(sqrtf((float)run) + 0.5f);
   gm = std::max(gm, (run + tn - 1) / tn);
   gm = std::max(1, std::min(gm, tm));
-  hipLaunchKernelGGL((gemm_dma_kernel<C, EPI>), dim3((unsigned)(tm * tn)), dim3(C::THREADS), C::LDS_TOTAL, st, g,
-                     tn, gm);
+  hipLaunchKernelGGL((gemm_dma_kernel<C, EPI, P>), dim3((unsigned)(tm * tn)), dim3(C::THREADS + 64 * P),
+                     C::LDS_TOTAL, st, g, tn, gm, bands);
 }
 
-template <class C>
+template <class C, int P = 0>
 void launch_epi(const GemmArgs& g, hipStream_t st) {
   const bool res = g.epi.residual != nullptr, gelu = g.epi.act == 1;
-  if (gelu && res) launch_cfg<C, EPI_GELU_RES>(g, st);
-  else if (gelu) launch_cfg<C, EPI_GELU>(g, st);
-  else if (res) launch_cfg<C, EPI_RES>(g, st);
-  else launch_cfg<C, EPI_PLAIN>(g, st);
+  if (gelu && res) launch_cfg<C, EPI_GELU_RES, P>(g, st);
+  else if (gelu) launch_cfg<C, EPI_GELU, P>(g, st);
+  else if (res) launch_cfg<C, EPI_RES, P>(g, st);
+  else launch_cfg<C, EPI_PLAIN, P>(g, st);
 }
 
-template <class C>
+template <class C, int P = 0>
 void prep_cfg() {
-  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES>)};
+  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN, P>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES, P>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU, P>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES, P>)};
   for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
 }
 
@@ -642,6 +705,8 @@ struct Tiles {
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 4, MODE>;
   using T64 = Cfg<64, 64, 4, MODE>;
+  // producer waves of the int8 256 x 192 tile (12 waves, 3 per SIMD)
+  static constexpr int P192 = MODE == M_I8 ? 4 : 0;
 };
 
 int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
@@ -680,7 +745,7 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
       const int64_t r256 = (tiles(g.M, g.N, 256, 256) + cus - 1) / cus;
       const int64_t r192 = (tiles(g.M, g.N, 256, 192) + cus - 1) / cus;
       if (r192 * 192 * 9 < r256 * 256 * 8) {
-        launch_epi<typename T::T256x192>(g, st);
+        launch_epi<typename T::T256x192, T::P192>(g, st);
         return;
       }
     }
@@ -698,7 +763,7 @@ template <int MODE>
 void prep_mode() {
   using T = Tiles<MODE>;
   prep_cfg<typename T::T256>();
-  if constexpr (MODE != M_Q4) prep_cfg<typename T::T256x192>();
+  if constexpr (MODE != M_Q4) prep_cfg<typename T::T256x192, T::P192>();
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
   prep_cfg<typename T::T64>();

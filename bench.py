@@ -776,6 +776,17 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         sys.exit(2)
+    if args.leg == "serve_loop":  # the headline loop's timing alone (for A/B runs of two builds)
+        import ald_inputs as I
+        from audio_latent_diffusion_amd import runtime
+        cfg = I.SERVE
+        params = device_params(cfg, cfg.seed)
+        model = runtime.DiTModel(cfg, params)
+        del params
+        loop = Loop(model, I.make_inputs(cfg), 1.0)
+        print(json.dumps(loop.timed(args.steps, args.warmup)))
+        loop.close()
+        return
     if args.leg:
         counter_legs(args.leg.split(","), 20)
         return

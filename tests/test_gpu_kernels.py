@@ -140,6 +140,27 @@ def test_w8a8_serve_shapes_sampled(M, K, N):
     f16_close(host(y)[rows], yo)
 
 
+@pytest.mark.parametrize("M,K,N", [(8192, 1536, 4608), (8192, 1536, 1536), (8192, 6144, 1536), (8192, 1536, 6144)])
+def test_w8a8_serve_shapes_every_tile(M, K, N):
+    """The serving block's W8A8 launches (256 x 192 tiles with producer waves
+    for qkv, o/q/ox and down, 256 x 256 for up; row-band tile order): the
+    whole int32 accumulator against the exact integer GEMM, so every tile of
+    the launch is checked, and the fp16 output on its first and last rows."""
+    g = torch.Generator(device="cuda").manual_seed(3 * M + K + N)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+    xs = torch.rand(M, device="cuda", generator=g) * 0.01
+    ws = torch.rand(N, device="cuda", generator=g) * 0.001
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y = B.w8a8_linear(None, wq, ws, xq=xq, x_scale=xs, acc=acc, prequant=True)
+    a, w = host(xq), host(wq)
+    ref = O.int_gemm(a, w)
+    assert np.array_equal(host(acc).astype(np.int64), ref)
+    rows = np.array([0, 1, M - 2, M - 1])
+    yo = (ref[rows] * host(xs)[rows, None].astype(np.float64) * host(ws)[None, :].astype(np.float64)).astype(np.float16)
+    f16_close(host(y)[rows], yo)
+
+
 # the two large tiles of the launch, ragged in M and N, K an odd number of
 # 128-byte stages: 256 x 192 (N = 1500 fills one round of 256 CUs with 256
 # such tiles, where 256 x 256 tiles would leave 64 CUs idle) and 256 x 256
