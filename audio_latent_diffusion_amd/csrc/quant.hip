@@ -35,28 +35,62 @@ __device__ __forceinline__ void unpack8(v4i c, float f[8]) {
   for (int i = 0; i < 8; ++i) f[i] = h2f(h[i]);
 }
 
-// Codes of 8 values packed into two 32-bit words.  Each code is the
-// round-half-even of the rounded fp32 product u * inv; adding 1.5 * 2^23
-// performs that rounding and leaves the code, in two's complement, in the
-// low byte of the sum's bits.  No clamp is needed: every u of the row has
-// |u| <= amax and inv = fp32(127 / amax), so |fp32(u * inv)| <= 127 (1 + 2^-24)^2
-// < 127.5 and the code stays within [-127, 127].  The product and the add
-// are kept apart (no fused multiply-add: the product is rounded first).
-__device__ __forceinline__ uint32_t code_bits(float u, float inv) {
-#pragma clang fp contract(off)
-  const float p = u * inv;
-  return __builtin_bit_cast(uint32_t, p + 12582912.0f);
-}
+// Codes are packed 8 to two 32-bit words.  Each code is the round-half-even
+// of the rounded fp32 product u * inv; adding 1.5 * 2^23 performs that
+// rounding and leaves the code, in two's complement, in the low byte of the
+// sum's bits.  No clamp is needed: every u of the row has |u| <= amax and
+// inv = fp32(127 / amax), so |fp32(u * inv)| <= 127 (1 + 2^-24)^2 < 127.5 and
+// the code stays within [-127, 127].  The product and the add are kept apart
+// (the product is rounded first).
 __device__ __forceinline__ uint32_t pack4_codes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);  // a.byte0, b.byte0, 0, 0
   const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
   return lo | (hi << 16);
 }
-__device__ __forceinline__ v2i quant8(const float f[8], float inv) {
-  uint32_t c[8];
+// codes of 8 fp16 values: each product u * inv is formed straight from the
+// fp16 operand (a mixed-precision fused multiply-add with a zero addend,
+// v_fma_mix_f32: the exact product rounded once to fp32, the same value as
+// converting u first and multiplying), then the add
+__device__ __forceinline__ v2i quant8_h(v4i c, float inv) {
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(&c);
+  uint32_t q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = code_bits(f[i], inv);
-  return v2i{(int)pack4_codes(c[0], c[1], c[2], c[3]), (int)pack4_codes(c[4], c[5], c[6], c[7])};
+  for (int i = 0; i < 8; ++i) {
+    const float p = __builtin_fmaf(h2f(h[i]), inv, 0.0f);
+    q[i] = __builtin_bit_cast(uint32_t, p + 12582912.0f);
+  }
+  return v2i{(int)pack4_codes(q[0], q[1], q[2], q[3]), (int)pack4_codes(q[4], q[5], q[6], q[7])};
+}
+
+// max |u| over 8 packed fp16 values, folded into a pair of 16-bit maxima:
+// for finite fp16 the magnitude bits order like the magnitudes, so the max
+// of (bits & 0x7FFF) is the bit pattern of the largest |u|, exactly
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 absmax8_h(u16x2 acc, v4i c) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&c);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu));
+  return acc;
+}
+
+// max of a non-negative integer over the wave (the DPP pattern of wave_sum)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_mov_u<0xB1, 0xF>(v));
+  v = max(v, dpp_mov_u<0x4E, 0xF>(v));
+  v = max(v, dpp_mov_u<0x141, 0xF>(v));
+  v = max(v, dpp_mov_u<0x140, 0xF>(v));
+  v = max(v, dpp_mov_u<0x142, 0xA>(v));
+  v = max(v, dpp_mov_u<0x143, 0x8>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// amax of a row from its lanes' 16-bit maxima, as fp32
+__device__ __forceinline__ float row_absmax(u16x2 acc) {
+  return h2f((uint16_t)wave_max_u32(max((uint32_t)acc.x, (uint32_t)acc.y)));
 }
 
 // amax -> (scale, reciprocal); amax == 0 -> (0, 0) so every code is 0
@@ -70,25 +104,20 @@ __device__ __forceinline__ void q8_scale(float amax, float& s, float& inv) {
   }
 }
 
-// codes and scale of one row held in registers
+// codes and scale of one row held in registers (no conversion of the row to
+// fp32: the amax from the fp16 bits, the products from fp16 operands)
 template <int NV, bool FULL>
 __device__ __forceinline__ void quant_row_regs(const RowRegs<NV>& r, int K, int lane, int8_t* __restrict__ qrow,
                                                float* __restrict__ scale_m) {
-  float f[NV][8];
-  float amax = 0.0f;
+  u16x2 acc = {0, 0};
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    unpack8(r.c[j], f[j]);  // padding chunks are zero
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[j][i]));
-  }
-  amax = wave_max_nonneg(amax);
+  for (int j = 0; j < NV; ++j) acc = absmax8_h(acc, r.c[j]);  // padding chunks are zero
   float s, inv;
-  q8_scale(amax, s, inv);
+  q8_scale(row_absmax(acc), s, inv);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (lane + WAVE * j) * 8;
-    if (FULL || e < K) st8_nt(qrow + e, quant8(f[j], inv));
+    if (FULL || e < K) st8_nt(qrow + e, quant8_h(r.c[j], inv));
   }
   if (lane == 0) *scale_m = s;
 }
@@ -119,38 +148,44 @@ __global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restri
 }
 
 // LayerNorm of one row held in registers (FULL: every chunk lies inside the
-// row): statistics in fp32 over the values converted once, output rounded to
-// fp16 into `out` (which may be `r` itself: r is read only before the first
-// write); u receives the fp16 result converted back to fp32 and the function
-// returns max |u| of this lane.
+// row): statistics in fp32 (the sum as pairwise sums of the fp16 values, the
+// square sums in two chains per chunk, so no long dependent chain sits
+// between the row's loads and its reductions), output rounded to fp16 into
+// `out` (which may be `r` itself: r is read only before the first write).
 template <int NV, bool FULL>
-__device__ __forceinline__ float layer_norm_row(const RowRegs<NV>& r, int H, int lane, const float* __restrict__ g,
-                                                const float* __restrict__ b, float eps, float (&u)[NV][8],
-                                                RowRegs<NV>& out) {
+__device__ __forceinline__ void layer_norm_row(const RowRegs<NV>& r, int H, int lane, const float* __restrict__ g,
+                                               const float* __restrict__ b, float eps, RowRegs<NV>& out) {
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    unpack8(r.c[j], u[j]);  // padding chunks are zero
+  for (int j = 0; j < NV; ++j) {  // padding chunks are zero
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&r.c[j]);
+    float p[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sum += u[j][i];
+    for (int k = 0; k < 4; ++k) p[k] = h2f((uint16_t)(w[k] & 0xFFFFu)) + h2f((uint16_t)(w[k] >> 16));
+    sum += (p[0] + p[1]) + (p[2] + p[3]);
   }
   const float inv_h = 1.0f / (float)H;  // loop-invariant: hoisted out of the row loop
   const float mean = wave_sum(sum) * inv_h;
+  float d[NV][8];
   float sq = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (lane + WAVE * j) * 8;
     if (FULL || e < H) {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(&r.c[j]);
+      float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        u[j][i] -= mean;
-        sq = fmaf(u[j][i], u[j][i], sq);
+      for (int i = 0; i < 8; i += 2) {
+        d[j][i] = h2f(h[i]) - mean;
+        d[j][i + 1] = h2f(h[i + 1]) - mean;
+        s0 = fmaf(d[j][i], d[j][i], s0);
+        s1 = fmaf(d[j][i + 1], d[j][i + 1], s1);
       }
+      sq += s0 + s1;
     }
   }
   const float var = wave_sum(sq) * inv_h;
   const float rstd = __builtin_amdgcn_rsqf(var + eps);  // hardware 1/sqrt (1 ulp)
-  float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (lane + WAVE * j) * 8;
@@ -163,14 +198,9 @@ __device__ __forceinline__ float layer_norm_row(const RowRegs<NV>& r, int H, int
       const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       uint16_t* h = reinterpret_cast<uint16_t*>(&out.c[j]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        h[i] = f2h(fmaf(u[j][i] * rstd, gg[i], bb[i]));
-        u[j][i] = h2f(h[i]);
-        amax = fmaxf(amax, fabsf(u[j][i]));
-      }
+      for (int i = 0; i < 8; ++i) h[i] = f2h(fmaf(d[j][i] * rstd, gg[i], bb[i]));
     }
   }
-  return amax;
 }
 
 template <int NV, bool FULL>
@@ -189,18 +219,24 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
     const int mn = m + stride;
     RowRegs<NV> nx;
     if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
-    float u[NV][8];
     RowRegs<NV>& y = r;  // the normalized row replaces the input row
-    const float amax = wave_max_nonneg(layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, u, y));
+    layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, y);
+    // the quantizer reads the fp16 LayerNorm output
+    u16x2 acc = {0, 0};
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = (lane + WAVE * j) * 8;
+      if (FULL || e < H) acc = absmax8_h(acc, y.c[j]);
+    }
     float s, inv;
-    q8_scale(amax, s, inv);
+    q8_scale(row_absmax(acc), s, inv);
     int8_t* qrow = q + (int64_t)m * H;
     uint16_t* urow = u_out ? u_out + (int64_t)m * H : nullptr;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = (lane + WAVE * j) * 8;
       if (FULL || e < H) {
-        st8_nt(qrow + e, quant8(u[j], inv));
+        st8_nt(qrow + e, quant8_h(y.c[j], inv));
         if (urow) st16_nt(urow + e, y.c[j]);
       }
     }
@@ -227,9 +263,8 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
     const int mn = m + stride;
     RowRegs<NV> nx;
     if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
-    float u[NV][8];
     RowRegs<NV>& o = r;  // the normalized row replaces the input row
-    (void)layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, u, o);
+    layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, o);
     uint16_t* yrow = y + (int64_t)m * ldy;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -288,6 +323,17 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const uint16_t* __restrict
 // wave (LayerNorm + quantization 63 -> 53 %)
 constexpr int64_t ROW_GRID_CAP = 16384;
 
+// workgroups of a row kernel over M rows: one row per wave up to the cap, or,
+// with `two_rows` (LayerNorm + quantization, whose reductions leave the load
+// path idle longer), two rows per wave once one per wave would take more
+// than 1024 workgroups: 8192 rows of 1536 take 9.1 us instead of 10.1 us, 8192
+// rows of 2048 11.5 us instead of 12.7 (MI355X)
+inline unsigned row_grid(int64_t M, bool two_rows) {
+  const int64_t one = (M + 3) / 4;
+  if (!two_rows || one <= 1024) return (unsigned)std::min(one, ROW_GRID_CAP);
+  return (unsigned)std::min(std::max<int64_t>((M + 7) / 8, 1024), ROW_GRID_CAP);
+}
+
 #define ALD_ROW_LAUNCH(KERNEL, NV, K, GRID, ST, ...)                                                 \
   do {                                                                                               \
     if ((K) == (NV) * 512) hipLaunchKernelGGL((KERNEL<NV, true>), GRID, dim3(256), 0, ST, __VA_ARGS__); \
@@ -295,9 +341,9 @@ constexpr int64_t ROW_GRID_CAP = 16384;
   } while (0)
 
 // one wave per row: NV 16-byte chunks per lane cover K values (NV * 512 >= K)
-#define ALD_ROW_DISPATCH(KERNEL, K, M, ST, ...)                                                      \
+#define ALD_ROW_DISPATCH(KERNEL, K, M, TWO, ST, ...)                                                 \
   do {                                                                                               \
-    dim3 grid_((unsigned)std::min<int64_t>(((M) + 3) / 4, ROW_GRID_CAP));                            \
+    dim3 grid_(row_grid((M), (TWO)));                                                                \
     const int nv_ = ((K) + 511) / 512;                                                               \
     if (nv_ <= 1) ALD_ROW_LAUNCH(KERNEL, 1, K, grid_, ST, __VA_ARGS__);                              \
     else if (nv_ <= 2) ALD_ROW_LAUNCH(KERNEL, 2, K, grid_, ST, __VA_ARGS__);                         \
@@ -312,19 +358,19 @@ constexpr int64_t ROW_GRID_CAP = 16384;
 void launch_row_quant(const uint16_t* x, int64_t ldx, int M, int K, int8_t* q, int64_t ldq, float* scale,
                       hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(row_quant_kernel, K, M, st, x, ldx, M, K, q, ldq, scale);
+  ALD_ROW_DISPATCH(row_quant_kernel, K, M, false, st, x, ldx, M, K, q, ldq, scale);
 }
 
 void launch_ln_quant(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
                      uint16_t* u_out, int8_t* q, float* scale, hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(ln_quant_kernel, H, M, st, x, ldx, M, H, g, b, eps, u_out, q, scale);
+  ALD_ROW_DISPATCH(ln_quant_kernel, H, M, true, st, x, ldx, M, H, g, b, eps, u_out, q, scale);
 }
 
 void launch_ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
                    uint16_t* y, int64_t ldy, hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(ln_f16_kernel, H, M, st, x, ldx, M, H, g, b, eps, y, ldy);
+  ALD_ROW_DISPATCH(ln_f16_kernel, H, M, false, st, x, ldx, M, H, g, b, eps, y, ldy);
 }
 
 void launch_q4_pack(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* scales, hipStream_t st) {

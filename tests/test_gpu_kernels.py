@@ -56,7 +56,9 @@ def test_quantize_q4_bit_exact(N, K):
     assert np.array_equal(host(s).view(np.uint16), so.view(np.uint16))
 
 
-@pytest.mark.parametrize("M,H", [(1, 64), (13, 256), (128, 1024), (40, 1536), (9, 2048)])
+# 5003 rows: more than 1024 four-row workgroups, so LayerNorm + quantization
+# walks two rows per wave, with a ragged second round
+@pytest.mark.parametrize("M,H", [(1, 64), (13, 256), (128, 1024), (40, 1536), (9, 2048), (5003, 1536)])
 def test_ln_quant(M, H):
     r = rng(M + H)
     x = (r.standard_normal((M, H)) * 2 + 0.5).astype(np.float16)
