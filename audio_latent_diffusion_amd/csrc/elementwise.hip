@@ -390,102 +390,103 @@ __global__ void cu_pairs_kernel(const int32_t* __restrict__ cu, int R, int64_t n
 // Input projection of the fp32 latent with the sinusoidal time embedding:
 //   h[m, n] = fp16( sum_k fp16(x[m % n_tok, k]) w_in[n, k] + b_in[n] + temb(t_r, n) )
 // for both CFG rows of every token (row m reads latent token m % n_tok, request
-// r of that token).  K (the latent width) is tiny, so this is a VALU kernel:
-// 64 x 64 output tiles, operands staged through LDS as fp32 (the fp16 products
-// are exact in fp32), 4 x 4 outputs per thread.
+// r of that token), on the matrix cores: v_mfma_f32_32x32x16_f16 forms the
+// fp16 products exactly and accumulates them in fp32.  Each wave computes a
+// 64 x 64 block (2 x 2 MFMA blocks of 32 x 32) over K (the latent width, a
+// multiple of 8) in steps of 16, zero-padded.  The operands go straight from
+// global memory into registers in the MFMA layout (lane l: row of its block
+// l % 32, the 8 values at K offset 8 (l / 32) of the step), converted to fp16
+// on the way; with K this small nothing is worth sharing through LDS.  The
+// weight fragment is the first operand, so accumulator register r of lane l
+// holds row l % 32 and column 8 (r / 4) + 4 (l / 32) + r % 4 of its block:
+// four consecutive columns per register quad, written as one 8-byte store.
 //   temb(t, n) = sin(1000 t w_j) for n < H/2, cos(1000 t w_j) after,
 //   w_j = exp(-ln(1e4) j / (H/2)), j = n mod H/2.
-// The argument reaches 1000 rad: it is reduced to a fraction of a turn here and
-// fed to the hardware sine (input in turns); the fp32 argument itself already
-// carries ~1e-4 rad of rounding error.
-__device__ __forceinline__ float temb_value(float t, int col, int H) {
-  const int half = H >> 1;
-  const int j = col < half ? col : col - half;
-  const float om = __expf(-9.210340371976184f * (float)j / (float)half);
-  float turns = 1000.0f * t * om * 0.15915494309189535f;
-  if (col >= half) turns += 0.25f;  // cos x = sin(x + pi/2)
-  turns -= floorf(turns);
-  return __builtin_amdgcn_sinf(turns);
-}
-
-// 32 x 32 output tiles, 256 threads of 2 x 2 outputs: at the 512-token step
-// (hidden 1024) that is 512 workgroups over all CUs, where 64 x 64 tiles gave
-// 128 and spent their time in LDS reads and FMAs of 16 outputs per thread
-constexpr int IP_T = 32;
-constexpr int IP_K = 64;  // K slab per pass
-
-__global__ __launch_bounds__(256) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M, int C,
-                                                     const uint16_t* __restrict__ w, int H,
-                                                     const float* __restrict__ bias, const float* __restrict__ t_cur,
-                                                     RowMap map, uint16_t* __restrict__ h) {
-  __shared__ float xs[IP_T][IP_K + 1];
-  __shared__ float wsm[IP_T][IP_K + 1];
-  const int tid = threadIdx.x;
-  const int n0 = blockIdx.x * IP_T;
-  const int tr = (tid >> 4) * 2, tc = (tid & 15) * 2;
+// 1000 w_j / (2 pi) (turns per unit of t) is computed once per workgroup and
+// column into LDS; per output the argument is t times it (plus a quarter turn
+// for the cosine half), reduced to a fraction of a turn and fed to the
+// hardware sine (input in turns).  The argument reaches 1000 rad and the fp32
+// value carries ~1e-4 rad of rounding error.
+template <int WGN, int WGM>
+__global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M,
+                                                                int C, const uint16_t* __restrict__ w, int H,
+                                                                const float* __restrict__ bias,
+                                                                const float* __restrict__ t_cur, RowMap map,
+                                                                uint16_t* __restrict__ h) {
+  constexpr int TN = 64 * WGN, TM = 64 * WGM;
+  __shared__ float turns_per_t[TN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * TN;
+  for (int i = tid; i < TN; i += 64 * WGN * WGM) {
+    const int half = H >> 1, col = n0 + i;
+    const int j = col < half ? col : col - half;
+    turns_per_t[i] = 1000.0f * __expf(-9.210340371976184f * (float)j / (float)half) * 0.15915494309189535f;
+  }
+  __syncthreads();
+  const int li = lane & 31, hi = lane >> 5;
+  const int cw = (wave % WGN) * 64;  // this wave's columns within the tile
+  int64_t wrow[2];
+#pragma unroll
+  for (int bj = 0; bj < 2; ++bj) wrow[bj] = (int64_t)min(n0 + cw + 32 * bj + li, H - 1) * C;
   // row tiles beyond the grid's y extent (65535) are walked with its stride
-  for (int m0 = blockIdx.y * IP_T; m0 < M; m0 += gridDim.y * IP_T) {
-    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    for (int k0 = 0; k0 < C; k0 += IP_K) {
-      // every load of the slab is issued before any is used: 2 x 16 bytes of
-      // latent and 16 bytes of weights per thread (C % 8 == 0)
-      float4 xv[2];
-      v4i wv;
+  for (int m0 = blockIdx.y * TM; m0 < M; m0 += gridDim.y * TM) {
+    const int mw = m0 + (wave / WGN) * 64;
+    int64_t xrow[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4, m = m0 + r;
-        xv[q] = (m < M && k0 + k < C) ? *reinterpret_cast<const float4*>(x + (m % n_tok) * C + k0 + k)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      {
-        const int r = tid >> 3, k = (tid & 7) * 8, n = n0 + r;
-        wv = (n < H && k0 + k < C) ? ld16(w + (int64_t)n * C + k0 + k) : v4i{0, 0, 0, 0};
+    for (int bi = 0; bi < 2; ++bi) xrow[bi] = (int64_t)(min(mw + 32 * bi + li, M - 1) % n_tok) * C;
+    v16f acc[2][2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const int kk = k0 + 8 * hi;
+      v8h xf[2], wf[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        if (kk < C) {
+          const float4 a = *reinterpret_cast<const float4*>(x + xrow[bi] + kk);
+          const float4 b = *reinterpret_cast<const float4*>(x + xrow[bi] + kk + 4);
+          xf[bi] = v8h{(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                       (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+        } else {
+          xf[bi] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int i = tid + 256 * q, r = i >> 4, k = (i & 15) * 4;
-        xs[r][k] = h2f(f2h(xv[q].x));
-        xs[r][k + 1] = h2f(f2h(xv[q].y));
-        xs[r][k + 2] = h2f(f2h(xv[q].z));
-        xs[r][k + 3] = h2f(f2h(xv[q].w));
-      }
-      {
-        const int r = tid >> 3, k = (tid & 7) * 8;
-        const uint16_t* hv = reinterpret_cast<const uint16_t*>(&wv);
+      for (int bj = 0; bj < 2; ++bj)
+        wf[bj] = kk < C ? __builtin_bit_cast(v8h, ld16(w + wrow[bj] + kk)) : v8h{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wsm[r][k + e] = h2f(hv[e]);
-      }
-      __syncthreads();
-#pragma unroll 16
-      for (int k = 0; k < IP_K; ++k) {
-        const float xa0 = xs[tr][k], xa1 = xs[tr + 1][k];
-        const float wb0 = wsm[tc][k], wb1 = wsm[tc + 1][k];
-        acc[0][0] = fmaf(xa0, wb0, acc[0][0]);
-        acc[0][1] = fmaf(xa0, wb1, acc[0][1]);
-        acc[1][0] = fmaf(xa1, wb0, acc[1][0]);
-        acc[1][1] = fmaf(xa1, wb1, acc[1][1]);
-      }
-      __syncthreads();
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[bj], xf[bi], acc[bi][bj], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = m0 + tr + i;
+    for (int bi = 0; bi < 2; ++bi) {
+      const int m = mw + 32 * bi + li;
       if (m >= M) continue;
-      const float t = t_cur[req_of(map, m)];
-      uint16_t o[2];
+      const float t = t_cur[req_of(map, (uint32_t)m)];
+      uint16_t* hrow = h + (int64_t)m * H;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = min(n0 + tc + j, H - 1);
-        o[j] = f2h(acc[i][j] + bias[n] + temb_value(t, n, H));
-      }
-      uint16_t* hp = h + (int64_t)m * H + n0 + tc;
-      if (n0 + tc + 1 < H && (H & 1) == 0) {
-        *reinterpret_cast<uint32_t*>(hp) = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-      } else {
+      for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (n0 + tc + j < H) hp[j] = o[j];
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int cl = cw + 32 * bj + 8 * q + 4 * hi;  // column within the tile
+          const int col = n0 + cl;
+          if (col >= H) continue;  // H % 16 == 0: a quad is inside or outside as a whole
+          uint32_t o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float turns = t * turns_per_t[cl + r];
+            if (col + r >= (H >> 1)) turns += 0.25f;  // cos x = sin(x + pi/2)
+            turns -= floorf(turns);
+            o[r] = f2h(acc[bi][bj][4 * q + r] + bias[col + r] + __builtin_amdgcn_sinf(turns));
+          }
+          *reinterpret_cast<uint2*>(hrow + col) = make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+        }
     }
   }
 }
@@ -493,8 +494,16 @@ __global__ __launch_bounds__(256) void inproj_kernel(const float* __restrict__ x
 void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* w, int H, const float* bias,
                    const float* t_cur, RowMap map, uint16_t* h, hipStream_t st) {
   if (M <= 0 || H <= 0) return;
-  dim3 grid((unsigned)((H + IP_T - 1) / IP_T), (unsigned)std::min<int64_t>((M + IP_T - 1) / IP_T, 65535));
-  hipLaunchKernelGGL(inproj_kernel, grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+  // 128 x 128 tiles of four waves, or single-wave 64 x 64 tiles when the
+  // large ones would not give every CU a workgroup (the 512-row step)
+  const int64_t big = (int64_t)((H + 127) / 128) * ((M + 127) / 128);
+  if (big >= 256) {
+    dim3 grid((unsigned)((H + 127) / 128), (unsigned)std::min<int64_t>((M + 127) / 128, 65535));
+    hipLaunchKernelGGL((inproj_kernel<2, 2>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+  } else {
+    dim3 grid((unsigned)((H + 63) / 64), (unsigned)std::min<int64_t>((M + 63) / 64, 65535));
+    hipLaunchKernelGGL((inproj_kernel<1, 1>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+  }
 }
 
 static inline dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }

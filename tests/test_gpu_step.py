@@ -91,6 +91,36 @@ def _oracle_steps(om, inp, steps, resid=RESID):
     return x, tr
 
 
+# A model with no blocks: the velocity is the output projection of the final
+# LayerNorm of the input projection, so these check the input projection and
+# its time embedding over every row directly.  Serving widths (8192 rows:
+# four-wave 128 x 128 tiles), the mid-size step (512 rows: single-wave 64 x 64
+# tiles) and ragged packed requests at hidden 1088 on both tile kinds (7216
+# rows: the last row tile and the last column tile cut short; 284 rows).
+# Bar: the fp16 rounding of h, the fp32 sums and the time embedding's ~1e-4
+# rad argument error move v by a few fp16 ulps of its largest entry.
+INPROJ_TOL = 2e-3
+
+
+@pytest.mark.parametrize("name", ["serve", "mid", "ragged_large", "ragged_small"])
+def test_input_projection_zero_blocks(name):
+    if name in ("serve", "mid"):
+        cfg = (I.SERVE if name == "serve" else I.MID).replace(n_blocks=0, steer_block=-1)
+        inp = I.make_inputs(cfg)
+    else:
+        lens = [1500, 2011, 97] if name == "ragged_large" else [37, 100, 5]
+        cfg = I.TINY.replace(n_blocks=0, steer_block=-1, requests=3, hidden=1088, n_heads=17)
+        inp = I.make_inputs(cfg, seqlens=np.array(lens))
+    p = I.make_params(cfg)
+    om = O.prepare_model(cfg, p)
+    step = 3  # t = 5/8, not 1: the embedding arguments differ from the first step's
+    _, _, vg = _gpu_steps(runtime.DiTModel(cfg, p), inp, [step])
+    _, _, tr = S.oracle_steps(om, inp, [step], RESID)
+    err = S.rel(vg, tr.v)
+    print(f"{name}: input projection (zero blocks) velocity err {err:.2e} (bar {INPROJ_TOL:.0e})")
+    assert err < INPROJ_TOL
+
+
 @pytest.mark.parametrize("wmode", ["w8a8", "f16", "q4", "w8a16"])
 def test_tiny_step_parity(wmode):
     """One steered step of the tiny DiT in each weight precision, and the
