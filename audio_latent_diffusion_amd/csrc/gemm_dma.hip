@@ -671,21 +671,22 @@ void launch_cfg(const GemmArgs& g, hipStream_t st) {
                      C::LDS_TOTAL, st, g, tn, gm, bands);
 }
 
-template <class C, int P = 0>
+// P producer waves for the epilogues without a residual, PR with one
+template <class C, int P = 0, int PR = P>
 void launch_epi(const GemmArgs& g, hipStream_t st) {
   const bool res = g.epi.residual != nullptr, gelu = g.epi.act == 1;
-  if (gelu && res) launch_cfg<C, EPI_GELU_RES, P>(g, st);
+  if (gelu && res) launch_cfg<C, EPI_GELU_RES, PR>(g, st);
   else if (gelu) launch_cfg<C, EPI_GELU, P>(g, st);
-  else if (res) launch_cfg<C, EPI_RES, P>(g, st);
+  else if (res) launch_cfg<C, EPI_RES, PR>(g, st);
   else launch_cfg<C, EPI_PLAIN, P>(g, st);
 }
 
-template <class C, int P = 0>
+template <class C, int P = 0, int PR = P>
 void prep_cfg() {
   const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN, P>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES, P>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES, PR>),
                       reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU, P>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES, P>)};
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES, PR>)};
   for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
 }
 
@@ -711,8 +712,11 @@ struct Tiles {
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 4, MODE>;
   using T64 = Cfg<64, 64, 4, MODE>;
-  // producer waves of the int8 256 x 192 tile (12 waves, 3 per SIMD)
+  // producer waves of the int8 large tiles (12 waves, 3 per SIMD); the
+  // 256 x 256 tile takes them only without a residual epilogue (with one its
+  // MFMA waves would not fit 3 per SIMD without spilling)
   static constexpr int P192 = MODE == M_I8 ? 4 : 0;
+  static constexpr int P256 = MODE == M_I8 ? 4 : 0;
 };
 
 int64_t tiles(int M, int N, int bm, int bn) { return (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
@@ -755,7 +759,7 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
         return;
       }
     }
-    launch_epi<typename T::T256>(g, st);
+    launch_epi<typename T::T256, T::P256, 0>(g, st);
   } else if (tiles(g.M, g.N, 128, 128) >= FILL) {
     launch_epi<typename T::T128>(g, st);
   } else if (tiles(g.M, g.N, 128, 64) >= FILL) {
@@ -768,7 +772,7 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
 template <int MODE>
 void prep_mode() {
   using T = Tiles<MODE>;
-  prep_cfg<typename T::T256>();
+  prep_cfg<typename T::T256, T::P256, 0>();
   if constexpr (MODE != M_Q4) prep_cfg<typename T::T256x192, T::P192>();
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
