@@ -498,7 +498,11 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   const int rl0 = lane / LPR;
   const int rbase = m0 + wm * C::WM;
   const int lr = lane & 31;
-  uint4 resv[RES ? NIT : 1];
+  // residual of a pass, double buffered: pass p + 1's loads are issued before
+  // pass p is processed, so their latency hides behind it
+  constexpr int NPASS = C::WN / PW;
+  constexpr int RBUF = RES ? (NPASS > 1 ? 2 : 1) : 1;
+  uint4 resv[RBUF][RES ? NIT : 1];
   auto load_res = [&](int p) {
     if constexpr (RES) {
       const int col = n0 + wn * C::WN + p * PW + cl;
@@ -508,12 +512,13 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
         const int row = min(rbase + it * RPI + rl0, g.M - 1);
         const uint16_t* rp = e.residual + (int64_t)row * e.ldr + min(col, g.N - 1);
         if (vec && left >= 8) {
-          resv[it] = *reinterpret_cast<const uint4*>(rp);
+          resv[p % RBUF][it] = *reinterpret_cast<const uint4*>(rp);
         } else {
           uint16_t h[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r) h[r] = r < left ? rp[r] : (uint16_t)0;
-          resv[it] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+          resv[p % RBUF][it] =
+              make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
         }
       }
     }
@@ -585,7 +590,7 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   const float* sc = reinterpret_cast<const float*>(smem + C::SC_OFF);
 #pragma unroll
   for (int p = 0; p < C::WN / PW; ++p) {
-    if (p > 0) load_res(p);
+    if (p + 1 < NPASS) load_res(p + 1);
 #pragma unroll
     for (int jj = 0; jj < PW / 32; ++jj) {
       const int j = p * (PW / 32) + jj;
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
         if (!e.y) continue;
         const float xs = sc[wm * C::WM + rl];
         float res[8];
-        if constexpr (RES) unpack_h8(resv[it], res);
+        if constexpr (RES) unpack_h8(resv[p % RBUF][it], res);
         uint32_t o[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
