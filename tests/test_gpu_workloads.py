@@ -7,8 +7,9 @@ the 4-bit widths (hidden 2048, MLP 8192, 4 requests x 1024 tokens) in
 seconds, so those are checked element by element: the model output of both
 CFG rows, the latent's increment over the step and the latent itself, each
 within 2e-2 (max |g - o| / max |o|), and at the serving widths the steering's
-own effect on the model output (bar 0.1).  The full 24-block serving model is
-checked the same way on one request (1024 CFG rows).  The mixed warm-start
+own effect on the model output (bar 0.1).  The full 24-block serving model and
+the full 24-block 4-bit model are checked the same way on one request (1024
+and 2048 CFG rows).  The mixed warm-start
 batch runs the full 16-block mid-size model on a 4-request packed sub-batch
 (lengths 128, 129, 577, 1024; two cold, two warm, one re-noised inside the
 checked steps); the full 32-request batch must give each request, bit for
@@ -96,6 +97,16 @@ def test_serve_full_depth_one_request():
     the oracle."""
     cfg = I.SERVE.replace(requests=1, steer_alpha=0.5, steer_steps=(0,))
     _parity(cfg, [0], resid=RESID_SERVE)
+
+
+@pytest.mark.timeout(900)
+def test_q4_full_depth_one_request():
+    """The full 24-block 4-bit-weight model (hidden 2048, 32 heads, MLP 8192,
+    group-32 weights with fp16 scales) on one request, a CFG pair of 1024
+    latent tokens (2048 rows), steering at block 12 active: the step's model
+    output, increment and latent against the oracle."""
+    cfg = I.Q4.replace(requests=1, steer_alpha=0.5, steer_steps=(0,))
+    _parity(cfg, [0])
 
 
 @pytest.fixture(scope="module")
