@@ -407,13 +407,16 @@ __global__ void cu_pairs_kernel(const int32_t* __restrict__ cu, int R, int64_t n
 // for the cosine half), reduced to a fraction of a turn and fed to the
 // hardware sine (input in turns).  The argument reaches 1000 rad and the fp32
 // value carries ~1e-4 rad of rounding error.
-template <int WGN, int WGM>
+// CK > 0: the latent width is the compile-time CK (the K loop unrolls and all
+// of a tile's operand loads are in flight at once); CK = 0: any multiple of 8
+template <int WGN, int WGM, int CK>
 __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M,
-                                                                int C, const uint16_t* __restrict__ w, int H,
+                                                                int C_rt, const uint16_t* __restrict__ w, int H,
                                                                 const float* __restrict__ bias,
                                                                 const float* __restrict__ t_cur, RowMap map,
                                                                 uint16_t* __restrict__ h) {
   constexpr int TN = 64 * WGN, TM = 64 * WGM;
+  const int C = CK > 0 ? CK : C_rt;
   __shared__ float turns_per_t[TN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * TN;
@@ -441,6 +444,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __r
       for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
+#pragma unroll
     for (int k0 = 0; k0 < C; k0 += 16) {
       const int kk = k0 + 8 * hi;
       v8h xf[2], wf[2];
@@ -496,13 +500,20 @@ void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* 
   if (M <= 0 || H <= 0) return;
   // 128 x 128 tiles of four waves, or single-wave 64 x 64 tiles when the
   // large ones would not give every CU a workgroup (the 512-row step)
+  // (the latent width 64 of every model here takes the unrolled kernels)
   const int64_t big = (int64_t)((H + 127) / 128) * ((M + 127) / 128);
   if (big >= 256) {
     dim3 grid((unsigned)((H + 127) / 128), (unsigned)std::min<int64_t>((M + 127) / 128, 65535));
-    hipLaunchKernelGGL((inproj_kernel<2, 2>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+    if (C == 64)
+      hipLaunchKernelGGL((inproj_kernel<2, 2, 64>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+    else
+      hipLaunchKernelGGL((inproj_kernel<2, 2, 0>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
   } else {
     dim3 grid((unsigned)((H + 63) / 64), (unsigned)std::min<int64_t>((M + 63) / 64, 65535));
-    hipLaunchKernelGGL((inproj_kernel<1, 1>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+    if (C == 64)
+      hipLaunchKernelGGL((inproj_kernel<1, 1, 64>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+    else
+      hipLaunchKernelGGL((inproj_kernel<1, 1, 0>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
   }
 }
 

@@ -95,17 +95,21 @@ def _oracle_steps(om, inp, steps, resid=RESID):
 # LayerNorm of the input projection, so these check the input projection and
 # its time embedding over every row directly.  Serving widths (8192 rows:
 # four-wave 128 x 128 tiles), the mid-size step (512 rows: single-wave 64 x 64
-# tiles) and ragged packed requests at hidden 1088 on both tile kinds (7216
-# rows: the last row tile and the last column tile cut short; 284 rows).
+# tiles), ragged packed requests at hidden 1088 on both tile kinds (7216
+# rows: the last row tile and the last column tile cut short; 284 rows) and
+# a latent width of 72.
 # Bar: the fp16 rounding of h, the fp32 sums and the time embedding's ~1e-4
 # rad argument error move v by a few fp16 ulps of its largest entry.
 INPROJ_TOL = 2e-3
 
 
-@pytest.mark.parametrize("name", ["serve", "mid", "ragged_large", "ragged_small"])
+@pytest.mark.parametrize("name", ["serve", "mid", "ragged_large", "ragged_small", "width_72"])
 def test_input_projection_zero_blocks(name):
     if name in ("serve", "mid"):
         cfg = (I.SERVE if name == "serve" else I.MID).replace(n_blocks=0, steer_block=-1)
+        inp = I.make_inputs(cfg)
+    elif name == "width_72":  # a latent width other than 64: the generic K loop, its last step half padded
+        cfg = I.TINY.replace(n_blocks=0, steer_block=-1, channels=72)
         inp = I.make_inputs(cfg)
     else:
         lens = [1500, 2011, 97] if name == "ragged_large" else [37, 100, 5]
