@@ -117,15 +117,17 @@ struct Cfg {
   static constexpr int RS = PW + 4;
   static constexpr int EPI_LDS = WAVES * WM * (RS + 1) * 4;
   // per-row and per-column epilogue scalars (x_scale[BM], w_scale[BN], bias[BN])
+  // (padded to whole copy instructions of 64 scalars)
   static constexpr int SC_OFF = LDS > EPI_LDS ? LDS : EPI_LDS;
-  static constexpr int LDS_TOTAL = SC_OFF + (BM + 2 * BN) * 4;
-  static constexpr int SC_LOADS = (BM + 2 * BN) / 64;  // 64 scalars per copy instruction
+  static constexpr int SC_N = BM + 2 * BN, SC_PAD = (SC_N + 63) / 64 * 64;
+  static constexpr int LDS_TOTAL = SC_OFF + SC_PAD * 4;
+  static constexpr int SC_LOADS = SC_PAD / 64;  // 64 scalars per copy instruction
   static_assert((BX + BWC + SCL) % WAVES == 0, "copies must split evenly over the waves");
   static_assert(BX % WAVES == 0, "X copies take whole rounds over the waves");
   static_assert(MI >= 1 && NJ >= 1 && WM == 32 * MI && WN == 32 * NJ, "wave tile");
   static_assert(LDS_TOTAL <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "scalar copies cover whole tiles");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "whole 32 x 32 MFMA blocks");
   static_assert(WN % PW == 0 && PW % 32 == 0, "epilogue passes cover the wave tile");
 };
 
@@ -536,12 +538,13 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
     float* sc = reinterpret_cast<float*>(smem + C::SC_OFF);
 #pragma unroll
     for (int i = wave; i < C::SC_LOADS; i += C::WAVES) {
-      const int q = i * 64 + lane;  // x_scale rows, then w_scale columns, then bias columns
+      const int q = i * 64 + lane;  // x_scale rows, then w_scale columns, then bias columns, then padding
       const float* src;
       if (q < C::BM) src = e.x_scale ? e.x_scale + min(m0 + q, g.M - 1) : nullptr;
       else if (q < C::BM + C::BN) src = e.w_scale ? e.w_scale + min(n0 + q - C::BM, g.N - 1) : nullptr;
-      else src = e.bias ? e.bias + min(n0 + q - C::BM - C::BN, g.N - 1) : nullptr;
-      if (src) {  // a missing operand (null pointer) is uniform over the wave
+      else if (q < C::SC_N) src = e.bias ? e.bias + min(n0 + q - C::BM - C::BN, g.N - 1) : nullptr;
+      else src = nullptr;
+      if (src) {  // lane l of copy i lands at sc[64 i + l]; lanes without a source write the default
         __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), (lds_void*)(sc + i * 64), 4, 0, 0);
       } else {
         sc[q] = (q >= C::BM + C::BN) ? 0.0f : 1.0f;
@@ -717,6 +720,7 @@ struct Tiles {
   using T128 = Cfg<128, 128, 4, MODE>;
   using T128x64 = Cfg<128, 64, 4, MODE>;
   using T64 = Cfg<64, 64, 4, MODE>;
+  using T32x64 = Cfg<32, 64, 4, MODE, 2, 1>;  // two waves of 32 x 32
   // producer waves of the int8 large tiles (12 waves, 3 per SIMD); the
   // 256 x 256 tile takes them only without a residual epilogue (with one its
   // MFMA waves would not fit 3 per SIMD without spilling)
@@ -770,6 +774,14 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
   } else if (tiles(g.M, g.N, 128, 64) >= FILL) {
     launch_epi<typename T::T128x64>(g, st);
   } else {
+    // int8 launches of fewer 64 x 64 tiles than CUs (the 512-row step's
+    // hidden-width projections) take 32 x 64 tiles: twice the workgroups
+    if constexpr (MODE == M_I8) {
+      if (tiles(g.M, g.N, 64, 64) < device_cus()) {
+        launch_epi<typename T::T32x64>(g, st);
+        return;
+      }
+    }
     launch_epi<typename T::T64>(g, st);
   }
 }
@@ -782,6 +794,7 @@ void prep_mode() {
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
   prep_cfg<typename T::T64>();
+  if constexpr (MODE == M_I8) prep_cfg<typename T::T32x64>();
 }
 
 }  // namespace
