@@ -51,17 +51,22 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
-// maximum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's keys):
-// v_permlane16_swap / v_permlane32_swap with both operands v leave v of the
-// partner lane (xor 16, resp. xor 32) in one of the two results, the lane's
-// own value in the other
+// maximum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's keys).
+// v_permlane16_swap / v_permlane32_swap on two copies of v leave v of the
+// partner lane (xor 16, resp. xor 32) in one register and the lane's own
+// value in the other.  The swaps are inline assembly: through the compiler
+// builtin the float maximum of the two results was compiled as the maximum
+// of the first with itself (the generated code compared only one lane in
+// four, so the row maximum covered a quarter of the row's keys).  The nop
+// covers the VALU-write-to-permlane-read hazard.
 __device__ __forceinline__ float max_over_query_lanes(float v) {
-  const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                  false, false);
-  v = fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
-                                                  false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  v = fmaxf(a, b);
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
 }
 
 // s_waitcnt vmcnt(N)
@@ -143,10 +148,12 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
   // that block is the sum of the fp16 weights over the keys, for the lane's
   // query), so the sum needs no VALU adds and no cross-lane reduction
   v4f oacc[QW][5];
-  float m_run[QW];
+  // cm_run[qb]: -c times the exponent reference of the lane's query (set by
+  // the first tile), so a weight is 2^(c s + cm_run)
+  float cm_run[QW];
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
-    m_run[qb] = -INFINITY;
+    cm_run[qb] = 0.0f;
 #pragma unroll
     for (int d = 0; d < 5; ++d) oacc[qb][d] = v4f{0, 0, 0, 0};
   }
@@ -276,33 +283,55 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int qb = 0; qb < QW; ++qb) {
-      float mx = sc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
-      mx = max_over_query_lanes(mx);
-      // The exponent reference m_run moves only when a row's maximum exceeds
-      // it by more than 8 / c (a factor 2^8): p then stays below 256, exact
+      // Online softmax in base 2 with a lazy reference: the weights are
+      // p = 2^(c s + cm_run), and the reference moves only when a row's
+      // exponent c s + cm_run would exceed 8 (p then stays below 256, exact
       // enough in fp16, and the output/sum rescale is rare after the first
-      // tile.
+      // tile).  The first tile sets the reference to the row maximum.  Later
+      // tiles form the exponents against the current reference, and only when
+      // one of the wave's exceeds 8 take each row's maximum exponent (over its
+      // 4 lanes) and shift the rows that moved, so a tile without a move needs
+      // only a lane-local maximum.
       const float c = a.scale_log2;
-      const float m_old = m_run[qb];
-      const bool move = mx > m_old + 8.0f / c;
-      const float m_new = move ? mx : m_old;
-      if (__any(move)) {
-        const float corr = __builtin_amdgcn_exp2f(c * (m_old - m_new));  // 1 where the row did not move
+      float ex[4][4];
+      if (t == 0) {
+        float mx = sc[qb][0][0];
 #pragma unroll
-        for (int db = 0; db < 5; ++db) oacc[qb][db] *= corr;
-        m_run[qb] = m_new;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[qb][kb][r]);
+        cm_run[qb] = -c * max_over_query_lanes(mx);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ex[kb][r] = fmaf(sc[qb][kb][r], c, cm_run[qb]);
+      } else {
+        float emax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ex[kb][r] = fmaf(sc[qb][kb][r], c, cm_run[qb]);
+            emax = fmaxf(emax, ex[kb][r]);
+          }
+        if (__any(emax > 8.0f)) {
+          const float me = max_over_query_lanes(emax);
+          const float shift = me > 8.0f ? me : 0.0f;  // 0 where the row does not move
+          const float corr = __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+          for (int db = 0; db < 5; ++db) oacc[qb][db] *= corr;
+          cm_run[qb] -= shift;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ex[kb][r] -= shift;
+        }
       }
-      const float cm = -c * m_new;
       v8h pf[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(fmaf(sc[qb][kb][r], c, cm));
+        for (int r = 0; r < 4; ++r) pf[kb >> 1][(kb & 1) * 4 + r] = (_Float16)__builtin_amdgcn_exp2f(ex[kb][r]);
 #pragma unroll
       for (int db = 0; db < 5; ++db) {
         const v8h* vv = db < 4 ? vf[db] : nullptr;

@@ -385,6 +385,47 @@ def test_attention_single_key_and_uniform():
               atol_frac=2.0 ** -9)
 
 
+# Scores spread over hundreds of units.  The weights are 2^(c (s - m)) in
+# fp16 against a row reference m, so a reference taken over only part of a
+# query's keys (one of the 4 lanes that hold them) overflows the weights to
+# inf and the row to NaN once the spread passes ~90; the unit-normal inputs
+# above never reach that.  Grid shapes as in test_attention_dense, with
+# ragged key counts.
+@pytest.mark.parametrize("B_,Sq,Sk,nh,mult", [(2, 64, 32, 4, 3.0), (4, 200, 150, 16, 2.0), (16, 500, 140, 16, 2.0),
+                                               (2, 256, 512, 8, 3.0), (16, 512, 128, 4, 4.0)])
+def test_attention_wide_score_range(B_, Sq, Sk, nh, mult):
+    r = rng(B_ * 7 + Sq + Sk)
+    W = nh * 64
+    q = (r.standard_normal((B_ * Sq, W)) * mult).astype(np.float16)
+    k = (r.standard_normal((B_ * Sk, W)) * mult).astype(np.float16)
+    v = r.standard_normal((B_ * Sk, W)).astype(np.float16)
+    out = B.attn_fwd(dev(q), dev(k), dev(v), nh, B_, Sq, Sk)
+    ref = _attn_ref(q, k, v, nh, np.arange(B_ + 1) * Sq, np.arange(B_ + 1) * Sk)
+    f16_close(host(out), ref, rtol=2.0 ** -8, atol_frac=2.0 ** -8)
+
+
+# Keys along one direction with scores rising (or falling) along the key
+# order by 60 units per 64-key tile: rising, every tile's maximum passes the
+# exponent reference and moves it (the rescale of the output and the row
+# sums runs at every tile); falling, the first tile holds each row's maximum.
+@pytest.mark.parametrize("order", ["rising", "falling"])
+@pytest.mark.parametrize("Sk", [512, 333])
+def test_attention_moving_reference(order, Sk):
+    r = rng(11 if order == "rising" else 12)
+    nh, Sq = 2, 96
+    W = nh * 64
+    u = np.full(64, 0.5)                                  # |u|^2 = 16
+    steps = np.arange(Sk) / 64.0 * 3.75                   # 60 score units per tile
+    if order == "falling":
+        steps = steps[::-1]
+    q = (np.tile(u, (Sq, nh)) + 0.05 * r.standard_normal((Sq, W))).astype(np.float16)
+    k = (np.tile(steps[:, None] * u[None, :], (1, nh)) + 0.05 * r.standard_normal((Sk, W))).astype(np.float16)
+    v = r.standard_normal((Sk, W)).astype(np.float16)
+    out = B.attn_fwd(dev(q), dev(k), dev(v), nh, 1, Sq, Sk)
+    ref = _attn_ref(q, k, v, nh, np.array([0, Sq]), np.array([0, Sk]))
+    f16_close(host(out), ref, rtol=2.0 ** -8, atol_frac=2.0 ** -8)
+
+
 # ------------------------------------------------------------- steering, CFG, sampler
 
 def test_steer_add():
