@@ -77,6 +77,40 @@ def test_ln_quant(M, H):
     assert np.array_equal(host(y), ug)
 
 
+def _extreme_rows(H, r):
+    """fp16 rows at the edges of the format and of the statistics: a large
+    common offset (variance far below the mean squared), a constant row
+    (zero variance), values near the fp16 maximum, subnormals only, one
+    spike in a row of zeros (at the first, a middle and the last column),
+    alternating signs, negative zeros."""
+    rows = [1000.0 + r.standard_normal(H), np.full(H, 3.0), 60000.0 * np.sign(r.standard_normal(H)),
+            6e-8 * r.integers(-900, 900, H), np.eye(1, H, 0)[0] * 7.0, np.eye(1, H, H // 2 + 3)[0] * -300.0,
+            np.eye(1, H, H - 1)[0] * 0.001, np.where(np.arange(H) % 2 == 0, 1.0, -1.0) * 512.0, np.full(H, -0.0),
+            r.standard_normal(H) * 1e-3 + 65000.0 * (np.arange(H) == 5)]
+    return np.stack(rows).astype(np.float16)
+
+
+# Rows at the edges of fp16 and of the statistics, through LayerNorm +
+# quantization (codes bit-exact against the quantization of the GPU's own
+# fp16 row, LayerNorm within the bar above) and through the activation
+# quantizer alone (bit-exact)
+@pytest.mark.parametrize("H", [256, 1536, 6144])
+def test_row_kernels_extreme_values(H):
+    r = rng(H + 3)
+    x = _extreme_rows(H, r)
+    g = (1 + 0.02 * r.standard_normal(H)).astype(np.float32)
+    b = (0.02 * r.standard_normal(H)).astype(np.float32)
+    u = torch.empty(x.shape, dtype=torch.float16, device="cuda")
+    q, s = B.ln_quant(dev(x), dev(g), dev(b), 1e-5, u_out=u)
+    ug = host(u)
+    f16_close(ug, O.layer_norm(x, g, b, 1e-5), rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    qo, so = O.quantize_rows_q8(ug)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    q, s = B.quantize_rows_q8(dev(x))
+    qo, so = O.quantize_rows_q8(x)
+    assert np.array_equal(host(q), qo) and host(s).tobytes() == so.tobytes()
+
+
 # ------------------------------------------------------------- W8A8 GEMM
 
 W8A8_SHAPES = [(1, 16, 1), (3, 32, 7), (77, 272, 130), (128, 256, 768), (200, 1024, 257), (512, 1024, 3072),
@@ -99,6 +133,32 @@ def test_w8a8_linear(M, K, N):
     assert np.array_equal(host(xq), ro.xq)
     assert np.array_equal(host(xs), ro.x_scale)
     assert np.array_equal(host(acc).astype(np.int64), ro.acc)
+    f16_close(host(y), ro.y)
+
+
+# Saturated codes: rows of +-1 and weights of +-0.01 quantize to +-127 everywhere,
+# so at K = 6144 the int32 accumulators reach 127 * 127 * 6144 ~ 9.9e7 (all
+# signs equal in some rows and columns); shapes of both large tiles and of the
+# small ones
+@pytest.mark.parametrize("M,K,N", [(512, 6144, 384), (8192, 1536, 1536), (96, 6144, 130)])
+def test_w8a8_saturated_codes(M, K, N):
+    r = rng(M + K + N)
+    x = np.where(r.random((M, K)) < 0.5, -1.0, 1.0).astype(np.float16)
+    x[0] = 1.0
+    w = np.where(r.random((N, K)) < 0.5, -0.01, 0.01).astype(np.float16)
+    w[0] = 0.01
+    w[1] = -0.01
+    wq, ws = O.quantize_rows_q8(w)
+    assert np.abs(wq.astype(np.int64)).min() == 127
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    y = B.w8a8_linear(dev(x), dev(wq), dev(ws), xq=xq, x_scale=xs, acc=acc)
+    ro = O.w8a8_linear(x, wq, ws, None)
+    assert np.array_equal(host(xq), ro.xq) and np.array_equal(host(xs), ro.x_scale)
+    a = host(acc).astype(np.int64)
+    assert a[0, 0] == 127 * 127 * K and a[0, 1] == -127 * 127 * K
+    assert np.array_equal(a, ro.acc)
     f16_close(host(y), ro.y)
 
 
