@@ -25,16 +25,19 @@
 //
 // LDS swizzles (16-byte chunk c of row r stored at slot c ^ f(r)):
 //   K: f(r) = (r & 7) ^ ((r >> 3) & 1): the 16 rows of one fragment read,
-//      same chunk, fall on distinct banks per 8-lane phase;
-//   V: f(r) = 2 (r & 3): the four keys of one transpose read land in four
-//      different 32-byte bank groups.
+//      same chunk, fall on distinct banks per 8-lane phase and per 256-byte
+//      (64-bank) period;
+//   V: f(r) = 2 ((r & 3) ^ ((r >> 2) & 1)): the four keys of one transpose
+//      read land in four different 32-byte bank groups, and the 8 keys two
+//      adjacent 16-lane groups read (rows 4 g + tk, g = 0, 1) cover the 256
+//      bytes of a 64-bank period once.
 //
-// Softmax: scores stay in raw units (the scale c > 0 commutes with max);
-// p = 2^(c s - c m) is one FMA and one v_exp_f32 against a reference m that
-// moves only when a row maximum passes it by more than a factor 2^8 (so
-// p < 256, and the output rescale is rare).  The row maximum reduces over the
-// 4 lanes that share a query with two lane-swap instructions; the row sum of
-// the fp16 weights comes out of the MFMA against a block of ones.
+// Softmax in base 2: p = 2^(c s + r) with r = -c m per row, one FMA and one
+// v_exp_f32.  The first tile sets m to the row maximum (reduced over the 4
+// lanes that share a query with two lane-swap instructions); the reference
+// moves only when an exponent c s + r would pass 8 (so p < 256, and the output
+// rescale is rare), which later tiles detect with a lane-local maximum.  The
+// row sum of the fp16 weights comes out of the MFMA against a block of ones.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,7 +52,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+__device__ __forceinline__ int vswz(int r) { return 2 * ((r & 3) ^ ((r >> 2) & 1)); }
 
 // maximum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's keys).
 // v_permlane16_swap / v_permlane32_swap on two copies of v leave v of the
@@ -206,14 +209,16 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) koff[c] = ql * 128 + (((4 * c + g) ^ kswz(ql)) << 4);
   // V^T transpose reads: lane j = 4 tk + tq of group g points at key
-  // 32 c + 16 h2 + 4 g + tk, dims 16 db + 4 tq .. + 3.  With the V swizzle
-  // (chunk ^ 2 (row & 3), row & 3 = tk) the byte offset is
-  //   4096 c + 2048 h2 + (4 g + tk) 128 + 32 (db ^ tk) + 16 (tq >> 1) + 8 (tq & 1),
+  // 32 c + 16 h2 + 4 g + tk, dims 16 db + 4 tq .. + 3, i.e. chunk
+  // 2 db + (tq >> 1) of that row.  The V swizzle depends on the row's low
+  // three bits only (4 g + tk), so the byte offset is
+  //   4096 c + 2048 h2 + (4 g + tk) 128 + 16 ((2 db + (tq >> 1)) ^ vswz(4 g + tk)) + 8 (tq & 1),
   // a per-lane part for each db plus an immediate for (c, h2).
   const int tk = ql >> 2, tq = ql & 3;
   int vlane[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) vlane[db] = (4 * g + tk) * 128 + 32 * (db ^ tk) + 16 * (tq >> 1) + 8 * (tq & 1);
+  for (int db = 0; db < 4; ++db)
+    vlane[db] = (4 * g + tk) * 128 + 16 * ((2 * db + (tq >> 1)) ^ vswz(4 * g + tk)) + 8 * (tq & 1);
 
   for (int t = 0; t < n_tiles; ++t) {
     // this wave's copies of tile t have landed (2 CI per tile; tile t + 1's are newer)
