@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restri
   constexpr bool PREFETCH = NV <= 6;
   const int lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;
-  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
   load_row<NV>(r, x + (int64_t)m * ldx, K, lane);
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
   constexpr bool PREFETCH = NV <= 6;
   const int lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;
-  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
   load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
   constexpr bool PREFETCH = NV <= 6;
   const int lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;
-  int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
   load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
