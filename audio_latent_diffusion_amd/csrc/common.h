@@ -74,6 +74,7 @@ __device__ __forceinline__ v2i ld8_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const v2i*>(p));
 }
 __device__ __forceinline__ void st8_nt(void* p, v2i v) { __builtin_nontemporal_store(v, reinterpret_cast<v2i*>(p)); }
+__device__ __forceinline__ void st8(void* p, v2i v) { *reinterpret_cast<v2i*>(p) = v; }
 
 // symmetric int8 code of an fp32 value given the fp32 reciprocal 127/amax:
 // one rounded product, then round-half-even, then clamp

@@ -117,7 +117,10 @@ __device__ __forceinline__ void quant_row_regs(const RowRegs<NV>& r, int K, int 
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (lane + WAVE * j) * 8;
-    if (FULL || e < K) st8_nt(qrow + e, quant8_h(r.c[j], inv));
+    // ordinary stores: the next GEMM reads the codes at once, and a
+    // nontemporal store made its first loads miss (serving step 88.2 -> 90.4
+    // steps/s with ordinary ones)
+    if (FULL || e < K) st8(qrow + e, quant8_h(r.c[j], inv));
   }
   if (lane == 0) *scale_m = s;
 }
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
     for (int j = 0; j < NV; ++j) {
       const int e = (lane + WAVE * j) * 8;
       if (FULL || e < H) {
-        st8_nt(qrow + e, quant8_h(y.c[j], inv));
+        st8(qrow + e, quant8_h(y.c[j], inv));  // ordinary store: read next by the GEMM
         if (urow) st16_nt(urow + e, y.c[j]);
       }
     }
