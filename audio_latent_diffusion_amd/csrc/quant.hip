@@ -19,12 +19,17 @@ struct RowRegs {
   v4i c[NV];  // chunk j of this lane covers elements (lane + 64 j) * 8 .. +8
 };
 
-template <int NV>
+// NT: non-temporal loads. LayerNorm loads the residual stream with ordinary
+// loads (NT = false): the residual epilogue of the next projection reads the
+// stream again, and on the 24-block serving step (8192 rows of 1536) ordinary
+// loads there make the step 1.1 % faster (MI355X, same-box A/B). The other row
+// kernels read activations nothing reads again.
+template <int NV, bool NT = true>
 __device__ __forceinline__ void load_row(RowRegs<NV>& r, const uint16_t* row, int K, int lane) {
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     int e = (lane + WAVE * j) * 8;
-    if (e < K) r.c[j] = ld16_nt(row + e);
+    if (e < K) r.c[j] = NT ? ld16_nt(row + e) : ld16(row + e);
     else r.c[j] = v4i{0, 0, 0, 0};
   }
 }
@@ -217,11 +222,11 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
   int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
-  load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
+  load_row<NV, false>(r, x + (int64_t)m * ldx, H, lane);
   for (;;) {
     const int mn = m + stride;
     RowRegs<NV> nx;
-    if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
+    if (PREFETCH && mn < M) load_row<NV, false>(nx, x + (int64_t)mn * ldx, H, lane);
     RowRegs<NV>& y = r;  // the normalized row replaces the input row
     layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, y);
     // the quantizer reads the fp16 LayerNorm output
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
     if (lane == 0) scale[m] = s;
     if (mn >= M) break;
     if (PREFETCH) r = nx;
-    else load_row<NV>(r, x + (int64_t)mn * ldx, H, lane);
+    else load_row<NV, false>(r, x + (int64_t)mn * ldx, H, lane);
     m = mn;
   }
 }
@@ -261,11 +266,11 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
   int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
-  load_row<NV>(r, x + (int64_t)m * ldx, H, lane);
+  load_row<NV, false>(r, x + (int64_t)m * ldx, H, lane);
   for (;;) {
     const int mn = m + stride;
     RowRegs<NV> nx;
-    if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, H, lane);
+    if (PREFETCH && mn < M) load_row<NV, false>(nx, x + (int64_t)mn * ldx, H, lane);
     RowRegs<NV>& o = r;  // the normalized row replaces the input row
     layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, o);
     uint16_t* yrow = y + (int64_t)m * ldy;
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
     }
     if (mn >= M) break;
     if (PREFETCH) r = nx;
-    else load_row<NV>(r, x + (int64_t)mn * ldx, H, lane);
+    else load_row<NV, false>(r, x + (int64_t)mn * ldx, H, lane);
     m = mn;
   }
 }
