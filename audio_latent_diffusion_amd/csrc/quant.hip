@@ -19,11 +19,22 @@ struct RowRegs {
   v4i c[NV];  // chunk j of this lane covers elements (lane + 64 j) * 8 .. +8
 };
 
-// NT: non-temporal loads. LayerNorm loads the residual stream with ordinary
-// loads (NT = false): the residual epilogue of the next projection reads the
-// stream again, and on the 24-block serving step (8192 rows of 1536) ordinary
-// loads there make the step 1.1 % faster (MI355X, same-box A/B). The other row
-// kernels read activations nothing reads again.
+// Cache hints of the row kernels (CACHED: ordinary accesses where the next
+// kernel reads the data again).  In the step, the int8 codes a quantizer
+// writes are read at once by the next GEMM, and the residual stream that
+// LayerNorm reads is read again by the next projection's residual epilogue.
+// While a launch's data (2 B read and 1 B written per element) fits the
+// 256 MB last-level cache, ordinary accesses leave it there for that reader:
+// the serving step (8192 rows) ran 2.4 % faster with ordinary code stores and
+// 1.1 % faster with ordinary LayerNorm loads (MI355X, same-box A/B).  Beyond
+// the cache they only cost bandwidth (262144 x 1536 LayerNorm + quantize
+// 75 -> 71 % of HBM, 65536 x 6144 quantize 79 -> 69 %), so larger launches
+// keep the non-temporal hints.  Activations read once keep non-temporal
+// loads.  The choice is a template parameter: as a run-time condition the
+// compiler merged the two accesses and dropped the non-temporal hint.
+inline bool fits_llc(int64_t M, int64_t K) { return 3 * M * K <= (int64_t(256) << 20); }
+
+// NT: non-temporal loads
 template <int NV, bool NT = true>
 __device__ __forceinline__ void load_row(RowRegs<NV>& r, const uint16_t* row, int K, int lane) {
 #pragma unroll
@@ -111,7 +122,7 @@ __device__ __forceinline__ void q8_scale(float amax, float& s, float& inv) {
 
 // codes and scale of one row held in registers (no conversion of the row to
 // fp32: the amax from the fp16 bits, the products from fp16 operands)
-template <int NV, bool FULL>
+template <int NV, bool FULL, bool CACHED>
 __device__ __forceinline__ void quant_row_regs(const RowRegs<NV>& r, int K, int lane, int8_t* __restrict__ qrow,
                                                float* __restrict__ scale_m) {
   u16x2 acc = {0, 0};
@@ -122,17 +133,17 @@ __device__ __forceinline__ void quant_row_regs(const RowRegs<NV>& r, int K, int 
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = (lane + WAVE * j) * 8;
-    // ordinary stores: the next GEMM reads the codes at once, and a
-    // nontemporal store made its first loads miss (serving step 88.2 -> 90.4
-    // steps/s with ordinary ones)
-    if (FULL || e < K) st8(qrow + e, quant8_h(r.c[j], inv));
+    if (FULL || e < K) {
+      if constexpr (CACHED) st8(qrow + e, quant8_h(r.c[j], inv));  // read next by the GEMM
+      else st8_nt(qrow + e, quant8_h(r.c[j], inv));
+    }
   }
   if (lane == 0) *scale_m = s;
 }
 
 // rows of up to 6 x 512 values prefetch the next row; longer rows already
 // keep NV 16-byte loads per lane in flight and need the registers
-template <int NV, bool FULL>
+template <int NV, bool FULL, bool CACHED>
 __global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                         int K, int8_t* __restrict__ q, int64_t ldq,
                                                         float* __restrict__ scale) {
@@ -147,7 +158,7 @@ __global__ __launch_bounds__(256) void row_quant_kernel(const uint16_t* __restri
     const int mn = m + stride;
     RowRegs<NV> nx;
     if (PREFETCH && mn < M) load_row<NV>(nx, x + (int64_t)mn * ldx, K, lane);
-    quant_row_regs<NV, FULL>(r, K, lane, q + (int64_t)m * ldq, scale + m);
+    quant_row_regs<NV, FULL, CACHED>(r, K, lane, q + (int64_t)m * ldq, scale + m);
     if (mn >= M) break;
     if (PREFETCH) r = nx;
     else load_row<NV>(r, x + (int64_t)mn * ldx, K, lane);
@@ -211,7 +222,7 @@ __device__ __forceinline__ void layer_norm_row(const RowRegs<NV>& r, int H, int 
   }
 }
 
-template <int NV, bool FULL>
+template <int NV, bool FULL, bool CACHED>
 __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M, int H,
                                                        const float* __restrict__ g, const float* __restrict__ b,
                                                        float eps, uint16_t* __restrict__ u_out,
@@ -222,11 +233,11 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
   int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
-  load_row<NV, false>(r, x + (int64_t)m * ldx, H, lane);
+  load_row<NV, !CACHED>(r, x + (int64_t)m * ldx, H, lane);
   for (;;) {
     const int mn = m + stride;
     RowRegs<NV> nx;
-    if (PREFETCH && mn < M) load_row<NV, false>(nx, x + (int64_t)mn * ldx, H, lane);
+    if (PREFETCH && mn < M) load_row<NV, !CACHED>(nx, x + (int64_t)mn * ldx, H, lane);
     RowRegs<NV>& y = r;  // the normalized row replaces the input row
     layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, y);
     // the quantizer reads the fp16 LayerNorm output
@@ -244,19 +255,20 @@ __global__ __launch_bounds__(256) void ln_quant_kernel(const uint16_t* __restric
     for (int j = 0; j < NV; ++j) {
       const int e = (lane + WAVE * j) * 8;
       if (FULL || e < H) {
-        st8(qrow + e, quant8_h(y.c[j], inv));  // ordinary store: read next by the GEMM
+        if constexpr (CACHED) st8(qrow + e, quant8_h(y.c[j], inv));  // read next by the GEMM
+        else st8_nt(qrow + e, quant8_h(y.c[j], inv));
         if (urow) st16_nt(urow + e, y.c[j]);
       }
     }
     if (lane == 0) scale[m] = s;
     if (mn >= M) break;
     if (PREFETCH) r = nx;
-    else load_row<NV, false>(r, x + (int64_t)mn * ldx, H, lane);
+    else load_row<NV, !CACHED>(r, x + (int64_t)mn * ldx, H, lane);
     m = mn;
   }
 }
 
-template <int NV, bool FULL>
+template <int NV, bool FULL, bool CACHED>
 __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M, int H,
                                                      const float* __restrict__ g, const float* __restrict__ b,
                                                      float eps, uint16_t* __restrict__ y, int64_t ldy) {
@@ -266,11 +278,11 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
   int m = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   if (m >= M) return;
   RowRegs<NV> r;
-  load_row<NV, false>(r, x + (int64_t)m * ldx, H, lane);
+  load_row<NV, !CACHED>(r, x + (int64_t)m * ldx, H, lane);
   for (;;) {
     const int mn = m + stride;
     RowRegs<NV> nx;
-    if (PREFETCH && mn < M) load_row<NV, false>(nx, x + (int64_t)mn * ldx, H, lane);
+    if (PREFETCH && mn < M) load_row<NV, !CACHED>(nx, x + (int64_t)mn * ldx, H, lane);
     RowRegs<NV>& o = r;  // the normalized row replaces the input row
     layer_norm_row<NV, FULL>(r, H, lane, g, b, eps, o);
     uint16_t* yrow = y + (int64_t)m * ldy;
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(256) void ln_f16_kernel(const uint16_t* __restrict_
     }
     if (mn >= M) break;
     if (PREFETCH) r = nx;
-    else load_row<NV, false>(r, x + (int64_t)mn * ldx, H, lane);
+    else load_row<NV, !CACHED>(r, x + (int64_t)mn * ldx, H, lane);
     m = mn;
   }
 }
@@ -342,43 +354,48 @@ inline unsigned row_grid(int64_t M, bool two_rows) {
   return (unsigned)std::min(std::max<int64_t>((M + 7) / 8, 1024), ROW_GRID_CAP);
 }
 
-#define ALD_ROW_LAUNCH(KERNEL, NV, K, GRID, ST, ...)                                                 \
+#define ALD_ROW_LAUNCH(KERNEL, C, NV, K, GRID, ST, ...)                                              \
   do {                                                                                               \
-    if ((K) == (NV) * 512) hipLaunchKernelGGL((KERNEL<NV, true>), GRID, dim3(256), 0, ST, __VA_ARGS__); \
-    else hipLaunchKernelGGL((KERNEL<NV, false>), GRID, dim3(256), 0, ST, __VA_ARGS__);               \
+    if ((K) == (NV) * 512) hipLaunchKernelGGL((KERNEL<NV, true, C>), GRID, dim3(256), 0, ST, __VA_ARGS__); \
+    else hipLaunchKernelGGL((KERNEL<NV, false, C>), GRID, dim3(256), 0, ST, __VA_ARGS__);            \
   } while (0)
 
 // one wave per row: NV 16-byte chunks per lane cover K values (NV * 512 >= K)
-#define ALD_ROW_DISPATCH(KERNEL, K, M, TWO, ST, ...)                                                 \
+#define ALD_ROW_DISPATCH(KERNEL, C, K, M, TWO, ST, ...)                                              \
   do {                                                                                               \
     dim3 grid_(row_grid((M), (TWO)));                                                                \
     const int nv_ = ((K) + 511) / 512;                                                               \
-    if (nv_ <= 1) ALD_ROW_LAUNCH(KERNEL, 1, K, grid_, ST, __VA_ARGS__);                              \
-    else if (nv_ <= 2) ALD_ROW_LAUNCH(KERNEL, 2, K, grid_, ST, __VA_ARGS__);                         \
-    else if (nv_ <= 3) ALD_ROW_LAUNCH(KERNEL, 3, K, grid_, ST, __VA_ARGS__);                         \
-    else if (nv_ <= 4) ALD_ROW_LAUNCH(KERNEL, 4, K, grid_, ST, __VA_ARGS__);                         \
-    else if (nv_ <= 6) ALD_ROW_LAUNCH(KERNEL, 6, K, grid_, ST, __VA_ARGS__);                         \
-    else if (nv_ <= 8) ALD_ROW_LAUNCH(KERNEL, 8, K, grid_, ST, __VA_ARGS__);                         \
-    else if (nv_ <= 12) ALD_ROW_LAUNCH(KERNEL, 12, K, grid_, ST, __VA_ARGS__);                       \
-    else ALD_ROW_LAUNCH(KERNEL, 16, K, grid_, ST, __VA_ARGS__);                                      \
+    if (nv_ <= 1) ALD_ROW_LAUNCH(KERNEL, C, 1, K, grid_, ST, __VA_ARGS__);                           \
+    else if (nv_ <= 2) ALD_ROW_LAUNCH(KERNEL, C, 2, K, grid_, ST, __VA_ARGS__);                      \
+    else if (nv_ <= 3) ALD_ROW_LAUNCH(KERNEL, C, 3, K, grid_, ST, __VA_ARGS__);                      \
+    else if (nv_ <= 4) ALD_ROW_LAUNCH(KERNEL, C, 4, K, grid_, ST, __VA_ARGS__);                      \
+    else if (nv_ <= 6) ALD_ROW_LAUNCH(KERNEL, C, 6, K, grid_, ST, __VA_ARGS__);                      \
+    else if (nv_ <= 8) ALD_ROW_LAUNCH(KERNEL, C, 8, K, grid_, ST, __VA_ARGS__);                      \
+    else if (nv_ <= 12) ALD_ROW_LAUNCH(KERNEL, C, 12, K, grid_, ST, __VA_ARGS__);                    \
+    else ALD_ROW_LAUNCH(KERNEL, C, 16, K, grid_, ST, __VA_ARGS__);                                   \
   } while (0)
 
 void launch_row_quant(const uint16_t* x, int64_t ldx, int M, int K, int8_t* q, int64_t ldq, float* scale,
                       hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(row_quant_kernel, K, M, false, st, x, ldx, M, K, q, ldq, scale);
+  if (fits_llc(M, K)) ALD_ROW_DISPATCH(row_quant_kernel, true, K, M, false, st, x, ldx, M, K, q, ldq, scale);
+  else ALD_ROW_DISPATCH(row_quant_kernel, false, K, M, false, st, x, ldx, M, K, q, ldq, scale);
 }
 
 void launch_ln_quant(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
                      uint16_t* u_out, int8_t* q, float* scale, hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(ln_quant_kernel, H, M, true, st, x, ldx, M, H, g, b, eps, u_out, q, scale);
+  if (fits_llc(M, H))
+    ALD_ROW_DISPATCH(ln_quant_kernel, true, H, M, true, st, x, ldx, M, H, g, b, eps, u_out, q, scale);
+  else
+    ALD_ROW_DISPATCH(ln_quant_kernel, false, H, M, true, st, x, ldx, M, H, g, b, eps, u_out, q, scale);
 }
 
 void launch_ln_f16(const uint16_t* x, int64_t ldx, int M, int H, const float* g, const float* b, float eps,
                    uint16_t* y, int64_t ldy, hipStream_t st) {
   if (M <= 0) return;
-  ALD_ROW_DISPATCH(ln_f16_kernel, H, M, false, st, x, ldx, M, H, g, b, eps, y, ldy);
+  if (fits_llc(M, H)) ALD_ROW_DISPATCH(ln_f16_kernel, true, H, M, false, st, x, ldx, M, H, g, b, eps, y, ldy);
+  else ALD_ROW_DISPATCH(ln_f16_kernel, false, H, M, false, st, x, ldx, M, H, g, b, eps, y, ldy);
 }
 
 void launch_q4_pack(const uint16_t* w, int N, int K, uint8_t* packed, uint16_t* scales, hipStream_t st) {

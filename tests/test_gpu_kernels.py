@@ -111,6 +111,37 @@ def test_row_kernels_extreme_values(H):
     assert np.array_equal(host(q), qo) and host(s).tobytes() == so.tobytes()
 
 
+# Launches whose data (2 B read and 1 B written per element) exceed the 256 MB
+# last-level cache take the non-temporal variants of the row kernels; the
+# step's launches take the cached ones.  65536 rows of 1536 (302 MB):
+# sampled rows against the oracle, every row of the two variants computed the
+# same way, so the codes are bit-exact here as at the step's sizes.
+def test_row_kernels_beyond_last_level_cache():
+    M, H = 65536, 1536
+    g = torch.Generator(device="cuda").manual_seed(11)
+    xt = (torch.randn((M, H), generator=g, device="cuda") * 2 + 0.5).half()
+    r = rng(12)
+    gam = (1 + 0.02 * r.standard_normal(H)).astype(np.float32)
+    bet = (0.02 * r.standard_normal(H)).astype(np.float32)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 2, M - 1], r.integers(0, M, 59)]))
+    idx = torch.from_numpy(rows).cuda()
+    xs = host(xt.index_select(0, idx))
+    q, s = B.quantize_rows_q8(xt)
+    qo, so = O.quantize_rows_q8(xs)
+    assert np.array_equal(host(q.index_select(0, idx)), qo)
+    assert host(s.index_select(0, idx)).tobytes() == so.tobytes()
+    del q, s
+    u = torch.empty((M, H), dtype=torch.float16, device="cuda")
+    q, s = B.ln_quant(xt, dev(gam), dev(bet), 1e-5, u_out=u)
+    ug = host(u.index_select(0, idx))
+    f16_close(ug, O.layer_norm(xs, gam, bet, 1e-5), rtol=2.0 ** -10, atol_frac=2.0 ** -11)
+    qo, so = O.quantize_rows_q8(ug)
+    assert np.array_equal(host(q.index_select(0, idx)), qo) and np.array_equal(host(s.index_select(0, idx)), so)
+    del q, s
+    y = B.ln_f16(xt, dev(gam), dev(bet), 1e-5)
+    assert np.array_equal(host(y.index_select(0, idx)), ug)
+
+
 # ------------------------------------------------------------- W8A8 GEMM
 
 W8A8_SHAPES = [(1, 16, 1), (3, 32, 7), (77, 272, 130), (128, 256, 768), (200, 1024, 257), (512, 1024, 3072),
