@@ -21,12 +21,7 @@ inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) 
 inline bool al8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 std::once_flag g_prep;
-void prepare() {
-  std::call_once(g_prep, [] {
-    gemm_prepare();
-    attn_prepare();
-  });
-}
+void prepare() { std::call_once(g_prep, [] { gemm_prepare(); }); }
 
 inline int launched() {
   hipError_t e = hipGetLastError();
@@ -646,7 +641,6 @@ int attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t q_
   else CHECK(Sk >= 0, ALD_E_INVALID);
   const int msq = cu_seqlens_q ? max_sq : Sq;
   if (msq == 0) return ALD_OK;
-  prepare();
   AttnArgs a{q, k, v, out, q_stride, kv_stride, o_stride, n_heads, Sq, Sk, cu_seqlens_q, cu_seqlens_k,
              scale * 1.4426950408889634f};
   launch_attn(a, batch, msq, stream);

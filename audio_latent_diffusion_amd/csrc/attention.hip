@@ -38,11 +38,6 @@
 // moves only when an exponent c s + r would pass 8 (so p < 256, and the output
 // rescale is rare), which later tiles detect with a lane-local maximum.  The
 // row sum of the fp16 weights comes out of the MFMA against a block of ones.
-//
-// Small grids (fewer than 256 workgroups of 64 queries) run workgroups of 32
-// queries whose two wave pairs split the key tiles between them and merge
-// at the end (KSPLIT): each wave walks half the tiles, which is what sets the
-// time of those short launches.
 #include "common.h"
 #include "kernels.h"
 
@@ -87,13 +82,7 @@ __device__ __forceinline__ void attn_vm_wait() {
 // EARLYQ: the tile copies are issued while this wave's Q loads are still in
 // flight (vector memory loads complete in issue order, so the wait for tile
 // 0 also covers Q); it pays off when there are only one or two key tiles
-// KSPLIT: the waves form two key groups of NW / 2 waves over the same
-// queries; group g takes key tiles g, g + 2, g + 4, ... (a step is one tile
-// per group, the LDS ring holds two steps), and at the end group 1 hands its
-// accumulators and exponent reference to group 0 through LDS, which merges,
-// normalises and stores.  Half the tiles per wave: for the short launches of
-// small grids, where one wave's chain through the tiles sets the time.
-template <int QW, int NW, bool EARLYQ, bool KSPLIT = false>
+template <int QW, int NW, bool EARLYQ>
 __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
   constexpr int RPW = KT / NW;  // tile rows each wave copies
   constexpr int CI = RPW / 8;   // copy instructions per wave and operand
@@ -123,18 +112,14 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
   const int q_len = a.cu_q ? a.cu_q[b + 1] - q_begin : a.Sq;
   const int k_begin = a.cu_k ? a.cu_k[b] : b * a.Sk;
   const int k_len = a.cu_k ? a.cu_k[b + 1] - k_begin : a.Sk;
-  constexpr int G = KSPLIT ? 2 : 1;  // key groups
-  const int group = KSPLIT ? wave / (NW / 2) : 0;
-  const int qwave = KSPLIT ? wave % (NW / 2) : wave;
-  const int QT = 16 * QW * NW / G;
+  const int QT = 16 * QW * NW;
   const int tq0 = qb * QT;
   if (tq0 >= q_len) return;  // whole workgroup exits together
 
   const int ql = lane & 15, g = lane >> 4;
-  const int wq0 = tq0 + qwave * 16 * QW;
+  const int wq0 = tq0 + wave * 16 * QW;
 
   if (k_len <= 0) {  // no keys: zeros
-    if (group != 0) return;
 #pragma unroll
     for (int qb = 0; qb < QW; ++qb) {
       int qi = wq0 + qb * 16 + ql;
@@ -217,7 +202,7 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
 
   if constexpr (!EARLYQ) attn_vm_wait<0>();  // Q fragments in registers before any tile copy is in flight
   issue_tile(0, 0);
-  if (n_tiles > 1) issue_tile(1, 1);  // KSPLIT: the second tile of step 0
+  if (n_tiles > 1) issue_tile(1, 1);
 
   // K fragment of lane (ql, g): row kb * 16 + ql, chunk 4 c + g (dims 32 c + 8 g)
   int koff[2];
@@ -235,27 +220,13 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db)
     vlane[db] = (4 * g + tk) * 128 + 16 * ((2 * db + (tq >> 1)) ^ vswz(4 * g + tk)) + 8 * (tq & 1);
 
-  const int n_steps = (n_tiles + G - 1) / G;
-  for (int st = 0; st < n_steps; ++st) {
-    const int t = st * G + group;  // this wave's tile
-    if constexpr (KSPLIT) {
-      // step st's copies (issued one step ahead) have landed; every wave is
-      // done with step st - 1, whose two slots take step st + 1
-      attn_vm_wait<0>();
-      __builtin_amdgcn_s_barrier();
-      const int tn = (st + 1) * 2;
-      if (tn < n_tiles) issue_tile(tn, ((st + 1) & 1) * 2);
-      if (tn + 1 < n_tiles) issue_tile(tn + 1, ((st + 1) & 1) * 2 + 1);
-      if (t >= n_tiles) continue;  // group 1 on the odd last tile
-    } else {
-      // this wave's copies of tile t have landed (2 CI per tile; tile t + 1's are newer)
-      if (t + 1 < n_tiles) attn_vm_wait<2 * CI>();
-      else attn_vm_wait<0>();
-      __builtin_amdgcn_s_barrier();  // every wave's copies visible; tile t - 1 fully consumed
-      if (t + 2 < n_tiles) issue_tile(t + 2, (t + 2) % ASTAGES);
-    }
-    const int slot_t = KSPLIT ? (st & 1) * 2 + group : t % ASTAGES;
-    const uint8_t* sK = smem + slot_t * 2 * TILE_BYTES;
+  for (int t = 0; t < n_tiles; ++t) {
+    // this wave's copies of tile t have landed (2 CI per tile; tile t + 1's are newer)
+    if (t + 1 < n_tiles) attn_vm_wait<2 * CI>();
+    else attn_vm_wait<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's copies visible; tile t - 1 fully consumed
+    if (t + 2 < n_tiles) issue_tile(t + 2, (t + 2) % ASTAGES);
+    const uint8_t* sK = smem + (t % ASTAGES) * 2 * TILE_BYTES;
     const uint8_t* sV = sK + TILE_BYTES;
     const int kbase = t * KT;
 
@@ -328,7 +299,7 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
       // only a lane-local maximum.
       const float c = a.scale_log2;
       float ex[4][4];
-      if (st == 0) {  // this wave's first tile
+      if (t == 0) {
         float mx = sc[qb][0][0];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -377,41 +348,6 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
     }
   }
 
-  if constexpr (KSPLIT) {
-    // group 1 hands its accumulators and references to group 0 through LDS
-    // (the ring is free once every wave is past its last tile); value k of
-    // lane l of query wave w at float (w * QW * 21 + k) * 64 + l
-    __syncthreads();
-    float* xch = reinterpret_cast<float*>(smem);
-    if (group == 1) {
-#pragma unroll
-      for (int qb = 0; qb < QW; ++qb) {
-        float* xq = xch + (qwave * QW + qb) * 21 * 64 + lane;
-#pragma unroll
-        for (int d = 0; d < 5; ++d)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) xq[(d * 4 + r) * 64] = oacc[qb][d][r];
-        xq[20 * 64] = cm_run[qb];
-      }
-    }
-    __syncthreads();
-    if (group == 1) return;
-    if (n_tiles > 1) {  // group 1 saw keys: rescale both to the larger reference and add
-#pragma unroll
-      for (int qb = 0; qb < QW; ++qb) {
-        const float* xq = xch + (qwave * QW + qb) * 21 * 64 + lane;
-        const float cm1 = xq[20 * 64];
-        const float cmx = fminf(cm_run[qb], cm1);
-        const float f0 = __builtin_amdgcn_exp2f(cmx - cm_run[qb]);
-        const float f1 = __builtin_amdgcn_exp2f(cmx - cm1);
-#pragma unroll
-        for (int d = 0; d < 5; ++d)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) oacc[qb][d][r] = oacc[qb][d][r] * f0 + xq[(d * 4 + r) * 64] * f1;
-      }
-    }
-  }
-
   // normalise and store: lane holds query ql, dims 16 db + 4 g + r
 #pragma unroll
   for (int qb = 0; qb < QW; ++qb) {
@@ -430,7 +366,6 @@ __global__ __launch_bounds__(64 * NW, 3) void attn_kernel(AttnArgs a) {
 }
 
 constexpr int ATTN_LDS = ASTAGES * 2 * TILE_BYTES;
-constexpr int ATTN_LDS_SPLIT = 4 * 2 * TILE_BYTES;  // two steps of two tiles
 
 template <bool EARLYQ>
 void launch_attn_q(const AttnArgs& a, int batch, int max_sq, hipStream_t st) {
@@ -447,16 +382,9 @@ void launch_attn_q(const AttnArgs& a, int batch, int max_sq, hipStream_t st) {
     dim3 grid((unsigned)((max_sq + 63) / 64), (unsigned)a.n_heads, (unsigned)batch);
     hipLaunchKernelGGL((attn_kernel<1, 4, EARLYQ>), grid, dim3(256), ATTN_LDS, st, a);
   } else {
-    // 32 queries per workgroup: two key groups of two waves each
     dim3 grid((unsigned)((max_sq + 31) / 32), (unsigned)a.n_heads, (unsigned)batch);
-    hipLaunchKernelGGL((attn_kernel<1, 4, EARLYQ, true>), grid, dim3(256), ATTN_LDS_SPLIT, st, a);
+    hipLaunchKernelGGL((attn_kernel<1, 2, EARLYQ>), grid, dim3(128), ATTN_LDS, st, a);
   }
-}
-
-void attn_prepare() {
-  const void* k[2] = {reinterpret_cast<const void*>(&attn_kernel<1, 4, true, true>),
-                      reinterpret_cast<const void*>(&attn_kernel<1, 4, false, true>)};
-  for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, ATTN_LDS_SPLIT);
 }
 
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st) {

@@ -70,7 +70,6 @@ void launch_gemm_dma(int akind, int bkind, const GemmArgs& g, hipStream_t st);
 void gemm_dma_prepare();
 
 void launch_attn(const AttnArgs& a, int batch, int max_sq, hipStream_t st);
-void attn_prepare();  // once per process, before the first launch_attn
 
 // project = 0: h += (alpha resid_norm) dir; project = 1: h += (alpha (h . dir)) dir
 // out of place: rows m < M_steer steered into dst, the other rows copied

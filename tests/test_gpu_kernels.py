@@ -412,14 +412,12 @@ def _attn_ref(q, k, v, nh, cu_q, cu_k):
     return O.attention_varlen(q, k, v, cu_q, cu_k, nh, 0.125)
 
 
-# the launch takes 4-wave workgroups of 32 queries whose two wave pairs split
-# the key tiles on small grids (one tile: the second pair idle; an odd count:
-# idle on the last step), 4-wave ones of 64 queries from 256 such workgroups
-# ((4, 200, 150, 16)) and 4-wave ones of 128 queries from 512 ((16, 400, 140,
-# 8)); grids of 1024 or more workgroups run remapped to one range of
-# (sequence, head) per XCD ((16, 500, ., 16)), and dense key sets of at most
-# 128 keys issue the Q loads together with the first tile copies; ragged
-# queries and keys
+# the launch takes 2-wave workgroups of 32 queries on small grids, 4-wave
+# ones of 64 queries from 256 such workgroups ((4, 200, 150, 16)) and 4-wave
+# ones of 128 queries from 512 ((16, 400, 140, 8)); grids of 1024 or more
+# workgroups run remapped to one range of (sequence, head) per XCD ((16, 500,
+# ., 16)), and dense key sets of at most 128 keys issue the Q loads together
+# with the first tile copies; ragged queries and keys
 @pytest.mark.parametrize("B_,Sq,Sk,nh", [(1, 1, 1, 1), (2, 64, 32, 4), (2, 100, 77, 3), (1, 256, 256, 2),
                                           (3, 130, 200, 2), (2, 96, 150, 2), (1, 40, 300, 3), (16, 512, 128, 1),
                                           (4, 200, 150, 16), (16, 400, 140, 8), (16, 500, 140, 16),
