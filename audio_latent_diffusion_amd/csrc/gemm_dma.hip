@@ -429,16 +429,37 @@ struct Frags {
   }
 };
 
+// LDS of config C with KS stage rings: the rings, then (overlapping them)
+// the epilogue staging, then the epilogue scalars
+template <class C, int KS>
+struct KsLds {
+  static constexpr int RINGS = KS * C::LDS;
+  static constexpr int SC_OFF = RINGS > C::EPI_LDS ? RINGS : C::EPI_LDS;
+  static constexpr int TOTAL = SC_OFF + C::SC_PAD * 4;
+  static_assert(TOTAL <= 160 * 1024, "LDS budget");
+};
+
 // P > 0: P more waves (after the C::WAVES MFMA waves) issue every stage copy,
 // so the MFMA waves never stall on copy issue; the copies of a stage are
 // still issued one stage ahead and made visible by the stage barrier.
+// KS = 2 (int8, no producers): two sets of C::WAVES waves split K in halves,
+// each with its own stage ring (both meet at every stage barrier); at the
+// end the second set's int32 accumulators are added to the first set's
+// (exact: the result does not depend on the split), which runs the
+// epilogue.  Each wave's dependent chain through the stages is halved, for
+// the short launches of small tiles where that chain sets the time.
 // bands != 0: row-band tile order (gm ignored), see band_tile.
-template <class C, int EPI, int P = 0>
-__global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm,
-                                                                          int bands) {
+template <class C, int EPI, int P = 0, int KS = 1>
+__global__ __launch_bounds__(C::THREADS * KS + 64 * P, 1) void gemm_dma_kernel(GemmArgs g, int tiles_n, int gm,
+                                                                               int bands) {
+  static_assert(KS == 1 || (KS == 2 && P == 0 && C::INT), "K halves: int8, no producer waves");
+  using L = KsLds<C, KS>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = KS > 1 ? wave_all / C::WAVES : 0;  // K half of this wave
+  const int wave = KS > 1 ? wave_all % C::WAVES : wave_all;
+  uint8_t* const ring = smem + kh * C::LDS;  // this half's stage ring
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   const uint8_t* const xb = static_cast<const uint8_t*>(g.A);  // operand bases
   const uint8_t* const wb = static_cast<const uint8_t*>(g.B);
@@ -449,7 +470,8 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   else tile_coords(xcd_tile(blockIdx.x, nt), nt / tiles_n, tiles_n, gm, tm, tn);
   const int m0 = tm * C::BM, n0 = tn * C::BN;
   constexpr bool INT = C::INT;
-  const int nk = g.K * (INT ? 1 : 2) / KB;
+  const int nk = g.K * (INT ? 1 : 2) / KB / KS;  // stages of this wave's K range
+  const int kb0 = kh * nk;                        // its first stage
 
   if constexpr (P > 0) {
     if (wave >= C::WAVES) {  // producer: stage copies one stage ahead, one barrier per stage
@@ -530,12 +552,14 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   // loop instead of opening the epilogue.  Issued ahead of every stage copy,
   // these loads are older than all of them, so the stage waits stay exact.
   constexpr bool EARLY_RES = RES && NIT <= 4;
-  if constexpr (EARLY_RES) load_res(0);
+  if constexpr (EARLY_RES) {
+    if (kh == 0) load_res(0);
+  }
 
   // the epilogue's per-row / per-column scalars travel to LDS first; they
   // are older than every stage copy, so the stage waits cover them too
-  {
-    float* sc = reinterpret_cast<float*>(smem + C::SC_OFF);
+  if (kh == 0) {
+    float* sc = reinterpret_cast<float*>(smem + L::SC_OFF);
 #pragma unroll
     for (int i = wave; i < C::SC_LOADS; i += C::WAVES) {
       const int q = i * 64 + lane;  // x_scale rows, then w_scale columns, then bias columns, then padding
@@ -553,7 +577,7 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   }
 #pragma unroll
   for (int s = 0; s < C::STAGES - 1; ++s)
-    if (P == 0 && s < nk) ld.issue(xb, wb, sb, wave, smem + s * C::STAGE_BYTES, s);
+    if (P == 0 && s < nk) ld.issue(xb, wb, sb, wave, ring + s * C::STAGE_BYTES, kb0 + s);
 
   Frags<C> fr;
   fr.init(lane, wn);
@@ -567,17 +591,17 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
     __builtin_amdgcn_s_barrier();
     const int kn = kt + C::STAGES - 1;
     const bool more = kn < nk;
-    uint8_t* const snext = smem + (kn % C::STAGES) * C::STAGE_BYTES;
-    const uint8_t* const stage = smem + (kt % C::STAGES) * C::STAGE_BYTES;
+    uint8_t* const snext = ring + (kn % C::STAGES) * C::STAGE_BYTES;
+    const uint8_t* const stage = ring + (kt % C::STAGES) * C::STAGE_BYTES;
     v4i xf[2][C::MI], wf[2][C::NJ];
     fr.read(stage, wm, wn, 0, xf[0], wf[0]);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (P == 0 && more) {
-        if (ks == 0) ld.template issue_part<0, C::KS>(xb, wb, sb, wave, snext, kn);
-        if (ks == 1) ld.template issue_part<1, C::KS>(xb, wb, sb, wave, snext, kn);
-        if (ks == 2) ld.template issue_part<2, C::KS>(xb, wb, sb, wave, snext, kn);
-        if (ks == 3) ld.template issue_part<3, C::KS>(xb, wb, sb, wave, snext, kn);
+        if (ks == 0) ld.template issue_part<0, C::KS>(xb, wb, sb, wave, snext, kb0 + kn);
+        if (ks == 1) ld.template issue_part<1, C::KS>(xb, wb, sb, wave, snext, kb0 + kn);
+        if (ks == 2) ld.template issue_part<2, C::KS>(xb, wb, sb, wave, snext, kb0 + kn);
+        if (ks == 3) ld.template issue_part<3, C::KS>(xb, wb, sb, wave, snext, kb0 + kn);
       }
       if (ks + 1 < C::KS) fr.read(stage, wm, wn, ks + 1, xf[(ks + 1) & 1], wf[(ks + 1) & 1]);
       mfma_slice<C>(acc, xf[ks & 1], wf[ks & 1]);
@@ -586,11 +610,38 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
 
   // with producers, this wave's own loads are only the epilogue scalars
   if constexpr (P > 0) vm_wait<0>();
+  if constexpr (KS > 1) {
+    // the second half's accumulators through LDS (the rings are free once
+    // every wave is past its last stage): value r of MFMA block (j, i) of
+    // lane l of wave w at int ((w * NJ + j) * MI + i) * 16 + r) * 64 + l
+    __syncthreads();
+    int* xch = reinterpret_cast<int*>(smem);
+    if (kh == 1) {
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xch[(((wave * C::NJ + j) * C::MI + i) * 16 + r) * 64 + lane] = acc[j][i][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[j][i][r] += xch[(((wave * C::NJ + j) * C::MI + i) * 16 + r) * 64 + lane];
+    }
+  }
   // Epilogue (the residual of pass 0 was loaded up front for the small tiles)
-  if constexpr (!EARLY_RES) load_res(0);
+  if constexpr (!EARLY_RES) {
+    if (kh == 0) load_res(0);
+  }
   __syncthreads();  // every wave is done with the operand stages; the scalars have landed
+  if (KS > 1 && kh != 0) return;
   uint32_t* reg = reinterpret_cast<uint32_t*>(smem) + wave * (C::WM * (RS + 1));
-  const float* sc = reinterpret_cast<const float*>(smem + C::SC_OFF);
+  const float* sc = reinterpret_cast<const float*>(smem + L::SC_OFF);
 #pragma unroll
   for (int p = 0; p < C::WN / PW; ++p) {
     if (p + 1 < NPASS) load_res(p + 1);
@@ -664,7 +715,7 @@ __global__ __launch_bounds__(C::THREADS + 64 * P, 1) void gemm_dma_kernel(GemmAr
   }
 }
 
-template <class C, int EPI, int P>
+template <class C, int EPI, int P, int KS = 1>
 void launch_cfg(const GemmArgs& g, hipStream_t st) {
   const int tm = (g.M + C::BM - 1) / C::BM, tn = (g.N + C::BN - 1) / C::BN;
   // large tiles over an X larger than W: row bands per XCD (band_tile);
@@ -675,27 +726,29 @@ void launch_cfg(const GemmArgs& g, hipStream_t st) {
   int gm = (int)(sqrtf((float)run) + 0.5f);
   gm = std::max(gm, (run + tn - 1) / tn);
   gm = std::max(1, std::min(gm, tm));
-  hipLaunchKernelGGL((gemm_dma_kernel<C, EPI, P>), dim3((unsigned)(tm * tn)), dim3(C::THREADS + 64 * P),
-                     C::LDS_TOTAL, st, g, tn, gm, bands);
+  hipLaunchKernelGGL((gemm_dma_kernel<C, EPI, P, KS>), dim3((unsigned)(tm * tn)), dim3(C::THREADS * KS + 64 * P),
+                     (KsLds<C, KS>::TOTAL), st, g, tn, gm, bands);
 }
 
-// P producer waves for the epilogues without a residual, PR with one
-template <class C, int P = 0, int PR = P>
+// P producer waves for the epilogues without a residual, PR with one; KS
+// K halves
+template <class C, int P = 0, int PR = P, int KS = 1>
 void launch_epi(const GemmArgs& g, hipStream_t st) {
   const bool res = g.epi.residual != nullptr, gelu = g.epi.act == 1;
-  if (gelu && res) launch_cfg<C, EPI_GELU_RES, PR>(g, st);
-  else if (gelu) launch_cfg<C, EPI_GELU, P>(g, st);
-  else if (res) launch_cfg<C, EPI_RES, PR>(g, st);
-  else launch_cfg<C, EPI_PLAIN, P>(g, st);
+  if (gelu && res) launch_cfg<C, EPI_GELU_RES, PR, KS>(g, st);
+  else if (gelu) launch_cfg<C, EPI_GELU, P, KS>(g, st);
+  else if (res) launch_cfg<C, EPI_RES, PR, KS>(g, st);
+  else launch_cfg<C, EPI_PLAIN, P, KS>(g, st);
 }
 
-template <class C, int P = 0, int PR = P>
+template <class C, int P = 0, int PR = P, int KS = 1>
 void prep_cfg() {
-  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN, P>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES, PR>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU, P>),
-                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES, PR>)};
-  for (const void* f : k) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_TOTAL);
+  const void* k[4] = {reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_PLAIN, P, KS>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_RES, PR, KS>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU, P, KS>),
+                      reinterpret_cast<const void*>(&gemm_dma_kernel<C, EPI_GELU_RES, PR, KS>)};
+  for (const void* f : k)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, KsLds<C, KS>::TOTAL);
 }
 
 // tile configurations per mode (BM, BN, stages, waves along N, waves along
@@ -778,7 +831,13 @@ void dispatch(const GemmArgs& g, hipStream_t st) {
     // hidden-width projections) take 32 x 64 tiles: twice the workgroups
     if constexpr (MODE == M_I8) {
       if (tiles(g.M, g.N, 64, 64) < device_cus()) {
-        launch_epi<typename T::T32x64>(g, st);
+        // with K in two halves of whole stages: the 512-row step's o, q, ox
+        // (5.35 -> 4.7 us) and down (K = 4096, 10.7 -> 8.1 us), mid-size loop
+        // 851 -> 907 steps/s (MI355X).  The 128 x 64 tiles of its qkv and up
+        // with split K (three-stage rings) ran faster alone but slowed the
+        // loop, so they keep one ring.
+        if ((g.K / KB) % 2 == 0 && g.K / KB >= 4) launch_epi<typename T::T32x64, 0, 0, 2>(g, st);
+        else launch_epi<typename T::T32x64>(g, st);
         return;
       }
     }
@@ -794,7 +853,10 @@ void prep_mode() {
   prep_cfg<typename T::T128>();
   prep_cfg<typename T::T128x64>();
   prep_cfg<typename T::T64>();
-  if constexpr (MODE == M_I8) prep_cfg<typename T::T32x64>();
+  if constexpr (MODE == M_I8) {
+    prep_cfg<typename T::T32x64>();
+    prep_cfg<typename T::T32x64, 0, 0, 2>();
+  }
 }
 
 }  // namespace
