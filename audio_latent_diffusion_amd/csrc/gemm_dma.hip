@@ -613,7 +613,7 @@ __global__ __launch_bounds__(C::THREADS * KS + 64 * P, 1) void gemm_dma_kernel(G
   if constexpr (KS > 1) {
     // the second half's accumulators through LDS (the rings are free once
     // every wave is past its last stage): value r of MFMA block (j, i) of
-    // lane l of wave w at int ((w * NJ + j) * MI + i) * 16 + r) * 64 + l
+    // lane l of wave w at int (((w * NJ + j) * MI + i) * 16 + r) * 64 + l
     __syncthreads();
     int* xch = reinterpret_cast<int*>(smem);
     if (kh == 1) {
