@@ -408,14 +408,17 @@ __global__ void cu_pairs_kernel(const int32_t* __restrict__ cu, int R, int64_t n
 // hardware sine (input in turns).  The argument reaches 1000 rad and the fp32
 // value carries ~1e-4 rad of rounding error.
 // CK > 0: the latent width is the compile-time CK (the K loop unrolls and all
-// of a tile's operand loads are in flight at once); CK = 0: any multiple of 8
-template <int WGN, int WGM, int CK>
+// of a tile's operand loads are in flight at once); CK = 0: any multiple of 8.
+// B: 32 x 32 blocks per wave along each side (B = 2: 64 x 64 per wave; B = 1:
+// 32 x 32, four times the waves over the same tile, for short launches).
+// Each output takes the same products in the same K order either way.
+template <int WGN, int WGM, int CK, int B = 2>
 __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __restrict__ x, int64_t n_tok, int M,
                                                                 int C_rt, const uint16_t* __restrict__ w, int H,
                                                                 const float* __restrict__ bias,
                                                                 const float* __restrict__ t_cur, RowMap map,
                                                                 uint16_t* __restrict__ h) {
-  constexpr int TN = 64 * WGN, TM = 64 * WGM;
+  constexpr int TN = 32 * B * WGN, TM = 32 * B * WGM;
   const int C = CK > 0 ? CK : C_rt;
   __shared__ float turns_per_t[TN];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -427,29 +430,29 @@ __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __r
   }
   __syncthreads();
   const int li = lane & 31, hi = lane >> 5;
-  const int cw = (wave % WGN) * 64;  // this wave's columns within the tile
-  int64_t wrow[2];
+  const int cw = (wave % WGN) * 32 * B;  // this wave's columns within the tile
+  int64_t wrow[B];
 #pragma unroll
-  for (int bj = 0; bj < 2; ++bj) wrow[bj] = (int64_t)min(n0 + cw + 32 * bj + li, H - 1) * C;
+  for (int bj = 0; bj < B; ++bj) wrow[bj] = (int64_t)min(n0 + cw + 32 * bj + li, H - 1) * C;
   // row tiles beyond the grid's y extent (65535) are walked with its stride
   for (int m0 = blockIdx.y * TM; m0 < M; m0 += gridDim.y * TM) {
-    const int mw = m0 + (wave / WGN) * 64;
-    int64_t xrow[2];
+    const int mw = m0 + (wave / WGN) * 32 * B;
+    int64_t xrow[B];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) xrow[bi] = (int64_t)(min(mw + 32 * bi + li, M - 1) % n_tok) * C;
-    v16f acc[2][2];
+    for (int bi = 0; bi < B; ++bi) xrow[bi] = (int64_t)(min(mw + 32 * bi + li, M - 1) % n_tok) * C;
+    v16f acc[B][B];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < B; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < B; ++bj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.0f;
 #pragma unroll
     for (int k0 = 0; k0 < C; k0 += 16) {
       const int kk = k0 + 8 * hi;
-      v8h xf[2], wf[2];
+      v8h xf[B], wf[B];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) {
+      for (int bi = 0; bi < B; ++bi) {
         if (kk < C) {
           const float4 a = *reinterpret_cast<const float4*>(x + xrow[bi] + kk);
           const float4 b = *reinterpret_cast<const float4*>(x + xrow[bi] + kk + 4);
@@ -460,22 +463,22 @@ __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __r
         }
       }
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < B; ++bj)
         wf[bj] = kk < C ? __builtin_bit_cast(v8h, ld16(w + wrow[bj] + kk)) : v8h{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
+      for (int bi = 0; bi < B; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < B; ++bj)
           acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[bj], xf[bi], acc[bi][bj], 0, 0, 0);
     }
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
+    for (int bi = 0; bi < B; ++bi) {
       const int m = mw + 32 * bi + li;
       if (m >= M) continue;
       const float t = t_cur[req_of(map, (uint32_t)m)];
       uint16_t* hrow = h + (int64_t)m * H;
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < B; ++bj)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int cl = cw + 32 * bj + 8 * q + 4 * hi;  // column within the tile
@@ -498,8 +501,9 @@ __global__ __launch_bounds__(64 * WGN * WGM) void inproj_kernel(const float* __r
 void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* w, int H, const float* bias,
                    const float* t_cur, RowMap map, uint16_t* h, hipStream_t st) {
   if (M <= 0 || H <= 0) return;
-  // 128 x 128 tiles of four waves, or single-wave 64 x 64 tiles when the
-  // large ones would not give every CU a workgroup (the 512-row step)
+  // 128 x 128 tiles of four waves (64 x 64 each), or 64 x 64 tiles of four
+  // waves (32 x 32 each) when the large ones would not give every CU a
+  // workgroup (the 512-row step)
   // (the latent width 64 of every model here takes the unrolled kernels)
   const int64_t big = (int64_t)((H + 127) / 128) * ((M + 127) / 128);
   if (big >= 256) {
@@ -509,11 +513,13 @@ void launch_inproj(const float* x, int64_t n_tok, int M, int C, const uint16_t* 
     else
       hipLaunchKernelGGL((inproj_kernel<2, 2, 0>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
   } else {
+    // 64 x 64 tiles as four waves of 32 x 32 (the 512-row step: 512 waves
+    // instead of 128 single-wave tiles; its loop 908 -> 913 steps/s, MI355X)
     dim3 grid((unsigned)((H + 63) / 64), (unsigned)std::min<int64_t>((M + 63) / 64, 65535));
     if (C == 64)
-      hipLaunchKernelGGL((inproj_kernel<1, 1, 64>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+      hipLaunchKernelGGL((inproj_kernel<2, 2, 64, 1>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
     else
-      hipLaunchKernelGGL((inproj_kernel<1, 1, 0>), grid, dim3(64), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
+      hipLaunchKernelGGL((inproj_kernel<2, 2, 0, 1>), grid, dim3(256), 0, st, x, n_tok, M, C, w, H, bias, t_cur, map, h);
   }
 }
 
