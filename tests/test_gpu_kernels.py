@@ -144,8 +144,12 @@ def test_row_kernels_beyond_last_level_cache():
 
 # ------------------------------------------------------------- W8A8 GEMM
 
-W8A8_SHAPES = [(1, 16, 1), (3, 32, 7), (77, 272, 130), (128, 256, 768), (200, 1024, 257), (512, 1024, 3072),
-               (130, 6144, 96)]
+# small launches take 32 x 64 tiles whose K splits in two halves when the
+# 128-byte stages are even in number and at least 4: (200, 1024, 257),
+# (70, 512, 100) (two stages per half, fewer than the ring's lookahead) and
+# (130, 6144, 96); (40, 384, 64) has an odd count and runs unsplit
+W8A8_SHAPES = [(1, 16, 1), (3, 32, 7), (77, 272, 130), (128, 256, 768), (200, 1024, 257), (70, 512, 100),
+               (40, 384, 64), (512, 1024, 3072), (130, 6144, 96)]
 
 
 @pytest.mark.parametrize("M,K,N", W8A8_SHAPES)
